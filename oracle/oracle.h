@@ -1,0 +1,124 @@
+/*
+ * CPU oracle for the tiled multiply-accumulate D = A*B + C and its epilogue.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or calls
+ * this code: only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no source, header, table or helper with the HIP
+ * library; the two agree only through the bytes of the seeded inputs.
+ *
+ * What it computes, and where that is defined:
+ *   - "NVIDIA MMA" (rainlin-net), section "From FMA to MMA to GEMM": the GEMM
+ *     element D[m,n] = sum_k A[m,k] B[k,n] + C[m,n].  Written out literally,
+ *     k ascending, in fp64 (float inputs) or int64 (s8 inputs).  Every product
+ *     of two fp16/bf16/fp8 values is exact in fp64, so the only rounding is the
+ *     fp64 running sum.
+ *   - same page, section "Input / accumulate / output": the accumulator is
+ *     followed by an epilogue "scale, bias, activation, cast".  Here:
+ *     y = alpha*(acc + C) + bias[n] in fp64, z = relu(y) when asked, then one
+ *     round-to-nearest-even cast to the output type.
+ *   - same page, section "Ampere: FP16/BF16 and integer MMA baseline": integer
+ *     results that do not fit wrap modulo 2^32 (no saturation requested).
+ *   - same page, section "Dense and 2:4 structured sparse multiplication": the
+ *     2:4 format keeps 2 of every 4 consecutive K positions of A, with their
+ *     positions as metadata; ascending positions per the "ordered metadata"
+ *     remark in the Ampere section.  Metadata bit packing is not on the pages;
+ *     the packing used here is stated at oracle_sparse24_compress.
+ *   - bit formats: IEEE binary16; bfloat16 = the upper 16 bits of binary32;
+ *     OCP FP8 E4M3 (bias 7, no infinity, 0x7F/0xFF NaN, max 448) and E5M2
+ *     (bias 15, IEEE-like infinities, max 57344), the bare FP8 formats named
+ *     in the precision tables of "NVIDIA MMA".
+ */
+#ifndef ORACLE_H
+#define ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types known to the oracle (its own numbering). */
+enum {
+    OR_F16 = 0,
+    OR_BF16 = 1,
+    OR_E4M3 = 2,
+    OR_E5M2 = 3,
+    OR_S8 = 4,
+    OR_F32 = 5,
+    OR_S32 = 6
+};
+
+typedef struct {
+    int64_t M, N, K;
+    int a_type, b_type, c_type, d_type;
+    int a_col_major; /* 0: A[m*lda + k]   1: A[k*lda + m] */
+    int b_col_major; /* 1: B[n*ldb + k]   0: B[k*ldb + n] */
+    int64_t lda, ldb, ldc, ldd; /* leading dimensions in elements; C, D row-major */
+    float alpha;   /* widened to fp64 before use */
+    int has_c;
+    int has_bias;  /* bias is fp32, one value per output column n */
+    int relu;
+} oracle_gemm_t;
+
+/* Decode element idx of an array of the given type to fp64 (s8/s32 exact). */
+double oracle_decode(int type, const void *base, int64_t idx);
+
+/* Round x to the given float type with round-to-nearest-even (overflow goes
+ * to +-inf, NaN stays NaN) and store its bit pattern at base[idx].  For OR_S32
+ * x must be an integer and is reduced modulo 2^32. Returns 0, or -1 for an
+ * unsupported type. */
+int oracle_encode(int type, double x, void *base, int64_t idx);
+
+/* Element-wise loops over oracle_decode / oracle_encode. */
+void oracle_decode_array(int type, const void *base, int64_t n, double *out);
+int oracle_encode_array(int type, const double *x, int64_t n, void *base);
+
+/* Full GEMM + epilogue.  D receives the encoded result.  Optional outputs
+ * (NULL to skip), each M*N fp64 values row-major:
+ *   Y - the exact-as-possible fp64 result before the final cast
+ *       (integers: the wrapped int32 value);
+ *   S - sum_k |A[m,k] B[k,n]| + |C[m,n]|, the scale of the rounding error.
+ * Returns 0, or -1 on an unsupported combination. */
+int oracle_gemm(const oracle_gemm_t *g, const void *A, const void *B, const void *C,
+                const float *bias, void *D, double *Y, double *S);
+
+/* The same definition evaluated at n chosen (rows[i], cols[i]) entries only;
+ * D_out receives n encoded elements, Y and S n values each (nullable). */
+int oracle_gemm_entries(const oracle_gemm_t *g, const void *A, const void *B, const void *C,
+                        const float *bias, int64_t n, const int64_t *rows, const int64_t *cols,
+                        void *D_out, double *Y, double *S);
+
+/* fp32 epilogue applied to a given fp32 tile T (= acc + C as a kernel holds
+ * it), in fp32 arithmetic: y = has_bias ? fmaf(alpha, t, bias[n]) : alpha*t,
+ * z = relu ? (y > 0 ? y : +0) : y, then an RNE cast of z to d_type.
+ * Used to pin a fused epilogue bit for bit. */
+int oracle_epilogue_f32(int64_t M, int64_t N, const float *T, float alpha, const float *bias,
+                        int relu, int d_type, void *D);
+
+/* 2:4 compression of a row-major fp16 [M,K] matrix, K % 4 == 0.
+ * Group g of row m is K positions 4g..4g+3.  Its kept positions i0 < i1 give
+ *   values[m*(K/2) + 2g]   = A[m, 4g+i0]
+ *   values[m*(K/2) + 2g+1] = A[m, 4g+i1]
+ *   nibble (i0 | i1 << 2) at bits 4*(g%8) .. 4*(g%8)+3 of meta[m*W + g/8],
+ * with W = ceil(K/32) words per row and unused high nibbles 0.
+ * Zeros (+0 and -0) are the dropped positions; a group with fewer than two
+ * non-zeros keeps its non-zero positions and fills up with the lowest unused
+ * positions; NaN counts as non-zero.
+ * Returns 0, or the 1-based row index of the first row holding a group with
+ * more than two non-zeros (then the outputs are unspecified). */
+int64_t oracle_sparse24_compress(int64_t M, int64_t K, const uint16_t *A, uint16_t *values,
+                                 uint32_t *meta);
+
+/* Inverse: logical fp16 [M,K] with +0 at the dropped positions.  Returns 0, or
+ * -1 if some nibble is not ascending (i0 >= i1). */
+int oracle_sparse24_decompress(int64_t M, int64_t K, const uint16_t *values, const uint32_t *meta,
+                               uint16_t *A);
+
+/* Threads the OpenMP loops use. */
+int oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,202 @@
+"""ctypes wrapper over the CPU oracle (liboracle.so).  TEST INFRASTRUCTURE ONLY.
+
+Arrays are numpy arrays holding raw element bits:
+  f16, bf16 -> uint16    e4m3, e5m2 -> uint8    s8 -> int8
+  f32 -> float32         s32 -> int32
+The library is built from oracle.c on first use when it is missing.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+TYPES = {"f16": 0, "bf16": 1, "e4m3": 2, "e5m2": 3, "s8": 4, "f32": 5, "s32": 6}
+STORAGE = {
+    "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8, "e5m2": np.uint8,
+    "s8": np.int8, "f32": np.float32, "s32": np.int32,
+}
+
+_lib = None
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("a_type", ctypes.c_int), ("b_type", ctypes.c_int),
+        ("c_type", ctypes.c_int), ("d_type", ctypes.c_int),
+        ("a_col_major", ctypes.c_int), ("b_col_major", ctypes.c_int),
+        ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64),
+        ("ldc", ctypes.c_int64), ("ldd", ctypes.c_int64),
+        ("alpha", ctypes.c_float),
+        ("has_c", ctypes.c_int), ("has_bias", ctypes.c_int), ("relu", ctypes.c_int),
+    ]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.LIB
+        if not os.path.exists(path):
+            _build.build()
+        L = ctypes.CDLL(path)
+        vp, i64, dp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p
+        L.oracle_decode.restype = ctypes.c_double
+        L.oracle_decode.argtypes = [ctypes.c_int, vp, i64]
+        L.oracle_encode.restype = ctypes.c_int
+        L.oracle_encode.argtypes = [ctypes.c_int, ctypes.c_double, vp, i64]
+        L.oracle_decode_array.restype = None
+        L.oracle_decode_array.argtypes = [ctypes.c_int, vp, i64, dp]
+        L.oracle_encode_array.restype = ctypes.c_int
+        L.oracle_encode_array.argtypes = [ctypes.c_int, dp, i64, vp]
+        L.oracle_gemm.restype = ctypes.c_int
+        L.oracle_gemm.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, dp, dp]
+        L.oracle_gemm_entries.restype = ctypes.c_int
+        L.oracle_gemm_entries.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, i64, vp, vp,
+                                          vp, dp, dp]
+        L.oracle_epilogue_f32.restype = ctypes.c_int
+        L.oracle_epilogue_f32.argtypes = [i64, i64, vp, ctypes.c_float, vp, ctypes.c_int,
+                                          ctypes.c_int, vp]
+        L.oracle_sparse24_compress.restype = ctypes.c_int64
+        L.oracle_sparse24_compress.argtypes = [i64, i64, vp, vp, vp]
+        L.oracle_sparse24_decompress.restype = ctypes.c_int
+        L.oracle_sparse24_decompress.argtypes = [i64, i64, vp, vp, vp]
+        L.oracle_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads():
+    return lib().oracle_num_threads()
+
+
+def decode(type_name, bits):
+    """Decode a raw array of the given type to float64, element by element."""
+    bits = np.ascontiguousarray(bits, dtype=STORAGE[type_name])
+    flat = bits.reshape(-1)
+    out = np.empty(flat.size, dtype=np.float64)
+    lib().oracle_decode_array(TYPES[type_name], _ptr(flat), flat.size, _ptr(out))
+    return out.reshape(bits.shape)
+
+
+def encode(type_name, values):
+    """RNE-encode float64 values (integers for s32) to raw bits of type_name."""
+    values = np.ascontiguousarray(values, dtype=np.float64)
+    flat = values.reshape(-1)
+    out = np.empty(flat.size, dtype=STORAGE[type_name])
+    if lib().oracle_encode_array(TYPES[type_name], _ptr(flat), flat.size, _ptr(out)) != 0:
+        raise ValueError("oracle cannot encode %s" % type_name)
+    return out.reshape(values.shape)
+
+
+def _desc(M, N, K, a_type, b_type, c_type, d_type, a_col_major, b_col_major,
+          lda, ldb, ldc, ldd, alpha, has_c, has_bias, relu):
+    return _Desc(M, N, K, TYPES[a_type], TYPES[b_type], TYPES[c_type], TYPES[d_type],
+                 int(a_col_major), int(b_col_major), lda, ldb, ldc, ldd,
+                 float(alpha), int(has_c), int(has_bias), int(relu))
+
+
+def _lds(M, N, K, a_col_major, b_col_major):
+    lda = M if a_col_major else K
+    ldb = K if b_col_major else N
+    return lda, ldb, N, N
+
+
+def gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, *, a_col_major=False,
+         b_col_major=True, alpha=1.0, relu=False, want_y=True, want_s=True):
+    """Full oracle GEMM on packed operands.
+
+    A is [M,K] row-major (or [K,M] when a_col_major), B is stored [N,K] when
+    b_col_major (else [K,N]), C and D are [M,N] row-major.  Returns
+    (D_bits, Y, S): the encoded output, the fp64 pre-cast result and the
+    error scale sum_k |a b| + |c|.
+    """
+    integer = a_type == "s8"
+    c_type = "s32" if integer else "f32"
+    lda, ldb, ldc, ldd = _lds(M, N, K, a_col_major, b_col_major)
+    g = _desc(M, N, K, a_type, b_type, c_type, d_type, a_col_major, b_col_major,
+              lda, ldb, ldc, ldd, alpha, C is not None, bias is not None, relu)
+    A = np.ascontiguousarray(A, dtype=STORAGE[a_type])
+    B = np.ascontiguousarray(B, dtype=STORAGE[b_type])
+    if C is not None:
+        C = np.ascontiguousarray(C, dtype=STORAGE[c_type])
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+    D = np.zeros((M, N), dtype=STORAGE[d_type])
+    Y = np.empty((M, N), dtype=np.float64) if want_y else None
+    S = np.empty((M, N), dtype=np.float64) if want_s else None
+    rc = lib().oracle_gemm(ctypes.byref(g), _ptr(A), _ptr(B), _ptr(C), _ptr(bias), _ptr(D),
+                           _ptr(Y), _ptr(S))
+    if rc != 0:
+        raise ValueError("oracle_gemm rejected the problem")
+    return D, Y, S
+
+
+def gemm_entries(A, B, C, bias, M, N, K, a_type, b_type, d_type, rows, cols, *,
+                 a_col_major=False, b_col_major=True, alpha=1.0, relu=False):
+    """The oracle definition at chosen (rows[i], cols[i]) only: (D_bits, Y, S)."""
+    integer = a_type == "s8"
+    c_type = "s32" if integer else "f32"
+    lda, ldb, ldc, ldd = _lds(M, N, K, a_col_major, b_col_major)
+    g = _desc(M, N, K, a_type, b_type, c_type, d_type, a_col_major, b_col_major,
+              lda, ldb, ldc, ldd, alpha, C is not None, bias is not None, relu)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    n = rows.size
+    D = np.zeros(n, dtype=STORAGE[d_type])
+    Y = np.empty(n, dtype=np.float64)
+    S = np.empty(n, dtype=np.float64)
+    rc = lib().oracle_gemm_entries(ctypes.byref(g), _ptr(A), _ptr(B), _ptr(C), _ptr(bias), n,
+                                   _ptr(rows), _ptr(cols), _ptr(D), _ptr(Y), _ptr(S))
+    if rc != 0:
+        raise ValueError("oracle_gemm_entries rejected the problem")
+    return D, Y, S
+
+
+def epilogue_f32(T, alpha, bias, relu, d_type):
+    """fp32-semantics epilogue of a given fp32 [M,N] tile (see oracle.h)."""
+    T = np.ascontiguousarray(T, dtype=np.float32)
+    M, N = T.shape
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+    D = np.zeros((M, N), dtype=STORAGE[d_type])
+    rc = lib().oracle_epilogue_f32(M, N, _ptr(T), float(alpha), _ptr(bias), int(relu),
+                                   TYPES[d_type], _ptr(D))
+    if rc != 0:
+        raise ValueError("oracle_epilogue_f32 rejected the output type")
+    return D
+
+
+class NotSparse24(ValueError):
+    pass
+
+
+def sparse24_compress(A):
+    """fp16 [M,K] bits -> (values [M,K/2] uint16, meta [M,ceil(K/32)] uint32)."""
+    A = np.ascontiguousarray(A, dtype=np.uint16)
+    M, K = A.shape
+    if K % 4:
+        raise ValueError("K must be a multiple of 4")
+    values = np.zeros((M, K // 2), dtype=np.uint16)
+    meta = np.zeros((M, (K + 31) // 32), dtype=np.uint32)
+    rc = lib().oracle_sparse24_compress(M, K, _ptr(A), _ptr(values), _ptr(meta))
+    if rc > 0:
+        raise NotSparse24("row %d has a group with more than two non-zeros" % (rc - 1))
+    if rc < 0:
+        raise ValueError("bad shape")
+    return values, meta
+
+
+def sparse24_decompress(values, meta, M, K):
+    values = np.ascontiguousarray(values, dtype=np.uint16)
+    meta = np.ascontiguousarray(meta, dtype=np.uint32)
+    A = np.zeros((M, K), dtype=np.uint16)
+    rc = lib().oracle_sparse24_decompress(M, K, _ptr(values), _ptr(meta), _ptr(A))
+    if rc != 0:
+        raise ValueError("metadata not ascending or bad shape")
+    return A

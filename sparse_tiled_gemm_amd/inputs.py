@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs for the GEMM workloads.
+
+This module only draws random numbers and stores them in the operand formats,
+using numpy's and torch's own conversions (numpy float16; torch bfloat16 and
+float8).  It holds none of the GEMM arithmetic and is shared by the CPU checks
+and the GPU runs so both read identical bytes.
+
+Arrays are returned as numpy arrays of raw element bits:
+  f16, bf16 -> uint16, e4m3, e5m2 -> uint8, s8 -> int8, f32 -> float32,
+  s32 -> int32.
+Operand layouts: A is [M,K] row-major, B is stored [N,K] (column-major K x N),
+C and D are [M,N] row-major, bias is [N] fp32.
+
+Seeds are 1000*workload + tensor (A=1, B=2, C=3, bias=4, sparsity pattern=5).
+"""
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
+
+
+def _rng(workload, tensor):
+    return np.random.default_rng(1000 * workload + tensor)
+
+
+def to_f16(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def to_bf16(x):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def to_e4m3(x):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def to_e5m2(x):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e5m2)
+    return t.view(torch.uint8).numpy()
+
+
+def f16_values(bits):
+    """float64 view of fp16 bits (numpy's own conversion; used by generators)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+class Problem(dict):
+    """Operands plus the call description: keys M, N, K, a_type, b_type, d_type,
+    A, B, C (or None), bias (or None), alpha, relu, and for the 2:4 workload
+    A_logical (the dense fp16 matrix the compressor receives)."""
+
+    @property
+    def flops(self):
+        return 2.0 * self["M"] * self["N"] * self["K"]
+
+
+def dense_f16(M=128, N=128, K=128, workload=1):
+    """fp16 A, B uniform[-1,1]; C fp32 uniform[-1,1]; fp32 out, no epilogue."""
+    A = to_f16(_rng(workload, 1).uniform(-1.0, 1.0, size=(M, K)))
+    B = to_f16(_rng(workload, 2).uniform(-1.0, 1.0, size=(N, K)))
+    C = _rng(workload, 3).uniform(-1.0, 1.0, size=(M, N)).astype(np.float32)
+    return Problem(M=M, N=N, K=K, a_type="f16", b_type="f16", d_type="f32", A=A, B=B, C=C,
+                   bias=None, alpha=1.0, relu=False)
+
+
+def dense_bf16(M=8192, N=8192, K=8192, workload=2, d_type="bf16"):
+    """bf16 A, B normal(0,1)/sqrt(K); C fp32 zeros (a real buffer); bf16 out."""
+    s = 1.0 / np.sqrt(K)
+    A = to_bf16(_rng(workload, 1).standard_normal(size=(M, K), dtype=np.float32) * s)
+    B = to_bf16(_rng(workload, 2).standard_normal(size=(N, K), dtype=np.float32) * s)
+    C = np.zeros((M, N), dtype=np.float32)
+    return Problem(M=M, N=N, K=K, a_type="bf16", b_type="bf16", d_type=d_type, A=A, B=B, C=C,
+                   bias=None, alpha=1.0, relu=False)
+
+
+def dense_s8(M=8192, N=8192, K=8192, workload=3):
+    """s8 A, B uniform integers in [-128,127]; C s32 uniform in [-2^20, 2^20]."""
+    A = _rng(workload, 1).integers(-128, 128, size=(M, K), dtype=np.int8)
+    B = _rng(workload, 2).integers(-128, 128, size=(N, K), dtype=np.int8)
+    C = _rng(workload, 3).integers(-(1 << 20), (1 << 20) + 1, size=(M, N), dtype=np.int32)
+    return Problem(M=M, N=N, K=K, a_type="s8", b_type="s8", d_type="s32", A=A, B=B, C=C,
+                   bias=None, alpha=1.0, relu=False)
+
+
+def dense_fp8(M=8192, N=8192, K=8192, workload=4):
+    """A normal(0,1) scaled by sA = 448/amax(A), clamped and rounded to E4M3;
+    B likewise with sB = 57344/amax(B) to E5M2; no C; alpha = fp32(1/(sA*sB));
+    bias fp32 normal(0,1) [N]; out = relu(alpha*acc + bias[n]) as fp16."""
+    a = _rng(workload, 1).standard_normal(size=(M, K), dtype=np.float32).astype(np.float64)
+    b = _rng(workload, 2).standard_normal(size=(N, K), dtype=np.float32).astype(np.float64)
+    sA = E4M3_MAX / np.abs(a).max()
+    sB = E5M2_MAX / np.abs(b).max()
+    A = to_e4m3(np.clip(a * sA, -E4M3_MAX, E4M3_MAX))
+    B = to_e5m2(np.clip(b * sB, -E5M2_MAX, E5M2_MAX))
+    bias = _rng(workload, 4).standard_normal(size=(N,)).astype(np.float32)
+    alpha = float(np.float32(1.0 / (sA * sB)))
+    return Problem(M=M, N=N, K=K, a_type="e4m3", b_type="e5m2", d_type="f16", A=A, B=B, C=None,
+                   bias=bias, alpha=alpha, relu=True)
+
+
+def sparse24_f16(M=8192, N=8192, K=8192, workload=5):
+    """Logical fp16 A with exactly two non-zeros in every 4 consecutive K
+    positions (one of the 6 position pairs, uniformly), non-zero values
+    uniform[-1,1] with exact zeros redrawn; B fp16 uniform[-1,1]; C fp32
+    uniform[-1,1]; fp32 out.  A_logical is what the compressor receives."""
+    if K % 4:
+        raise ValueError("K must be a multiple of 4")
+    G = K // 4
+    pairs = np.array([(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)], dtype=np.int64)
+    choice = _rng(workload, 5).integers(0, 6, size=(M, G))
+    pos = pairs[choice]  # [M, G, 2], ascending
+    vr = _rng(workload, 1)
+    vals = to_f16(vr.uniform(-1.0, 1.0, size=(M, G, 2)))
+    zero = (vals & 0x7FFF) == 0
+    while zero.any():
+        vals[zero] = to_f16(vr.uniform(-1.0, 1.0, size=int(zero.sum())))
+        zero = (vals & 0x7FFF) == 0
+    A = np.zeros((M, G, 4), dtype=np.uint16)
+    rows = np.arange(M)[:, None]
+    grps = np.arange(G)[None, :]
+    A[rows, grps, pos[..., 0]] = vals[..., 0]
+    A[rows, grps, pos[..., 1]] = vals[..., 1]
+    A = A.reshape(M, K)
+    B = to_f16(_rng(workload, 2).uniform(-1.0, 1.0, size=(N, K)))
+    C = _rng(workload, 3).uniform(-1.0, 1.0, size=(M, N)).astype(np.float32)
+    return Problem(M=M, N=N, K=K, a_type="f16", b_type="f16", d_type="f32", A=None, B=B, C=C,
+                   bias=None, alpha=1.0, relu=False, A_logical=A)
+
+
+WORKLOADS = {
+    "f16_128": lambda: dense_f16(128, 128, 128),
+    "bf16_8192": lambda: dense_bf16(8192, 8192, 8192),
+    "bf16_skinny_16x8192x8192": lambda: dense_bf16(16, 8192, 8192),
+    "s8_8192": lambda: dense_s8(8192, 8192, 8192),
+    "fp8_8192": lambda: dense_fp8(8192, 8192, 8192),
+    "sparse24_f16_8192": lambda: sparse24_f16(8192, 8192, 8192),
+}

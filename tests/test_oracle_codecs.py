@@ -1,0 +1,111 @@
+"""Pins for the oracle's element codecs: every code of each 8/16-bit input
+format against numpy/torch's own conversions and against closed-form values,
+and the round-to-nearest-even output casts against library conversions and
+the round-half-even bit method."""
+import numpy as np
+import pytest
+import torch
+
+
+def _torch_decode(bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits))
+    return t.view(dtype).to(torch.float32).numpy().astype(np.float64)
+
+
+def test_f16_decode_all_codes(orc):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = orc.decode("f16", bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(got, ref, equal_nan=True)
+
+
+def test_bf16_decode_all_codes(orc):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = orc.decode("bf16", bits)
+    ref = _torch_decode(bits.view(np.int16), torch.bfloat16)
+    assert np.array_equal(got, ref, equal_nan=True)
+
+
+@pytest.mark.parametrize("name,tdtype", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_decode_all_codes(orc, name, tdtype):
+    bits = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    got = orc.decode(name, bits)
+    ref = _torch_decode(bits, tdtype)
+    assert np.array_equal(got, ref, equal_nan=True)
+
+
+def test_fp8_closed_forms(orc):
+    e4 = lambda b: float(orc.decode("e4m3", np.array([b], np.uint8))[0])
+    e5 = lambda b: float(orc.decode("e5m2", np.array([b], np.uint8))[0])
+    # OCP E4M3: max normal S.1111.110 = 1.75 * 2^8, one = 0.0111.000, smallest subnormal 2^-9
+    assert e4(0x7E) == 448.0 and e4(0xFE) == -448.0
+    assert e4(0x38) == 1.0 and e4(0x01) == 2.0 ** -9 and e4(0x08) == 2.0 ** -6
+    assert np.isnan(e4(0x7F)) and np.isnan(e4(0xFF))
+    assert e4(0x80) == 0.0 and np.signbit(e4(0x80))
+    # OCP E5M2: max normal 1.75 * 2^15, one = 0.01111.00, smallest subnormal 2^-16, inf 0x7C
+    assert e5(0x7B) == 57344.0 and e5(0x3C) == 1.0 and e5(0x01) == 2.0 ** -16
+    assert e5(0x7C) == np.inf and e5(0xFC) == -np.inf and np.isnan(e5(0x7D))
+
+
+def _f16_grid_samples(rng):
+    """Doubles that exercise f16 rounding: random values over the whole
+    range, exact midpoints between neighbours (ties), subnormals, overflow."""
+    h = np.arange(0, 0x7C00, dtype=np.uint16)
+    v = h.view(np.float16).astype(np.float64)
+    mids = (v[:-1] + v[1:]) / 2.0  # exact in fp64
+    near = np.concatenate([np.nextafter(mids, 0), np.nextafter(mids, 1e9)])
+    rnd = rng.uniform(-70000, 70000, size=200000)
+    small = rng.uniform(-2 ** -13, 2 ** -13, size=100000)
+    edge = np.array([65504.0, 65519.99, 65520.0, 65536.0, 1e9, 2 ** -25, 2 ** -25 * 1.0000001,
+                     3 * 2 ** -26, 0.0, -0.0, np.inf, -np.inf])
+    x = np.concatenate([v, mids, near, rnd, small, edge])
+    return np.concatenate([x, -x])
+
+
+def test_f16_encode_matches_numpy(orc):
+    x = _f16_grid_samples(np.random.default_rng(11))
+    got = orc.encode("f16", x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def _bf16_rne_bits(f32):
+    """Round-half-even of fp32 bit patterns to their upper 16 bits
+    (the classic integer method); NaNs excluded by the caller."""
+    u = f32.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def test_bf16_encode_matches_bit_method_and_torch(orc):
+    rng = np.random.default_rng(12)
+    u = rng.integers(0, 1 << 32, size=3_000_000, dtype=np.uint64).astype(np.uint32)
+    # all tie cases and their neighbours around a sweep of exponents
+    hi = rng.integers(0, 1 << 16, size=200000, dtype=np.uint32) << 16
+    ties = np.concatenate([hi | 0x8000, hi | 0x7FFF, hi | 0x8001])
+    u = np.concatenate([u, ties, np.array([0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 0x00000001,
+                                           0x00008000, 0x00018000, 0x80008000], np.uint32)])
+    f = u.view(np.float32)
+    f = f[~np.isnan(f)]
+    got = orc.encode("bf16", f.astype(np.float64))
+    assert np.array_equal(got, _bf16_rne_bits(f))
+    ref_t = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref_t)
+
+
+def test_f32_encode_matches_numpy(orc):
+    rng = np.random.default_rng(13)
+    x = np.concatenate([rng.standard_normal(500000) * 10.0 ** rng.integers(-40, 40, 500000),
+                        np.array([3.4028235677973366e38, 3.4028235e38 * 1.0000001, 1e-46, 0.0])])
+    x = np.concatenate([x, -x])
+    got = orc.encode("f32", x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_s32_encode_wraps(orc):
+    x = np.array([0, 1, -1, 2 ** 31 - 1, 2 ** 31, -2 ** 31, -2 ** 31 - 1, 2 ** 32 + 5], np.float64)
+    got = orc.encode("s32", x)
+    assert got.tolist() == [0, 1, -1, 2 ** 31 - 1, -2 ** 31, -2 ** 31, 2 ** 31 - 1, 5]
