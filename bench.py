@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Throughput of the gfx950 GEMM library on its synthetic workloads.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-extras] [--no-cpu-baseline]
+
+One step is one call of the library (gemm_run, or gemm_sparse24_run for the
+2:4 workload) over the workload's operands, which are resident in device
+memory before the timed region starts.  The headline workload is the dense
+bf16 GEMM at M = N = K = 8192 (bf16 out); its TFLOPS is `value`.  The other
+workloads are timed the same way and reported under "workloads".  Prints one
+JSON line.
+
+Only one GPU is used: --gpus above 1 exits with an error message.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X datasheet dense peaks (TFLOP/s or TOP/s) and HBM bandwidth (GB/s).
+PEAK = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "s8": 5033.2, "sparse_f16": 5033.2}
+HBM_GBS = 8000.0
+
+HEADLINE = "bf16_8192"
+
+
+def _workloads():
+    from sparse_tiled_gemm_amd import inputs
+    return {
+        "f16_128": (lambda: inputs.dense_f16(128, 128, 128), "f16"),
+        "bf16_8192": (lambda: inputs.dense_bf16(8192, 8192, 8192), "bf16"),
+        "bf16_skinny_16x8192x8192": (lambda: inputs.dense_bf16(16, 8192, 8192), "bf16"),
+        "s8_8192": (lambda: inputs.dense_s8(8192, 8192, 8192), "s8"),
+        "fp8_8192": (lambda: inputs.dense_fp8(8192, 8192, 8192), "fp8"),
+        "sparse24_f16_8192": (lambda: inputs.sparse24_f16(8192, 8192, 8192), "sparse_f16"),
+    }
+
+
+def _dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    view = {1: np.uint8, 2: np.int16, 4: np.int32}[a.itemsize]
+    return torch.from_numpy(a.view(view)).cuda()
+
+
+def algorithmic_bytes(p, sparse=False):
+    """Operand bytes read and written once: A (or values + metadata), B, C,
+    bias, D."""
+    from sparse_tiled_gemm_amd import gemm as G
+    M, N, K = p["M"], p["N"], p["K"]
+    eb = G.ELEM_BYTES
+    if sparse:
+        a = M * (K // 2) * 2 + M * ((K + 31) // 32) * 4
+    else:
+        a = M * K * eb[p["a_type"]]
+    b = N * K * eb[p["b_type"]]
+    c = M * N * 4 if p["C"] is not None else 0
+    bias = N * 4 if p["bias"] is not None else 0
+    d = M * N * eb[p["d_type"]]
+    return a + b + c + bias + d
+
+
+def run_workload(name, steps, warmup, rotate_b=1):
+    """Time `steps` library calls; returns a dict of measurements."""
+    import torch
+    from sparse_tiled_gemm_amd import gemm as G
+    make, kind = _workloads()[name]
+    p = make()
+    M, N, K = p["M"], p["N"], p["K"]
+    sparse = p.get("A_logical") is not None
+    desc = G.make_desc(M, N, K, p["a_type"], p["b_type"], p["d_type"], has_c=p["C"] is not None,
+                       has_bias=p["bias"] is not None, alpha=p["alpha"],
+                       act="relu" if p["relu"] else "none", sparse_a=sparse)
+    plan = G.gemm_plan(desc)
+    Bs = [_dev(p["B"]) for _ in range(rotate_b)]
+    tC = _dev(p["C"]) if p["C"] is not None else None
+    tbias = _dev(p["bias"]) if p["bias"] is not None else None
+    D = torch.empty(M * N * G.ELEM_BYTES[p["d_type"]], dtype=torch.uint8, device="cuda")
+    if sparse:
+        vb, mb = G.gemm_sparse24_sizes(M, K)
+        tAl = _dev(p["A_logical"])
+        vals = torch.empty(vb, dtype=torch.uint8, device="cuda")
+        meta = torch.empty(mb, dtype=torch.uint8, device="cuda")
+        G.gemm_sparse24_compress(M, K, "f16", tAl, vals, meta)
+        del tAl
+
+        def call(i):
+            G.gemm_sparse24_run(plan, vals, meta, Bs[i % rotate_b], tC, tbias, D)
+    else:
+        tA = _dev(p["A"])
+
+        def call(i):
+            G.gemm_run(plan, tA, Bs[i % rotate_b], tC, tbias, D)
+
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        call(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    flops = 2.0 * M * N * K
+    out = {
+        "workload": name, "kernel": plan.name, "M": M, "N": N, "K": K,
+        "a_type": p["a_type"], "b_type": p["b_type"], "d_type": p["d_type"],
+        "ms_per_call": ms, "us_per_call": ms * 1e3,
+    }
+    byts = algorithmic_bytes(p, sparse)
+    out["algorithmic_bytes"] = byts
+    out["GBps"] = byts / (ms * 1e-3) / 1e9
+    if sparse:
+        out["effective_TFLOPS"] = flops / (ms * 1e-3) / 1e12
+        out["algorithmic_TFLOPS"] = flops / 2 / (ms * 1e-3) / 1e12
+        out["frac_sparse_peak"] = out["effective_TFLOPS"] / PEAK[kind]
+        out["frac_dense_peak_algorithmic"] = out["algorithmic_TFLOPS"] / (PEAK[kind] / 2)
+    else:
+        unit = "TOPS" if kind == "s8" else "TFLOPS"
+        out[unit] = flops / (ms * 1e-3) / 1e12
+        out["frac_peak"] = out[unit] / PEAK[kind]
+    out["frac_hbm"] = out["GBps"] / HBM_GBS
+    return out, p
+
+
+def cpu_baseline(p, rows=512):
+    """The CPU oracle on rows 0..rows-1 of the workload (bounded sample)."""
+    from oracle import oracle
+    M, N, K = p["M"], p["N"], p["K"]
+    r = min(rows, M)
+    t0 = time.perf_counter()
+    oracle.gemm(p["A"][:r], p["B"], p["C"][:r] if p["C"] is not None else None, p["bias"], r,
+                N, K, p["a_type"], p["b_type"], p["d_type"], alpha=p["alpha"], relu=p["relu"],
+                want_y=False, want_s=False)
+    dt = time.perf_counter() - t0
+    return {"value": 2.0 * r * N * K / dt / 1e12, "unit": "TFLOPS", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": "rows 0..%d of A: a %dx%dx%d slice of the %dx%dx%d workload, fp64 "
+                      "accumulation, same epilogue" % (r - 1, r, N, K, M, N, K)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(_workloads().keys()))
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the GEMM library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(0)
+    from sparse_tiled_gemm_amd import gemm as G
+    G.load()
+
+    head, p = run_workload(args.workload, args.steps, args.warmup)
+    kind = _workloads()[args.workload][1]
+    unit = "TOPS" if kind == "s8" else "TFLOPS"
+    sparse = kind == "sparse_f16"
+    value = head["effective_TFLOPS"] if sparse else head[unit]
+    achieved = value
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK[kind],
+                "unit": "TOP/s" if kind == "s8" else "TFLOP/s", "frac": achieved / PEAK[kind],
+                "traffic": None, "kernel": head["kernel"],
+                "algorithmic_flops_per_launch": 2.0 * p["M"] * p["N"] * p["K"]}
+    result = {
+        "metric": "TFLOPS (TOPS int8) at M=N=K=8192 per dtype; % of MFMA peak",
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_call"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "f16": "f16", "fp8": "fp8_e4m3xe5m2", "s8": "s8",
+                  "sparse_f16": "f16"}[kind],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": p["M"], "N": p["N"], "K": p["K"],
+                   "a_type": p["a_type"], "b_type": p["b_type"], "d_type": p["d_type"],
+                   "parallelism": "none (one GPU)"},
+        "frac_of_peak": value / PEAK[kind],
+        "roofline": roofline,
+    }
+    del p
+    if not args.no_cpu_baseline:
+        _, pc = None, _workloads()[args.workload][0]()
+        result["cpu_baseline"] = cpu_baseline(pc)
+        del pc
+    if not args.no_extras:
+        extras = {}
+        for name in _workloads():
+            if name == args.workload:
+                continue
+            rot = 4 if name.startswith("bf16_skinny") else 1
+            try:
+                r, _ = run_workload(name, args.steps, args.warmup, rotate_b=rot)
+            except Exception as e:  # report, keep the headline line
+                r = {"error": str(e)}
+            extras[name] = r
+            torch.cuda.empty_cache()
+        result["workloads"] = extras
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

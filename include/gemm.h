@@ -1,0 +1,185 @@
+/*
+ * gemm.h - C ABI of the MI355X (gfx950) tiled multiply-accumulate library
+ * libstgemm.so:
+ *
+ *     D = cast( act( alpha * (A*B + C) + bias[n] ) )
+ *
+ * with low-precision A/B (fp16, bf16, fp8 E4M3/E5M2, s8), an fp32 or int32
+ * accumulator along K, and a 2:4 structured-sparse-A variant.
+ *
+ * Definitions this interface follows (three public pages on tensor-core MMA):
+ *  - "NVIDIA MMA" (rainlin-net), section "From FMA to MMA to GEMM":
+ *    D[m,n] = sum_k A[m,k] B[k,n] + C[m,n] with A M x K, B K x N, C/D M x N;
+ *    a GEMM is many tile MMAs plus data movement, a K loop and an epilogue.
+ *  - same page, section "Input / accumulate / output": input types, the
+ *    accumulator type and the output type are separate choices; the epilogue
+ *    applies scale, bias, activation and cast, in that order.
+ *  - same page, section "Dense and 2:4 structured sparse multiplication":
+ *    only A is compressed (2 kept values of every 4 K positions plus their
+ *    positions); B, C and D stay dense.
+ *  - "CUDA 014 - MMA instruction usage" (blog-9y3), section "MMA instruction
+ *    format": A row-major and B column-major is the natural operand pairing
+ *    (both contiguous along K); the fast kernels here use that pairing.
+ *
+ * Conventions
+ *  - Sizes and leading dimensions are in elements.  A is M x K, row-major
+ *    (A[m*lda + k]) or column-major (A[k*lda + m]).  B is K x N, column-major
+ *    (stored N x K, B[n*ldb + k]) or row-major (B[k*ldb + n]).  C and D are
+ *    M x N row-major (C[m*ldc + n]).  A leading dimension of 0 means packed.
+ *  - All data pointers are device pointers (HIP device memory).  The caller
+ *    owns every buffer; the library never allocates device memory in
+ *    gemm_run / gemm_sparse24_run and needs no workspace.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Launches are asynchronous: a kernel fault surfaces at the caller's next
+ *    synchronisation.  gemm_sparse24_compress alone synchronises its stream.
+ *  - Every function returns a status; no exception or abort crosses the ABI.
+ *    gemm_last_error() gives a thread-local message about the last failure.
+ *  - A plan is immutable after gemm_plan returns: it may be shared by threads
+ *    and used on any stream of the device it was made on.
+ *  - The kernel a plan selects depends on M, N, K, the input types, layouts
+ *    and leading dimensions (and, at run time, pointer alignment) - never on
+ *    the epilogue or output type.  Two plans that differ only in epilogue or
+ *    d_type therefore sum in the same order.
+ */
+#ifndef STGEMM_GEMM_H
+#define STGEMM_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_NULL_POINTER = 1,  /* a required pointer argument is NULL */
+    GEMM_ERR_INVALID_VALUE = 2, /* negative size, bad enum, ld too small, ... */
+    GEMM_ERR_UNSUPPORTED = 3,   /* valid request outside the support matrix */
+    GEMM_ERR_MISALIGNED = 4,    /* pointer alignment a call requires is not met */
+    GEMM_ERR_NOT_SPARSE24 = 5,  /* a group of 4 holds more than 2 non-zeros */
+    GEMM_ERR_DEVICE = 6,        /* current device is not gfx950 */
+    GEMM_ERR_HIP = 7            /* a HIP runtime call failed */
+} gemm_status_t;
+
+typedef enum {
+    GEMM_F16 = 1,     /* IEEE binary16 */
+    GEMM_BF16 = 2,    /* bfloat16 */
+    GEMM_F8_E4M3 = 3, /* OCP FP8 E4M3 (max 448, no infinity) */
+    GEMM_F8_E5M2 = 4, /* OCP FP8 E5M2 (max 57344) */
+    GEMM_S8 = 5,      /* int8, two's complement */
+    GEMM_F32 = 6,     /* IEEE binary32 */
+    GEMM_S32 = 7      /* int32, two's complement */
+} gemm_dtype_t;
+
+typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout_t;
+
+typedef enum { GEMM_ACT_NONE = 0, GEMM_ACT_RELU = 1 } gemm_act_t;
+
+/* Kernel family request.  GEMM_ALGO_AUTO lets the plan choose; any other
+ * value forces that family and gemm_plan returns GEMM_ERR_UNSUPPORTED when it
+ * cannot serve the descriptor (used by tests and tuning sweeps). */
+typedef enum {
+    GEMM_ALGO_AUTO = 0,
+    GEMM_ALGO_TILED = 1,   /* LDS-staged, double-buffered MFMA kernel */
+    GEMM_ALGO_GENERIC = 2, /* any layout / shape / alignment, MFMA, no LDS */
+    GEMM_ALGO_SKINNY = 3,  /* small M, bandwidth-oriented */
+    GEMM_ALGO_TILED_128 = 4, /* GEMM_ALGO_TILED with 128 x 128 workgroup tiles */
+    GEMM_ALGO_TILED_256 = 5  /* GEMM_ALGO_TILED with 256 x 256 workgroup tiles */
+} gemm_algo_t;
+
+/* Problem descriptor.
+ *
+ * Support matrix (everything else is GEMM_ERR_UNSUPPORTED):
+ *   a, b in {F16}, {BF16}, or {F8_E4M3, F8_E5M2} (the two fp8 formats may
+ *   differ): c_type F32, d_type F32 / F16 / BF16, any epilogue.
+ *   a = b = S8: c_type S32, d_type S32, alpha == 1, no bias, no activation;
+ *   the int32 sum wraps modulo 2^32 (no saturation).
+ *   sparse_a = 1: a = b = F16, A row-major, K % 4 == 0; used with
+ *   gemm_sparse24_run (A is then given in compressed form).
+ * Epilogue, in fp32 for float outputs:  t = acc (+ C[m,n] if has_c);
+ *   y = has_bias ? fmaf(alpha, t, bias[n]) : alpha * t;
+ *   z = (act == RELU) ? (y > 0 ? y : +0) : y;  D = round-to-nearest-even(z).
+ * bias is fp32, N values, one per output column. */
+typedef struct {
+    int64_t M, N, K;
+    int32_t a_type, b_type, c_type, d_type; /* gemm_dtype_t */
+    int32_t a_layout, b_layout;             /* gemm_layout_t */
+    int64_t lda, ldb, ldc, ldd;             /* 0 = packed */
+    float alpha;                            /* 1.0f = no scaling */
+    int32_t has_c;                          /* read C (else t = acc) */
+    int32_t has_bias;
+    int32_t act;                            /* gemm_act_t */
+    int32_t sparse_a;                       /* 1: 2:4-compressed A */
+    int32_t algo;                           /* gemm_algo_t, normally AUTO */
+} gemm_desc_t;
+
+typedef struct gemm_plan gemm_plan_t;
+typedef void *gemm_stream_t; /* hipStream_t */
+
+/* Validate a descriptor without touching any device (pure host function).
+ * Returns GEMM_OK, GEMM_ERR_NULL_POINTER, GEMM_ERR_INVALID_VALUE or
+ * GEMM_ERR_UNSUPPORTED. */
+gemm_status_t gemm_validate_desc(const gemm_desc_t *desc);
+
+/* Validate, check that the current HIP device is gfx950, select the kernel
+ * and return a new plan in *out (host memory, owned by the caller, released
+ * with gemm_plan_destroy).  On failure *out is set to NULL. */
+gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out);
+
+/* Release a plan (NULL is accepted). */
+gemm_status_t gemm_plan_destroy(gemm_plan_t *plan);
+
+/* Write the selected kernel's name (NUL-terminated, truncated to len) into
+ * buf.  For logs and tests. */
+gemm_status_t gemm_plan_describe(const gemm_plan_t *plan, char *buf, size_t len);
+
+/* Enqueue D = epilogue(A*B + C) on `stream` (dense A).  C may be NULL only
+ * when the plan has has_c == 0; bias may be NULL only when has_bias == 0.
+ * Returns after the launch is enqueued.  Pointers need only element
+ * alignment: the fast kernels need 16-byte aligned A and B and fall back to
+ * the generic kernel otherwise.  D must not overlap A, B or bias; D == C
+ * (in-place accumulate) is allowed. */
+gemm_status_t gemm_run(const gemm_plan_t *plan, const void *A, const void *B, const void *C,
+                       const void *bias, void *D, gemm_stream_t stream);
+
+/* Bytes of the compressed form of an M x K fp16 A (K % 4 == 0):
+ * values are M x K/2 fp16; metadata is M x ceil(K/32) uint32. */
+gemm_status_t gemm_sparse24_sizes(int64_t M, int64_t K, int32_t a_type, size_t *values_bytes,
+                                  size_t *meta_bytes);
+
+/* Compress a dense row-major M x K fp16 A (device) into the 2:4 form:
+ *   group g of row m covers K positions 4g .. 4g+3; its kept positions
+ *   i0 < i1 (the non-zeros, filled up with the lowest free positions when a
+ *   group has fewer than two) give
+ *     values[m*(K/2) + 2g] = A[m, 4g+i0],  values[m*(K/2) + 2g+1] = A[m, 4g+i1]
+ *   and the nibble (i0 | i1 << 2) at bits 4(g%8)..4(g%8)+3 of
+ *   meta[m*ceil(K/32) + g/8]; unused high nibbles are 0.
+ * +0 and -0 count as zero, NaN as non-zero.  Positions ascend, as the
+ * ordered-metadata form on "NVIDIA MMA" (section "Ampere: FP16/BF16 and
+ * integer MMA baseline") requires; the bit packing is this library's own.
+ * Synchronises `stream` (a one-time weight preprocessing step) and returns
+ * GEMM_ERR_NOT_SPARSE24 when some group holds more than two non-zeros
+ * (values/meta are then unspecified).  A must be 8-byte aligned, values and
+ * meta 4-byte aligned. */
+gemm_status_t gemm_sparse24_compress(int64_t M, int64_t K, int32_t a_type, const void *A,
+                                     void *values, uint32_t *meta, gemm_stream_t stream);
+
+/* Enqueue D = epilogue(A*B + C) with A given as (values, meta) from
+ * gemm_sparse24_compress.  The plan must have sparse_a == 1. */
+gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, const uint32_t *meta,
+                                const void *B, const void *C, const void *bias, void *D,
+                                gemm_stream_t stream);
+
+/* Static text for a status code. */
+const char *gemm_status_string(gemm_status_t status);
+
+/* Thread-local detail about the most recent failure on this thread ("" if
+ * none).  Valid until the thread's next call into the library. */
+const char *gemm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,497 @@
+// C ABI of libstgemm.so: descriptor validation, plan selection and launch.
+// The operation and its conventions are documented in include/gemm.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+
+#include "internal.hpp"
+
+using namespace stg;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gemm_status_t fail(gemm_status_t st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+gemm_status_t ok()
+{
+    g_last_error[0] = '\0';
+    return GEMM_OK;
+}
+
+gemm_status_t hip_fail(hipError_t e, const char *what)
+{
+    return fail(GEMM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_fp8(int t) { return t == GEMM_F8_E4M3 || t == GEMM_F8_E5M2; }
+bool is_float_in(int t) { return t == GEMM_F16 || t == GEMM_BF16 || is_fp8(t); }
+int elem_bytes(int t)
+{
+    switch (t) {
+    case GEMM_F16:
+    case GEMM_BF16: return 2;
+    case GEMM_F8_E4M3:
+    case GEMM_F8_E5M2:
+    case GEMM_S8: return 1;
+    default: return 4;
+    }
+}
+
+int op_kind(int a, int b)
+{
+    if (a == GEMM_F16 && b == GEMM_F16)
+        return OPK_F16;
+    if (a == GEMM_BF16 && b == GEMM_BF16)
+        return OPK_BF16;
+    if (a == GEMM_S8 && b == GEMM_S8)
+        return OPK_S8;
+    if (is_fp8(a) && is_fp8(b)) {
+        const bool a5 = a == GEMM_F8_E5M2, b5 = b == GEMM_F8_E5M2;
+        return a5 ? (b5 ? OPK_F8_E5E5 : OPK_F8_E5E4) : (b5 ? OPK_F8_E4E5 : OPK_F8_E4E4);
+    }
+    return -1;
+}
+
+const char *op_name(int op)
+{
+    static const char *names[] = {"f16", "bf16", "e4m3xe4m3", "e4m3xe5m2", "e5m2xe4m3",
+                                  "e5m2xe5m2", "s8"};
+    return (op >= 0 && op < OPK_COUNT) ? names[op] : "?";
+}
+
+int out_kind(int d)
+{
+    switch (d) {
+    case GEMM_F32: return OUT_F32;
+    case GEMM_F16: return OUT_F16;
+    case GEMM_BF16: return OUT_BF16;
+    default: return OUT_S32;
+    }
+}
+
+// Fill packed leading dimensions; returns false if a given one is too small.
+bool normalise(gemm_desc_t &d)
+{
+    const int64_t a_min = d.a_layout == GEMM_ROW_MAJOR ? d.K : d.M;
+    const int64_t b_min = d.b_layout == GEMM_COL_MAJOR ? d.K : d.N;
+    auto fix = [](int64_t &ld, int64_t mn) {
+        if (ld == 0)
+            ld = mn > 0 ? mn : 1;
+        return ld >= mn && ld > 0;
+    };
+    return fix(d.lda, a_min) & fix(d.ldb, b_min) & fix(d.ldc, d.N) & fix(d.ldd, d.N);
+}
+
+struct DeviceInfo {
+    int checked = 0;
+    int is_gfx950 = 0;
+    int num_cu = 0;
+    char arch[64] = "";
+};
+DeviceInfo g_dev[64];
+std::mutex g_dev_mu;
+
+gemm_status_t check_device(int *dev_out, DeviceInfo *info_out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64)
+        return fail(GEMM_ERR_DEVICE, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DeviceInfo &di = g_dev[dev];
+    if (!di.checked) {
+        hipDeviceProp_t p;
+        e = hipGetDeviceProperties(&p, dev);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipGetDeviceProperties");
+        snprintf(di.arch, sizeof di.arch, "%s", p.gcnArchName);
+        di.is_gfx950 = strncmp(p.gcnArchName, "gfx950", 6) == 0;
+        di.num_cu = p.multiProcessorCount;
+        di.checked = 1;
+    }
+    if (!di.is_gfx950)
+        return fail(GEMM_ERR_DEVICE, "device %d is %s, this library is built for gfx950", dev,
+                    di.arch);
+    *dev_out = dev;
+    if (info_out)
+        *info_out = di;
+    return GEMM_OK;
+}
+
+// Can the LDS-tiled kernel serve this descriptor (ignoring pointer alignment)?
+bool tiled_ok(const gemm_desc_t &d)
+{
+    // 64-byte K tiles; 32-bit buffer offsets cover 256 rows plus the K extent
+    const int eb = elem_bytes(d.a_type);
+    const int64_t lim = (int64_t)1 << 30;
+    return d.a_layout == GEMM_ROW_MAJOR && d.b_layout == GEMM_COL_MAJOR && d.K > 0 &&
+           (d.K * eb) % 64 == 0 && (d.lda * eb) % 16 == 0 && (d.ldb * eb) % 16 == 0 &&
+           d.lda * eb * 256 < lim && d.ldb * eb * 256 < lim;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+} // namespace
+
+extern "C" {
+
+const char *gemm_status_string(gemm_status_t s)
+{
+    switch (s) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_NULL_POINTER: return "GEMM_ERR_NULL_POINTER";
+    case GEMM_ERR_INVALID_VALUE: return "GEMM_ERR_INVALID_VALUE";
+    case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED";
+    case GEMM_ERR_MISALIGNED: return "GEMM_ERR_MISALIGNED";
+    case GEMM_ERR_NOT_SPARSE24: return "GEMM_ERR_NOT_SPARSE24";
+    case GEMM_ERR_DEVICE: return "GEMM_ERR_DEVICE";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
+    default: return "GEMM_ERR_UNKNOWN";
+    }
+}
+
+const char *gemm_last_error(void) { return g_last_error; }
+
+gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
+{
+    if (!desc)
+        return fail(GEMM_ERR_NULL_POINTER, "desc is NULL");
+    gemm_desc_t d = *desc;
+    if (d.M < 0 || d.N < 0 || d.K < 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "negative size M=%lld N=%lld K=%lld",
+                    (long long)d.M, (long long)d.N, (long long)d.K);
+    auto dtype_ok = [](int t) { return t >= GEMM_F16 && t <= GEMM_S32; };
+    if (!dtype_ok(d.a_type) || !dtype_ok(d.b_type) || !dtype_ok(d.d_type) ||
+        !(d.c_type == 0 || dtype_ok(d.c_type)))
+        return fail(GEMM_ERR_INVALID_VALUE, "unknown dtype code");
+    if ((d.a_layout != GEMM_ROW_MAJOR && d.a_layout != GEMM_COL_MAJOR) ||
+        (d.b_layout != GEMM_ROW_MAJOR && d.b_layout != GEMM_COL_MAJOR))
+        return fail(GEMM_ERR_INVALID_VALUE, "unknown layout code");
+    if (d.act != GEMM_ACT_NONE && d.act != GEMM_ACT_RELU)
+        return fail(GEMM_ERR_INVALID_VALUE, "unknown activation code");
+    if ((d.has_c != 0 && d.has_c != 1) || (d.has_bias != 0 && d.has_bias != 1) ||
+        (d.sparse_a != 0 && d.sparse_a != 1))
+        return fail(GEMM_ERR_INVALID_VALUE, "has_c / has_bias / sparse_a must be 0 or 1");
+    if (d.algo < GEMM_ALGO_AUTO || d.algo > GEMM_ALGO_TILED_256)
+        return fail(GEMM_ERR_INVALID_VALUE, "unknown algo code");
+    if (d.lda < 0 || d.ldb < 0 || d.ldc < 0 || d.ldd < 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "negative leading dimension");
+    if (!normalise(d))
+        return fail(GEMM_ERR_INVALID_VALUE, "leading dimension smaller than the matrix extent");
+
+    if (d.a_type == GEMM_S8 || d.b_type == GEMM_S8) {
+        if (d.a_type != GEMM_S8 || d.b_type != GEMM_S8)
+            return fail(GEMM_ERR_UNSUPPORTED, "s8 must be paired with s8");
+        if (!(d.c_type == GEMM_S32 || (d.c_type == 0 && !d.has_c)))
+            return fail(GEMM_ERR_UNSUPPORTED, "s8 inputs take an s32 C");
+        if (d.d_type != GEMM_S32)
+            return fail(GEMM_ERR_UNSUPPORTED, "s8 inputs produce s32 output");
+        if (d.alpha != 1.0f || d.has_bias || d.act != GEMM_ACT_NONE)
+            return fail(GEMM_ERR_UNSUPPORTED, "s32 output takes no alpha, bias or activation");
+    } else {
+        if (!is_float_in(d.a_type) || !is_float_in(d.b_type))
+            return fail(GEMM_ERR_UNSUPPORTED, "A/B must be f16, bf16, fp8 or s8");
+        if (op_kind(d.a_type, d.b_type) < 0)
+            return fail(GEMM_ERR_UNSUPPORTED, "A/B type pair not supported (f16/f16, "
+                                              "bf16/bf16 or fp8/fp8)");
+        if (!(d.c_type == GEMM_F32 || (d.c_type == 0 && !d.has_c)))
+            return fail(GEMM_ERR_UNSUPPORTED, "float inputs take an f32 C");
+        if (d.d_type != GEMM_F32 && d.d_type != GEMM_F16 && d.d_type != GEMM_BF16)
+            return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16 or bf16");
+    }
+    if (d.sparse_a) {
+        if (d.a_type != GEMM_F16 || d.b_type != GEMM_F16)
+            return fail(GEMM_ERR_UNSUPPORTED, "2:4 sparse A supports f16 x f16 only");
+        if (d.a_layout != GEMM_ROW_MAJOR)
+            return fail(GEMM_ERR_UNSUPPORTED, "2:4 sparse A must be row-major");
+        if (d.K % 4 != 0)
+            return fail(GEMM_ERR_UNSUPPORTED, "2:4 sparse A needs K %% 4 == 0");
+        if (d.lda != d.K)
+            return fail(GEMM_ERR_UNSUPPORTED, "2:4 sparse A must be packed (lda == K)");
+    }
+    return ok();
+}
+
+gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
+{
+    if (!out)
+        return fail(GEMM_ERR_NULL_POINTER, "out is NULL");
+    *out = nullptr;
+    gemm_status_t st = gemm_validate_desc(desc);
+    if (st != GEMM_OK)
+        return st;
+    gemm_desc_t d = *desc;
+    normalise(d);
+    int dev = 0;
+    DeviceInfo di;
+    st = check_device(&dev, &di);
+    if (st != GEMM_OK)
+        return st;
+
+    gemm_plan_t *p = new (std::nothrow) gemm_plan_t();
+    if (!p)
+        return fail(GEMM_ERR_INVALID_VALUE, "out of host memory");
+    p->d = d;
+    p->device = dev;
+    p->op = op_kind(d.a_type, d.b_type);
+    p->fallback = KF_GENERIC;
+
+    if (d.sparse_a) {
+        const bool fast = d.b_layout == GEMM_COL_MAJOR && d.K % 64 == 0 && d.ldb % 8 == 0;
+        int fam = -1;
+        switch (d.algo) {
+        case GEMM_ALGO_AUTO: fam = fast ? KF_SPARSE_TILED : KF_SPARSE_GENERIC; break;
+        case GEMM_ALGO_TILED:
+        case GEMM_ALGO_TILED_256: fam = fast ? KF_SPARSE_TILED : -1; break;
+        case GEMM_ALGO_GENERIC: fam = KF_SPARSE_GENERIC; break;
+        default: fam = -1;
+        }
+        if (fam < 0) {
+            delete p;
+            return fail(GEMM_ERR_UNSUPPORTED, "requested algorithm cannot serve this sparse problem");
+        }
+        p->family = fam;
+        p->fallback = KF_SPARSE_GENERIC;
+        snprintf(p->name, sizeof p->name, "%s_f16",
+                 fam == KF_SPARSE_TILED ? "sparse24_tiled" : "sparse24_generic");
+        *out = p;
+        return ok();
+    }
+
+    const bool tiled = tiled_ok(d);
+    int fam = -1;
+    const int64_t big_tiles = ceil_div(d.M, 256) * ceil_div(d.N, 256);
+    const int auto_tiled = big_tiles >= di.num_cu ? KF_TILED_256 : KF_TILED_128;
+    switch (d.algo) {
+    case GEMM_ALGO_AUTO: fam = tiled ? auto_tiled : KF_GENERIC; break;
+    case GEMM_ALGO_TILED: fam = tiled ? auto_tiled : -1; break;
+    case GEMM_ALGO_TILED_128: fam = tiled ? KF_TILED_128 : -1; break;
+    case GEMM_ALGO_TILED_256: fam = tiled ? KF_TILED_256 : -1; break;
+    case GEMM_ALGO_GENERIC: fam = KF_GENERIC; break;
+    default: fam = -1;
+    }
+    if (fam < 0) {
+        delete p;
+        return fail(GEMM_ERR_UNSUPPORTED, "requested algorithm cannot serve this problem");
+    }
+    p->family = fam;
+    const char *fname = fam == KF_TILED_256 ? "tiled256" : fam == KF_TILED_128 ? "tiled128"
+                                                                             : "generic";
+    snprintf(p->name, sizeof p->name, "%s_%s", fname, op_name(p->op));
+    *out = p;
+    return ok();
+}
+
+gemm_status_t gemm_plan_destroy(gemm_plan_t *plan)
+{
+    delete plan;
+    return ok();
+}
+
+gemm_status_t gemm_plan_describe(const gemm_plan_t *plan, char *buf, size_t len)
+{
+    if (!plan || !buf)
+        return fail(GEMM_ERR_NULL_POINTER, "plan or buf is NULL");
+    if (len == 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "len is 0");
+    snprintf(buf, len, "%s", plan->name);
+    return ok();
+}
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static gemm_status_t check_epilogue_ptrs(const gemm_desc_t &d, const void *C, const void *bias,
+                                         const void *D)
+{
+    if (!D)
+        return fail(GEMM_ERR_NULL_POINTER, "D is NULL");
+    if (d.has_c && !C)
+        return fail(GEMM_ERR_NULL_POINTER, "C is NULL but the plan reads C");
+    if (d.has_bias && !bias)
+        return fail(GEMM_ERR_NULL_POINTER, "bias is NULL but the plan adds a bias");
+    if ((d.has_c && !aligned(C, 4)) || (d.has_bias && !aligned(bias, 4)) ||
+        !aligned(D, elem_bytes(d.d_type)))
+        return fail(GEMM_ERR_MISALIGNED, "C, bias or D not aligned to its element size");
+    return GEMM_OK;
+}
+
+static EpiArgs make_epi(const gemm_desc_t &d, const void *C, const void *bias, void *D)
+{
+    EpiArgs e;
+    e.M = d.M;
+    e.N = d.N;
+    e.C = d.has_c ? C : nullptr;
+    e.ldc = d.ldc;
+    e.bias = d.has_bias ? (const float *)bias : nullptr;
+    e.alpha = d.alpha;
+    e.relu = d.act == GEMM_ACT_RELU;
+    e.d_kind = out_kind(d.d_type);
+    e.D = D;
+    e.ldd = d.ldd;
+    return e;
+}
+
+gemm_status_t gemm_run(const gemm_plan_t *plan, const void *A, const void *B, const void *C,
+                       const void *bias, void *D, gemm_stream_t stream)
+{
+    if (!plan)
+        return fail(GEMM_ERR_NULL_POINTER, "plan is NULL");
+    const gemm_desc_t &d = plan->d;
+    if (d.sparse_a)
+        return fail(GEMM_ERR_UNSUPPORTED, "plan is for 2:4 sparse A: use gemm_sparse24_run");
+    if (d.M == 0 || d.N == 0)
+        return ok();
+    if (d.K > 0 && (!A || !B))
+        return fail(GEMM_ERR_NULL_POINTER, "A or B is NULL");
+    gemm_status_t st = check_epilogue_ptrs(d, C, bias, D);
+    if (st != GEMM_OK)
+        return st;
+    const int eb = elem_bytes(d.a_type);
+    if (d.K > 0 && (!aligned(A, eb) || !aligned(B, eb)))
+        return fail(GEMM_ERR_MISALIGNED, "A or B not aligned to its element size");
+
+    GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.K = d.K;
+    if (d.a_layout == GEMM_ROW_MAJOR) {
+        g.a_rs = d.lda;
+        g.a_cs = 1;
+    } else {
+        g.a_rs = 1;
+        g.a_cs = d.lda;
+    }
+    if (d.b_layout == GEMM_COL_MAJOR) {
+        g.b_rs = 1;
+        g.b_cs = d.ldb;
+    } else {
+        g.b_rs = d.ldb;
+        g.b_cs = 1;
+    }
+    g.e = make_epi(d, C, bias, D);
+
+    int fam = plan->family;
+    if (fam != KF_GENERIC && (!aligned(A, 16) || !aligned(B, 16)))
+        fam = plan->fallback;
+    hipError_t e = launch_dense(fam, plan->op, g, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "kernel launch");
+    return ok();
+}
+
+gemm_status_t gemm_sparse24_sizes(int64_t M, int64_t K, int32_t a_type, size_t *values_bytes,
+                                  size_t *meta_bytes)
+{
+    if (!values_bytes || !meta_bytes)
+        return fail(GEMM_ERR_NULL_POINTER, "output pointer is NULL");
+    if (M < 0 || K < 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "negative size");
+    if (a_type != GEMM_F16)
+        return fail(GEMM_ERR_UNSUPPORTED, "2:4 compression supports f16 only");
+    if (K % 4)
+        return fail(GEMM_ERR_UNSUPPORTED, "K must be a multiple of 4");
+    *values_bytes = (size_t)M * (size_t)(K / 2) * 2;
+    *meta_bytes = (size_t)M * (size_t)((K + 31) / 32) * 4;
+    return ok();
+}
+
+gemm_status_t gemm_sparse24_compress(int64_t M, int64_t K, int32_t a_type, const void *A,
+                                     void *values, uint32_t *meta, gemm_stream_t stream)
+{
+    size_t vb = 0, mb = 0;
+    gemm_status_t st = gemm_sparse24_sizes(M, K, a_type, &vb, &mb);
+    if (st != GEMM_OK)
+        return st;
+    if (M == 0 || K == 0)
+        return ok();
+    if (!A || !values || !meta)
+        return fail(GEMM_ERR_NULL_POINTER, "A, values or meta is NULL");
+    if (!aligned(A, 8) || !aligned(values, 4) || !aligned(meta, 4))
+        return fail(GEMM_ERR_MISALIGNED, "A must be 8-byte, values and meta 4-byte aligned");
+    int dev = 0;
+    st = check_device(&dev, nullptr);
+    if (st != GEMM_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    int *flag = nullptr;
+    hipError_t e = hipMalloc((void **)&flag, sizeof(int));
+    if (e != hipSuccess)
+        return hip_fail(e, "hipMalloc(flag)");
+    int host_flag = 0;
+    e = hipMemsetAsync(flag, 0, sizeof(int), s);
+    if (e == hipSuccess)
+        e = launch_sparse24_compress(M, K, (const uint16_t *)A, (uint16_t *)values, meta, flag, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);
+    hipError_t ef = hipFree(flag);
+    if (e != hipSuccess)
+        return hip_fail(e, "sparse24 compress");
+    if (ef != hipSuccess)
+        return hip_fail(ef, "hipFree(flag)");
+    if (host_flag)
+        return fail(GEMM_ERR_NOT_SPARSE24,
+                    "A has a group of 4 with more than two non-zeros (first such row: %d)",
+                    0x7fffffff - host_flag);
+    return ok();
+}
+
+gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, const uint32_t *meta,
+                                const void *B, const void *C, const void *bias, void *D,
+                                gemm_stream_t stream)
+{
+    if (!plan)
+        return fail(GEMM_ERR_NULL_POINTER, "plan is NULL");
+    const gemm_desc_t &d = plan->d;
+    if (!d.sparse_a)
+        return fail(GEMM_ERR_UNSUPPORTED, "plan is for dense A: use gemm_run");
+    if (d.M == 0 || d.N == 0)
+        return ok();
+    if (d.K > 0 && (!values || !meta || !B))
+        return fail(GEMM_ERR_NULL_POINTER, "values, meta or B is NULL");
+    gemm_status_t st = check_epilogue_ptrs(d, C, bias, D);
+    if (st != GEMM_OK)
+        return st;
+    if (d.K > 0 && (!aligned(values, 2) || !aligned(meta, 4) || !aligned(B, 2)))
+        return fail(GEMM_ERR_MISALIGNED, "values, meta or B not aligned to its element size");
+    SparseArgs a;
+    a.values = (const uint16_t *)values;
+    a.meta = meta;
+    a.B = B;
+    a.K = d.K;
+    if (d.b_layout == GEMM_COL_MAJOR) {
+        a.b_rs = 1;
+        a.b_cs = d.ldb;
+    } else {
+        a.b_rs = d.ldb;
+        a.b_cs = 1;
+    }
+    a.e = make_epi(d, C, bias, D);
+    int fam = plan->family;
+    if (fam == KF_SPARSE_TILED && (!aligned(values, 16) || !aligned(B, 16) || !aligned(meta, 16)))
+        fam = plan->fallback;
+    hipError_t e = launch_sparse(fam, a, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "kernel launch");
+    return ok();
+}
+
+} // extern "C"

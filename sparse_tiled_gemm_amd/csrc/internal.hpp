@@ -1,0 +1,50 @@
+// Library-internal declarations shared by the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm.h"
+#include "kernel_args.hpp"
+
+namespace stg {
+
+// MFMA operand-pair kinds.
+enum OpKind {
+    OPK_F16 = 0,
+    OPK_BF16,
+    OPK_F8_E4E4,
+    OPK_F8_E4E5,
+    OPK_F8_E5E4,
+    OPK_F8_E5E5,
+    OPK_S8,
+    OPK_COUNT
+};
+
+// Kernel families a plan can select.
+enum KernelFamily {
+    KF_GENERIC = 0, // any layout / shape / alignment
+    KF_TILED_256,   // 256 x 256 workgroup tile, LDS double buffer
+    KF_TILED_128,   // 128 x 128 workgroup tile, LDS double buffer
+    KF_SKINNY,      // M <= 64, bandwidth-oriented
+    KF_SPARSE_GENERIC,
+    KF_SPARSE_TILED
+};
+
+hipError_t launch_dense(int family, int op, const GemmArgs &g, hipStream_t s);
+hipError_t launch_sparse(int family, const SparseArgs &a, hipStream_t s);
+// Compressor: writes values/meta; *flag (device int, zeroed by the caller)
+// becomes 0x7fffffff - r for the lowest row r holding a group with more than
+// two non-zeros, and stays 0 otherwise.
+hipError_t launch_sparse24_compress(int64_t M, int64_t K, const uint16_t *A, uint16_t *values,
+                                    uint32_t *meta, int *flag, hipStream_t s);
+
+} // namespace stg
+
+struct gemm_plan {
+    gemm_desc_t d;   // normalised: packed leading dimensions filled in
+    int op;          // stg::OpKind
+    int family;      // stg::KernelFamily
+    int fallback;    // family used when run-time alignment rules out `family`
+    int device;      // HIP device the plan was made on
+    char name[96];
+};

@@ -1,0 +1,45 @@
+// Argument blocks passed by value to the GEMM kernels (host and device).
+#pragma once
+
+#include <stdint.h>
+
+namespace stg {
+
+enum OutKind { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2, OUT_S32 = 3 };
+
+// Epilogue inputs.  C == nullptr: no C term; bias == nullptr: no bias.
+struct EpiArgs {
+    int64_t M, N;
+    const void *C;
+    int64_t ldc;
+    const float *bias;
+    float alpha;
+    int relu;
+    int d_kind; // OutKind
+    void *D;
+    int64_t ldd;
+};
+
+// Dense operands.  Element (m,k) of A is at A[m*a_rs + k*a_cs] and element
+// (k,n) of B at B[k*b_rs + n*b_cs] (strides in elements).  The K-contiguous
+// kernels use only lda = a_rs and ldb = b_cs.
+struct GemmArgs {
+    const void *A;
+    const void *B;
+    int64_t K;
+    int64_t a_rs, a_cs;
+    int64_t b_rs, b_cs;
+    EpiArgs e;
+};
+
+// 2:4-compressed A: values [M, K/2] fp16, meta [M, ceil(K/32)] u32.
+struct SparseArgs {
+    const uint16_t *values;
+    const uint32_t *meta;
+    const void *B; // element (k,n) at B[k*b_rs + n*b_cs]
+    int64_t K;
+    int64_t b_rs, b_cs;
+    EpiArgs e;
+};
+
+} // namespace stg

@@ -1,0 +1,98 @@
+"""Parity criteria between a GPU result and the oracle.
+
+- Integer outputs: bit-exact.
+- fp32 outputs: |D - Y| <= tol * |alpha| * S + ulp32(Y), where Y is the
+  oracle's fp64 result before the cast and S = sum_k |a b| + |c| (with alpha
+  = 1 and no bias this is the normalised bound max |D - D_ref| / S <= tol).
+- fp16 / bf16 outputs: within 1 ulp of the oracle's correctly rounded value
+  (distance of the ordered bit patterns), or, where fp32 accumulation error
+  alone can exceed one output ulp (results near 0),
+  |D - Y| <= ulp_out(Y) + tol * |alpha| * S.
+tol = 1e-5 for fp16/bf16 inputs and 1e-4 for fp8 inputs.
+"""
+import numpy as np
+
+from exact import lib_decode
+
+TOL = {"f16": 1e-5, "bf16": 1e-5, "e4m3": 1e-4, "e5m2": 1e-4}
+
+
+def ordered16(bits):
+    b = np.asarray(bits).astype(np.uint16).astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def ulp16(y, d_type):
+    """Spacing of fp16 / bf16 values at |y|."""
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    fbits, emin = (10, -14) if d_type == "f16" else (7, -126)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, emin)
+    return np.ldexp(1.0, (e - fbits).astype(np.int64))
+
+
+def ulp32(y):
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.ldexp(1.0, (np.maximum(e, -126) - 23).astype(np.int64))
+
+
+class Result:
+    def __init__(self, ok, n, max_norm_err=0.0, n_second_clause=0, n_bad=0, detail=""):
+        self.ok, self.n, self.max_norm_err = ok, n, max_norm_err
+        self.n_second_clause, self.n_bad, self.detail = n_second_clause, n_bad, detail
+
+    def __repr__(self):
+        return ("Result(ok=%s, n=%d, max_norm_err=%.3g, second_clause=%d, bad=%d %s)" %
+                (self.ok, self.n, self.max_norm_err, self.n_second_clause, self.n_bad,
+                 self.detail))
+
+
+def check(D, d_type, D_ref, Y, S, in_type, alpha=1.0):
+    """D, D_ref: raw output bits (same shape); Y, S: oracle fp64 arrays."""
+    D = np.asarray(D)
+    n = D.size
+    if d_type == "s32":
+        bad = np.asarray(D).view(np.int32) != np.asarray(D_ref).view(np.int32)
+        nb = int(bad.sum())
+        det = ""
+        if nb:
+            i = np.flatnonzero(bad.reshape(-1))[0]
+            det = "first mismatch at flat %d: %d vs %d" % (
+                i, D.reshape(-1).view(np.int32)[i], np.asarray(D_ref).reshape(-1).view(np.int32)[i])
+        return Result(nb == 0, n, 0.0, 0, nb, det)
+    tol = TOL[in_type]
+    Y = np.asarray(Y, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    scale = abs(alpha) * S
+    with np.errstate(divide="ignore", invalid="ignore"):
+        if d_type == "f32":
+            d = np.asarray(D, dtype=np.float32).astype(np.float64)
+            err = np.abs(d - Y)
+            ok = err <= tol * scale + ulp32(Y)
+            norm = np.where(scale > 0, err / np.where(scale > 0, scale, 1), np.where(err > 0, np.inf, 0))
+            nb = int((~ok).sum())
+            det = ""
+            if nb:
+                i = np.flatnonzero(~ok.reshape(-1))[0]
+                det = "first bad flat %d: D=%r Y=%r S=%r" % (i, d.reshape(-1)[i], Y.reshape(-1)[i],
+                                                            S.reshape(-1)[i])
+            return Result(nb == 0, n, float(norm.max()) if n else 0.0, 0, nb, det)
+        d = lib_decode(d_type, np.asarray(D).astype(np.uint16))
+        dist = np.abs(ordered16(D) - ordered16(D_ref))
+        first = dist <= 1
+        err = np.abs(d - Y)
+        second = err <= ulp16(Y, d_type) + tol * scale
+        ok = first | second
+        norm = np.where(scale > 0, err / np.where(scale > 0, scale, 1), 0.0)
+        nb = int((~ok).sum())
+        det = ""
+        if nb:
+            i = np.flatnonzero(~ok.reshape(-1))[0]
+            det = "first bad flat %d: D=%r Dref=%r Y=%r S=%r" % (
+                i, d.reshape(-1)[i], lib_decode(d_type, np.asarray(D_ref).astype(np.uint16)).reshape(-1)[i],
+                Y.reshape(-1)[i], S.reshape(-1)[i])
+        return Result(nb == 0, n, float(norm.max()) if n else 0.0, int((~first & second).sum()),
+                      nb, det)

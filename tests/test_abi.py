@@ -1,0 +1,101 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+declared in include/gemm.h, and gemm_validate_desc (a pure host function)
+maps bad descriptors to the documented status codes.  No GPU needed."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_tiled_gemm_amd import gemm as G
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "gemm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = G.load()
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert "gemm_sparse24_run" in names and "gemm_plan" in names
+
+
+def test_status_strings():
+    for code, name in [(0, "GEMM_OK"), (3, "GEMM_ERR_UNSUPPORTED"), (5, "GEMM_ERR_NOT_SPARSE24")]:
+        assert G.gemm_status_string(code) == name
+
+
+def _ok(**kw):
+    base = dict(M=64, N=64, K=64, a_type="bf16", b_type="bf16", d_type="bf16")
+    base.update(kw)
+    return G.make_desc(**base)
+
+
+@pytest.mark.parametrize("desc,status", [
+    (dict(), G.GEMM_OK),
+    (dict(a_type="f16", b_type="f16", d_type="f32"), G.GEMM_OK),
+    (dict(a_type="e4m3", b_type="e5m2", d_type="f16", has_c=False, has_bias=True, alpha=0.5,
+          act="relu"), G.GEMM_OK),
+    (dict(a_type="s8", b_type="s8", d_type="s32"), G.GEMM_OK),
+    (dict(M=-1), G.GEMM_ERR_INVALID_VALUE),
+    (dict(K=-5), G.GEMM_ERR_INVALID_VALUE),
+    (dict(lda=10), G.GEMM_ERR_INVALID_VALUE),          # row-major A needs lda >= K
+    (dict(ldb=3), G.GEMM_ERR_INVALID_VALUE),
+    (dict(ldd=63), G.GEMM_ERR_INVALID_VALUE),
+    (dict(a_type="s8", b_type="f16", d_type="f32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="f16", b_type="bf16", d_type="f32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="f16", b_type="e4m3", d_type="f32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="s8", b_type="s8", d_type="s32", alpha=2.0), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="s8", b_type="s8", d_type="s32", has_bias=True), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="s8", b_type="s8", d_type="s32", act="relu"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="s8", b_type="s8", d_type="f32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(d_type="s32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(d_type="e4m3"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(c_type="bf16"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(sparse_a=True), G.GEMM_ERR_UNSUPPORTED),     # sparse is f16 only
+    (dict(sparse_a=True, a_type="f16", b_type="f16", K=66), G.GEMM_ERR_UNSUPPORTED),
+    (dict(sparse_a=True, a_type="f16", b_type="f16", a_layout="col"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(sparse_a=True, a_type="f16", b_type="f16", d_type="f32"), G.GEMM_OK),
+])
+def test_validate_desc(desc, status):
+    assert G.gemm_validate_desc(_ok(**desc)) == status, G.gemm_last_error()
+
+
+def test_validate_bad_enums_and_null():
+    d = _ok()
+    d.a_type = 99
+    assert G.gemm_validate_desc(d) == G.GEMM_ERR_INVALID_VALUE
+    d = _ok()
+    d.act = 7
+    assert G.gemm_validate_desc(d) == G.GEMM_ERR_INVALID_VALUE
+    d = _ok()
+    d.algo = 42
+    assert G.gemm_validate_desc(d) == G.GEMM_ERR_INVALID_VALUE
+    assert G.gemm_validate_desc(None) == G.GEMM_ERR_NULL_POINTER
+    assert "NULL" in G.gemm_last_error()
+
+
+def test_sparse24_sizes():
+    vb, mb = G.gemm_sparse24_sizes(8192, 8192)
+    assert vb == 8192 * 4096 * 2 and mb == 8192 * 256 * 4
+    vb, mb = G.gemm_sparse24_sizes(3, 36)
+    assert vb == 3 * 18 * 2 and mb == 3 * 2 * 4
+    with pytest.raises(G.GemmError) as e:
+        G.gemm_sparse24_sizes(4, 6)
+    assert e.value.status == G.GEMM_ERR_UNSUPPORTED
+    with pytest.raises(G.GemmError):
+        G.gemm_sparse24_sizes(4, 8, "bf16")
+
+
+def test_run_rejects_null_plan_without_gpu():
+    L = G.load()
+    assert L.gemm_run(None, None, None, None, None, None, None) == G.GEMM_ERR_NULL_POINTER
+    assert L.gemm_plan(None, ctypes.byref(ctypes.c_void_p())) == G.GEMM_ERR_NULL_POINTER

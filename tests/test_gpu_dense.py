@@ -1,0 +1,202 @@
+"""GPU parity of the dense kernels against the oracle, element by element,
+at sizes the oracle finishes in seconds that span several workgroup tiles
+with ragged M/N tails, for every input-type pair and kernel family, plus
+epilogue, layout, stride, alignment and degenerate-shape cases."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from checks import check
+from gpu_util import gpu_gemm, say, to_dev, empty_out
+from sparse_tiled_gemm_amd import gemm as G
+from sparse_tiled_gemm_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+CONV = {"f16": inputs.to_f16, "bf16": inputs.to_bf16, "e4m3": inputs.to_e4m3,
+        "e5m2": inputs.to_e5m2}
+PAIRS = [("f16", "f16"), ("bf16", "bf16"), ("e4m3", "e5m2"), ("e5m2", "e4m3"),
+         ("e4m3", "e4m3"), ("e5m2", "e5m2"), ("s8", "s8")]
+
+
+def make(a_type, b_type, M, N, K, seed, a_col=False, b_col=True, c=True, bias=False):
+    rng = np.random.default_rng(seed)
+    ashape = (K, M) if a_col else (M, K)
+    bshape = (N, K) if b_col else (K, N)
+    if a_type == "s8":
+        A = rng.integers(-128, 128, size=ashape, dtype=np.int8)
+        B = rng.integers(-128, 128, size=bshape, dtype=np.int8)
+        C = rng.integers(-(1 << 20), (1 << 20) + 1, size=(M, N), dtype=np.int32) if c else None
+        return A, B, C, None
+    sa = 16.0 if a_type.startswith("e") else 1.0
+    A = CONV[a_type](rng.standard_normal(ashape) * sa)
+    B = CONV[b_type](rng.standard_normal(bshape) * sa)
+    C = rng.uniform(-1, 1, size=(M, N)).astype(np.float32) if c else None
+    bv = rng.standard_normal(N).astype(np.float32) if bias else None
+    return A, B, C, bv
+
+
+def compare(orc, A, B, C, bias, M, N, K, a_type, b_type, d_type, algo, expect_kernel=None,
+            **kw):
+    say("case", a_type, b_type, d_type, (M, N, K), algo, kw.get("alpha", 1.0),
+        kw.get("relu", False), kw.get("a_col", False), kw.get("b_col", True))
+    D, name = gpu_gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, algo=algo, **kw)
+    if expect_kernel:
+        assert name.startswith(expect_kernel), name
+    okw = dict(a_col_major=kw.get("a_col", False), b_col_major=kw.get("b_col", True),
+               alpha=kw.get("alpha", 1.0), relu=kw.get("relu", False))
+    Dr, Y, S = orc.gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, **okw)
+    r = check(D, d_type, Dr, Y, S, a_type, kw.get("alpha", 1.0))
+    say("  ", name, r)
+    assert r.ok, r
+    return D, name
+
+
+@pytest.mark.parametrize("a_type,b_type", PAIRS)
+@pytest.mark.parametrize("algo,shape", [("tiled256", (600, 520, 256)),
+                                        ("tiled128", (300, 260, 192)),
+                                        ("generic", (129, 257, 96)),
+                                        ("generic", (17, 9, 20))])
+def test_dense_parity(orc, a_type, b_type, algo, shape):
+    M, N, K = shape
+    A, B, C, _ = make(a_type, b_type, M, N, K, seed=zlib.crc32(repr((a_type, b_type, shape)).encode()))
+    d_type = "s32" if a_type == "s8" else "f32"
+    compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, algo, expect_kernel=algo)
+
+
+@pytest.mark.parametrize("a_type,b_type", [("bf16", "bf16"), ("f16", "f16"), ("e4m3", "e5m2")])
+@pytest.mark.parametrize("d_type", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("algo", ["tiled128", "generic"])
+@pytest.mark.parametrize("epi", [dict(), dict(alpha=0.75), dict(bias=True, relu=True),
+                                 dict(alpha=-1.5, bias=True, c=False)])
+def test_epilogue_variants(orc, a_type, b_type, d_type, algo, epi):
+    M, N, K = 200, 136, 128
+    A, B, C, bias = make(a_type, b_type, M, N, K, seed=7, c=epi.get("c", True),
+                         bias=epi.get("bias", False))
+    if a_type.startswith("e"):
+        # keep fp16 outputs in range for fp8 inputs of magnitude ~16
+        epi = dict(epi)
+        epi["alpha"] = epi.get("alpha", 1.0) / 256.0
+    compare(orc, A, B, C, bias, M, N, K, a_type, b_type, d_type, algo, expect_kernel=algo,
+            alpha=epi.get("alpha", 1.0), relu=epi.get("relu", False))
+
+
+@pytest.mark.parametrize("algo", ["tiled256", "tiled128", "generic"])
+@pytest.mark.parametrize("a_type,b_type,d_type", [("bf16", "bf16", "bf16"), ("f16", "f16", "f16"),
+                                                  ("e4m3", "e5m2", "f16"),
+                                                  ("e4m3", "e5m2", "bf16")])
+def test_epilogue_bit_exact(orc, algo, a_type, b_type, d_type):
+    """The fused epilogue equals the oracle's fp32 epilogue applied to the
+    same kernel's fp32 accumulator output, bit for bit (same plan family, so
+    the same summation order)."""
+    M, N, K = 384, 320, 256
+    A, B, C, bias = make(a_type, b_type, M, N, K, seed=11, bias=True)
+    alpha = 0.3 if not a_type.startswith("e") else 0.3 / 256.0
+    T, n1 = gpu_gemm(A, B, C, None, M, N, K, a_type, b_type, "f32", algo=algo)
+    D, n2 = gpu_gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, algo=algo, alpha=alpha,
+                     relu=True)
+    assert n1.split("_")[0] == n2.split("_")[0] == algo
+    ref = orc.epilogue_f32(T, alpha, bias, True, d_type)
+    mism = int((D != ref).sum())
+    say("epilogue", algo, a_type, d_type, "mismatches", mism)
+    assert mism == 0
+
+
+@pytest.mark.parametrize("a_type,b_type", [("f16", "f16"), ("bf16", "bf16"), ("e4m3", "e5m2"),
+                                           ("s8", "s8")])
+@pytest.mark.parametrize("a_col,b_col", [(False, False), (True, True), (True, False)])
+def test_other_layouts(orc, a_type, b_type, a_col, b_col):
+    M, N, K = 70, 90, 100
+    A, B, C, _ = make(a_type, b_type, M, N, K, seed=3, a_col=a_col, b_col=b_col)
+    d_type = "s32" if a_type == "s8" else "f32"
+    compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, "auto", expect_kernel="generic",
+            a_col=a_col, b_col=b_col)
+
+
+@pytest.mark.parametrize("a_type,b_type", [("bf16", "bf16"), ("s8", "s8"), ("e4m3", "e5m2")])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 4096, 64), (64, 1, 64), (5, 7, 1000),
+                                   (256, 256, 100), (33, 65, 4)])
+def test_edge_shapes(orc, a_type, b_type, shape):
+    M, N, K = shape
+    A, B, C, _ = make(a_type, b_type, M, N, K, seed=5)
+    d_type = "s32" if a_type == "s8" else "f32"
+    compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, "auto")
+
+
+@pytest.mark.parametrize("a_type", ["bf16", "s8"])
+def test_k_zero_gives_epilogue_of_c(orc, a_type):
+    M, N = 40, 24
+    A, B, C, _ = make(a_type, a_type, M, N, 1, seed=9)
+    d_type = "s32" if a_type == "s8" else "f32"
+    D, _ = gpu_gemm(A[:, :0], B[:, :0], C, None, M, N, 0, a_type, a_type, d_type)
+    assert np.array_equal(D, C)
+
+
+def test_padded_leading_dimensions(orc):
+    M, N, K = 300, 200, 256
+    lda, ldb, ldc, ldd = K + 64, K + 32, N + 8, N + 24
+    rng = np.random.default_rng(21)
+    Ap = inputs.to_bf16(rng.standard_normal((M, lda)))
+    Bp = inputs.to_bf16(rng.standard_normal((N, ldb)))
+    Cp = rng.uniform(-1, 1, (M, ldc)).astype(np.float32)
+    for algo in ["tiled128", "tiled256", "generic"]:
+        say("padded", algo)
+        D, name = gpu_gemm(Ap, Bp, Cp, None, M, N, K, "bf16", "bf16", "bf16", algo=algo,
+                           lda=lda, ldb=ldb, ldc=ldc, ldd=ldd)
+        assert name.startswith(algo)
+        Dr, Y, S = orc.gemm(np.ascontiguousarray(Ap[:, :K]), np.ascontiguousarray(Bp[:, :K]),
+                            np.ascontiguousarray(Cp[:, :N]), None, M, N, K, "bf16", "bf16", "bf16")
+        r = check(D, "bf16", Dr, Y, S, "bf16")
+        assert r.ok, r
+
+
+def test_misaligned_operands_fall_back(orc):
+    """A and B offset by one element: the tiled plan falls back to the
+    generic kernel at run time and the result is still right."""
+    M, N, K = 256, 192, 128
+    A, B, C, _ = make("bf16", "bf16", M, N, K, seed=4)
+    tA = to_dev(np.concatenate([np.zeros(1, np.uint16), A.reshape(-1)]))
+    tB = to_dev(np.concatenate([np.zeros(1, np.uint16), B.reshape(-1)]))
+    desc = G.make_desc(M, N, K, "bf16", "bf16", "f32", algo="tiled128")
+    plan = G.gemm_plan(desc)
+    D = empty_out(M, N, "f32")
+    G.gemm_run(plan, tA.data_ptr() + 2, tB.data_ptr() + 2, to_dev(C), None, D)
+    torch.cuda.synchronize()
+    D = D.cpu().numpy().view(np.float32).reshape(M, N)
+    Dr, Y, S = orc.gemm(A, B, C, None, M, N, K, "bf16", "bf16", "f32")
+    assert check(D, "f32", Dr, Y, S, "bf16").ok
+
+
+def test_in_place_accumulate_d_equals_c(orc):
+    M, N, K = 256, 256, 128
+    A, B, C, _ = make("f16", "f16", M, N, K, seed=6)
+    tC = to_dev(C)
+    D, _ = gpu_gemm(A, B, None, None, M, N, K, "f16", "f16", "f32", c_dev=tC, out=tC)
+    Dr, Y, S = orc.gemm(A, B, C, None, M, N, K, "f16", "f16", "f32")
+    assert check(D, "f32", Dr, Y, S, "f16").ok
+
+
+@pytest.mark.parametrize("algo", ["tiled128", "generic"])
+def test_int32_wraps_modulo_2_32(orc, algo):
+    """127*127 summed over K = 140032 exceeds 2^31: the int32 result wraps."""
+    M, N, K = 64, 64, 140032
+    A = np.full((M, K), 127, np.int8)
+    B = np.full((N, K), 127, np.int8)
+    B[1::2] = -128
+    C = np.zeros((M, N), np.int32)
+    D, name = gpu_gemm(A, B, C, None, M, N, K, "s8", "s8", "s32", algo=algo)
+    Dr, _, _ = orc.gemm(A, B, C, None, M, N, K, "s8", "s8", "s32")
+    assert np.array_equal(D, Dr)
+    assert 127 * 127 * K > 2 ** 31 and D[0, 0] == 127 * 127 * K - 2 ** 32
+
+
+def test_plan_does_not_depend_on_epilogue():
+    names = set()
+    for d_type in ["f32", "f16", "bf16"]:
+        for bias, relu in [(False, False), (True, True)]:
+            d = G.make_desc(8192, 8192, 8192, "bf16", "bf16", d_type, has_bias=bias,
+                            act="relu" if relu else "none")
+            names.add(G.gemm_plan(d).name)
+    assert len(names) == 1, names

@@ -1,0 +1,96 @@
+"""GPU parity of the 2:4 path: the compressor's bytes against the oracle's
+compressor (bit-exact), its rejection of groups with more than two
+non-zeros, and sparse GEMM results against the oracle's dense GEMM on the
+logical A."""
+import numpy as np
+import pytest
+import torch
+
+from checks import check
+from gpu_util import gpu_compress, gpu_sparse_gemm, say, to_dev
+from sparse_tiled_gemm_amd import gemm as G
+from sparse_tiled_gemm_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("M,K", [(1, 4), (3, 36), (130, 200), (257, 1024), (64, 4100)])
+def test_compress_matches_oracle(orc, M, K):
+    p = inputs.sparse24_f16(M=M, N=4, K=K)
+    say("compress", M, K)
+    vals, meta, vb, mb = gpu_compress(p["A_logical"])
+    rv, rm = orc.sparse24_compress(p["A_logical"])
+    assert np.array_equal(vals.cpu().numpy()[:vb].view(np.uint16).reshape(rv.shape), rv)
+    assert np.array_equal(meta.cpu().numpy()[:mb].view(np.uint32).reshape(rm.shape), rm)
+
+
+def test_compress_fewer_than_two_nonzeros(orc):
+    rng = np.random.default_rng(2)
+    M, K = 64, 256
+    p = inputs.sparse24_f16(M=M, N=4, K=K)
+    A = p["A_logical"].copy()
+    # zero out one or both kept values in a third of the groups; write -0 in some
+    g = A.reshape(M, K // 4, 4)
+    kill = rng.random((M, K // 4, 4)) < 0.3
+    g[kill & (g != 0)] = 0
+    g[(rng.random(g.shape) < 0.1) & (g == 0)] = 0x8000
+    A = g.reshape(M, K)
+    vals, meta, vb, mb = gpu_compress(A)
+    rv, rm = orc.sparse24_compress(A)
+    assert np.array_equal(vals.cpu().numpy()[:vb].view(np.uint16).reshape(rv.shape), rv)
+    assert np.array_equal(meta.cpu().numpy()[:mb].view(np.uint32).reshape(rm.shape), rm)
+
+
+def test_compress_rejects_three_nonzeros():
+    p = inputs.sparse24_f16(M=32, N=4, K=64)
+    A = p["A_logical"].copy()
+    A[17, 8:12] = inputs.to_f16(np.array([1.0, 2.0, 3.0, 0.0]))
+    with pytest.raises(G.GemmError) as e:
+        gpu_compress(A)
+    assert e.value.status == G.GEMM_ERR_NOT_SPARSE24
+    assert "17" in str(e.value)
+
+
+@pytest.mark.parametrize("algo,shape", [("tiled", (600, 520, 256)), ("tiled", (256, 256, 64)),
+                                        ("generic", (129, 257, 96)), ("generic", (17, 9, 20)),
+                                        ("auto", (100, 100, 100))])
+def test_sparse_parity(orc, algo, shape):
+    M, N, K = shape
+    p = inputs.sparse24_f16(M=M, N=N, K=K)
+    say("sparse", algo, shape)
+    vals, meta, _, _ = gpu_compress(p["A_logical"])
+    D, name = gpu_sparse_gemm(vals, meta, p["B"], p["C"], M, N, K, algo=algo)
+    say("  ", name)
+    if algo != "auto":
+        assert name.startswith("sparse24_" + algo)
+    Dr, Y, S = orc.gemm(p["A_logical"], p["B"], p["C"], None, M, N, K, "f16", "f16", "f32")
+    r = check(D, "f32", Dr, Y, S, "f16")
+    say("  ", r)
+    assert r.ok, r
+
+
+@pytest.mark.parametrize("algo", ["tiled", "generic"])
+@pytest.mark.parametrize("d_type", ["bf16", "f16"])
+def test_sparse_epilogue(orc, algo, d_type):
+    M, N, K = 300, 264, 128
+    p = inputs.sparse24_f16(M=M, N=N, K=K)
+    bias = np.random.default_rng(3).standard_normal(N).astype(np.float32)
+    vals, meta, _, _ = gpu_compress(p["A_logical"])
+    D, name = gpu_sparse_gemm(vals, meta, p["B"], p["C"], M, N, K, d_type, algo=algo, bias=bias,
+                              alpha=0.5, relu=True)
+    Dr, Y, S = orc.gemm(p["A_logical"], p["B"], p["C"], bias, M, N, K, "f16", "f16", d_type,
+                        alpha=0.5, relu=True)
+    r = check(D, d_type, Dr, Y, S, "f16", 0.5)
+    assert r.ok, r
+
+
+def test_sparse_row_major_b(orc):
+    M, N, K = 96, 80, 64
+    p = inputs.sparse24_f16(M=M, N=N, K=K)
+    Brow = np.ascontiguousarray(p["B"].T)  # [K, N]
+    vals, meta, _, _ = gpu_compress(p["A_logical"])
+    D, name = gpu_sparse_gemm(vals, meta, Brow, p["C"], M, N, K, b_col=False)
+    assert name.startswith("sparse24_generic")
+    Dr, Y, S = orc.gemm(p["A_logical"], Brow, p["C"], None, M, N, K, "f16", "f16", "f32",
+                        b_col_major=False)
+    assert check(D, "f32", Dr, Y, S, "f16").ok
