@@ -144,10 +144,14 @@ __device__ inline void tile_coords_sp(int id, int tiles_m, int tiles_n, int &tm,
     tn = in / gsize;
 }
 
-// v_smfmac_f32_32x32x32_f16: lane l supplies, for row l%32 of A, the 8 kept
-// values of logical K slice (l/32)*16 .. +15 (4 groups), their 16-bit
-// position code (4 nibbles, group order, i0 in the low 2 bits), and for
-// column l%32 of B the 16 dense values of the same K slice.
+// v_smfmac_f32_32x32x32_f16 covers 32 logical K positions k0..k0+31.  Lane l
+// (h = l / 32) supplies, for row l % 32 of A, the 8 kept values of logical K
+// 16h .. 16h+15 (4 groups, in group order) and their position code in the
+// low 16 bits of the index register (nibble g = group g, first position in
+// the low 2 bits; abid selects the register's upper half instead); for
+// column l % 32 of B it supplies K 8h .. 8h+7 in elements 0..7 and
+// 16+8h .. 16+8h+7 in elements 8..15.  (Measured on gfx950 with single-
+// instruction probes; it is exactly this library's nibble packing.)
 __device__ inline f16_t smfmac32(const uint32_t *a, const uint32_t *b, int idx, f16_t c)
 {
     h8_t va = __builtin_bit_cast(h8_t, *(const u4_t *)a);
@@ -265,14 +269,15 @@ __global__ __launch_bounds__(256, 1) void k_sparse_tiled(SparseArgs a, int tiles
                 const uint32_t w = *(const uint32_t *)(st + OFF_M + r * AMB + s * 4);
                 ix[i] = (int)((w >> (16 * half)) & 0xFFFFu);
             }
-            // B: 32 bytes at byte s*64 + half*32
-            const int cb = (s * 64 + half * 32) >> 4;
+            // B: 16-byte chunks 4s + half (K 8h..8h+7 of the slice) and
+            // 4s + half + 2 (K 16+8h..)
+            const int cb = 4 * s + half;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int r = brow + j * 32;
                 *(u4_t *)&bf[j][0] = *(const u4_t *)(st + OFF_B + r * BB + ((cb ^ swz128(r)) << 4));
                 *(u4_t *)&bf[j][4] =
-                    *(const u4_t *)(st + OFF_B + r * BB + (((cb + 1) ^ swz128(r)) << 4));
+                    *(const u4_t *)(st + OFF_B + r * BB + (((cb + 2) ^ swz128(r)) << 4));
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
