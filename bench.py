@@ -133,7 +133,7 @@ def run_workload(name, steps, warmup, rotate_b=1):
     return out, p
 
 
-def cpu_baseline(p, rows=512):
+def cpu_baseline(p, rows=4096):
     """The CPU oracle on rows 0..rows-1 of the workload (bounded sample)."""
     from oracle import oracle
     M, N, K = p["M"], p["N"], p["K"]
@@ -157,12 +157,16 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(_workloads().keys()))
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--force-kernel", default=None,
+                    help="kernel family to force (tuning: sets STGEMM_FORCE_KERNEL)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the GEMM library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
+    if args.force_kernel:
+        os.environ["STGEMM_FORCE_KERNEL"] = args.force_kernel
     import torch
     torch.cuda.set_device(0)
     from sparse_tiled_gemm_amd import gemm as G

@@ -19,7 +19,7 @@ SOURCES = ["gemm_api.cpp", "kernels_dense.hip", "kernels_sparse.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-ffp-contract=off",
     "-Wall", "-Wno-unused-function",
     # packed fp32 instructions stay out of generated code (they are not used
     # deliberately anywhere here); the host pass warns it does not know the

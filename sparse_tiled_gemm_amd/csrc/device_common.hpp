@@ -19,6 +19,11 @@
 
 #include "kernel_args.hpp"
 
+// Lambdas in the kernels are always inlined: a lambda left as a call would
+// force everything it captures by reference (the accumulators, the kernel
+// arguments) into scratch memory.
+#define STG_AI __attribute__((always_inline))
+
 namespace stg {
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
@@ -153,7 +158,7 @@ template <class OP, int FM, int FN>
 __device__ inline void epilogue_grid(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
                                      int64_t m0, int64_t n0, int lane)
 {
-    auto run = [&](auto kind) {
+    auto run = [&](auto kind) STG_AI {
         constexpr int K = decltype(kind)::value;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -168,6 +173,122 @@ __device__ inline void epilogue_grid(const EpiArgs &e, typename OP::acc_t (&acc)
         case OUT_F32: run(std::integral_constant<int, OUT_F32>{}); break;
         case OUT_F16: run(std::integral_constant<int, OUT_F16>{}); break;
         default: run(std::integral_constant<int, OUT_BF16>{}); break;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- LDS-staged epilogue
+
+// Four consecutive columns of one output row, col .. col+3 (all < N), with
+// 16-byte aligned C / bias rows and an output row aligned to 4 elements.
+template <int KIND>
+__device__ inline void epilogue_store4(const EpiArgs &e, int64_t row, int64_t col, f4_t v)
+{
+    if (e.C)
+        v += *(const f4_t *)((const float *)e.C + row * e.ldc + col);
+    f4_t y;
+    if (e.bias) {
+        const f4_t b = *(const f4_t *)(e.bias + col);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            y[q] = __builtin_fmaf(e.alpha, v[q], b[q]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            y[q] = e.alpha * v[q];
+    }
+    if (e.relu) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            y[q] = (y[q] > 0.0f) ? y[q] : 0.0f;
+    }
+    const int64_t o = row * e.ldd + col;
+    if constexpr (KIND == OUT_F32) {
+        *(f4_t *)((float *)e.D + o) = y;
+    } else {
+        uint2 packed;
+        if constexpr (KIND == OUT_F16) {
+            packed.x = f32_to_f16_bits(y[0]) | ((uint32_t)f32_to_f16_bits(y[1]) << 16);
+            packed.y = f32_to_f16_bits(y[2]) | ((uint32_t)f32_to_f16_bits(y[3]) << 16);
+        } else {
+            packed.x = f32_to_bf16_bits(y[0]) | ((uint32_t)f32_to_bf16_bits(y[1]) << 16);
+            packed.y = f32_to_bf16_bits(y[2]) | ((uint32_t)f32_to_bf16_bits(y[3]) << 16);
+        }
+        *(uint2 *)((uint16_t *)e.D + o) = packed;
+    }
+}
+
+template <int KIND>
+__device__ inline void epilogue_store4(const EpiArgs &e, int64_t row, int64_t col, i4_t v)
+{
+    if (e.C) {
+        const i4_t c = *(const i4_t *)((const int32_t *)e.C + row * e.ldc + col);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            v[q] = (int)((uint32_t)v[q] + (uint32_t)c[q]);
+    }
+    *(i4_t *)((int32_t *)e.D + row * e.ldd + col) = v;
+}
+
+// Epilogue of a wave's (32 FM) x (32 FN) accumulator block at (m0, n0),
+// staged through `lds_wave` (32 * (32 FN + 4) words of LDS owned by this
+// wave): for each 32-row slab, the fragments are written to LDS in row-major
+// order, then read back four consecutive columns per lane, so C and bias are
+// read and D is written with 8- or 16-byte accesses along the rows.
+template <class OP, int FM, int FN, int KIND>
+__device__ inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
+                                      int64_t m0, int64_t n0, int lane, uint32_t *lds_wave)
+{
+    constexpr int COLS = 32 * FN, PITCH = COLS + 4, LPR = COLS / 4; // lanes per row
+    constexpr int RPP = 64 / LPR;                                    // rows per pass
+    typedef std::conditional_t<OP::INT, i4_t, f4_t> v4_t;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                // copy the element out first: a bit_cast applied to a
+                // vector-element expression would read element 0
+                const auto x = acc[i][j][r];
+                lds_wave[row * PITCH + j * 32 + (lane & 31)] = __builtin_bit_cast(uint32_t, x);
+            }
+        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): the slab is in LDS
+        __builtin_amdgcn_wave_barrier();
+        const int c4 = (lane % LPR) * 4;
+        const int64_t col = n0 + c4;
+        for (int p = 0; p < 32 / RPP; ++p) {
+            const int rr = p * RPP + lane / LPR;
+            const int64_t row = m0 + 32 * i + rr;
+            const v4_t v = __builtin_bit_cast(v4_t, *(const u4_t *)(lds_wave + rr * PITCH + c4));
+            if (row < e.M) {
+                if (e.vec && col + 3 < e.N) {
+                    epilogue_store4<KIND>(e, row, col, v);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (col + q < e.N)
+                            epilogue_store<KIND>(e, row, col + q, v[q]);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F); // reads done before the next slab overwrites
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+template <class OP, int FM, int FN>
+__device__ inline void epilogue_grid_lds(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
+                                         int64_t m0, int64_t n0, int lane, uint32_t *lds_wave)
+{
+    if constexpr (OP::INT) {
+        epilogue_slabs<OP, FM, FN, OUT_S32>(e, acc, m0, n0, lane, lds_wave);
+    } else {
+        switch (e.d_kind) {
+        case OUT_F32: epilogue_slabs<OP, FM, FN, OUT_F32>(e, acc, m0, n0, lane, lds_wave); break;
+        case OUT_F16: epilogue_slabs<OP, FM, FN, OUT_F16>(e, acc, m0, n0, lane, lds_wave); break;
+        default: epilogue_slabs<OP, FM, FN, OUT_BF16>(e, acc, m0, n0, lane, lds_wave); break;
         }
     }
 }

@@ -148,6 +148,25 @@ bool tiled_ok(const gemm_desc_t &d)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+const char *family_name(int f)
+{
+    switch (f) {
+    case KF_GENERIC: return "generic";
+    case KF_TILED_256: return "tiled256";
+    case KF_TILED_128: return "tiled128";
+    case KF_SKINNY: return "skinny";
+    case KF_SPARSE_GENERIC: return "sparse24_generic";
+    case KF_SPARSE_TILED: return "sparse24_tiled";
+    case KF_TILED_DMA4: return "tiled256dma4";
+    case KF_TILED_DMA5: return "tiled256dma5";
+    default: return "?";
+    }
+}
+
+bool is_tiled(int f) { return f == KF_TILED_256 || f == KF_TILED_128 || f == KF_TILED_DMA4 || f == KF_TILED_DMA5; }
+
 } // namespace
 
 extern "C" {
@@ -291,10 +310,15 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
         delete p;
         return fail(GEMM_ERR_UNSUPPORTED, "requested algorithm cannot serve this problem");
     }
+    // Tuning override: STGEMM_FORCE_KERNEL=<family name> replaces the choice
+    // for descriptors that family can serve (ignored otherwise).
+    if (const char *force = getenv("STGEMM_FORCE_KERNEL")) {
+        for (int f = 0; f < KF_COUNT; ++f)
+            if (strcmp(force, family_name(f)) == 0 && (f == KF_GENERIC || (tiled && is_tiled(f))))
+                fam = f;
+    }
     p->family = fam;
-    const char *fname = fam == KF_TILED_256 ? "tiled256" : fam == KF_TILED_128 ? "tiled128"
-                                                                             : "generic";
-    snprintf(p->name, sizeof p->name, "%s_%s", fname, op_name(p->op));
+    snprintf(p->name, sizeof p->name, "%s_%s", family_name(fam), op_name(p->op));
     *out = p;
     return ok();
 }
@@ -314,8 +338,6 @@ gemm_status_t gemm_plan_describe(const gemm_plan_t *plan, char *buf, size_t len)
     snprintf(buf, len, "%s", plan->name);
     return ok();
 }
-
-static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 static gemm_status_t check_epilogue_ptrs(const gemm_desc_t &d, const void *C, const void *bias,
                                          const void *D)
@@ -345,6 +367,9 @@ static EpiArgs make_epi(const gemm_desc_t &d, const void *C, const void *bias, v
     e.d_kind = out_kind(d.d_type);
     e.D = D;
     e.ldd = d.ldd;
+    const int db = elem_bytes(d.d_type);
+    e.vec = (!d.has_c || (aligned(C, 16) && d.ldc % 4 == 0)) &&
+            (!d.has_bias || aligned(bias, 16)) && aligned(D, 4 * db) && d.ldd % 4 == 0;
     return e;
 }
 

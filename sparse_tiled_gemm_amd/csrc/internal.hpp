@@ -27,7 +27,10 @@ enum KernelFamily {
     KF_TILED_128,   // 128 x 128 workgroup tile, LDS double buffer
     KF_SKINNY,      // M <= 64, bandwidth-oriented
     KF_SPARSE_GENERIC,
-    KF_SPARSE_TILED
+    KF_SPARSE_TILED,
+    KF_TILED_DMA4, // 256 x 256, direct global -> LDS copies, 4 LDS stages
+    KF_TILED_DMA5, // same with 5 LDS stages (160 KB)
+    KF_COUNT
 };
 
 hipError_t launch_dense(int family, int op, const GemmArgs &g, hipStream_t s);

@@ -18,6 +18,8 @@ struct EpiArgs {
     int d_kind; // OutKind
     void *D;
     int64_t ldd;
+    int vec; // 1: C, bias and D rows allow 16-byte (C, f32/s32 D) / 8-byte accesses
+             //    at multiples of 4 columns
 };
 
 // Dense operands.  Element (m,k) of A is at A[m*a_rs + k*a_cs] and element

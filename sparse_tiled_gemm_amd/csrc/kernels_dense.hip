@@ -15,9 +15,12 @@
 //     loads, 4 consecutive threads per row; the buffer resource is based at
 //     the tile's first row and bounded by the matrix, so rows past M or N
 //     read as zero;
-//   - LDS holds two K tiles (double buffer): tile k+1 is loaded into registers
-//     while tile k is multiplied, then written to the other buffer; one
-//     barrier per K tile;
+//   - software pipeline with three LDS stages: while tile t is multiplied,
+//     tile t+2 (loaded into registers during tile t-1) is written to LDS and
+//     tile t+3 is fetched into the other register set; MFMA fragments are
+//     double-buffered in registers, so the next K step's (or next tile's
+//     first) fragments are read from LDS during the current step's MFMAs;
+//     one barrier per K tile;
 //   - 16-byte chunks are XOR-swizzled within a row (chunk c of row r sits at
 //     slot c ^ (((r >> 1) ^ (r >> 3)) & 3)) so the 32 rows that one fragment
 //     read touches spread over all banks - the bank-conflict remedy of the same page's
@@ -136,21 +139,25 @@ __global__ __launch_bounds__(256, 1) void k_tiled(GemmArgs g, int tiles_m, int t
     constexpr int A_LD = BM / RPP, B_LD = BN / RPP;
     constexpr int WM = BM / 2, WN = BN / 2; // wave sub-tile (2 x 2 waves)
     constexpr int FM = WM / 32, FN = WN / 32;
+    constexpr int NSTAGE = 3;
     constexpr int STAGE = (BM + BN) * BKB;
     constexpr int NV = OP::LANE_BYTES / 16; // 16-byte LDS reads per operand
-    constexpr int KSTEPS = BKB / OP::KB;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+    constexpr int FW = OP::LANE_BYTES / 4;  // 32-bit words per operand fragment
+    constexpr int KS = BKB / OP::KB;        // MFMA K steps per tile
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NSTAGE * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int64_t m_blk = (int64_t)tm * BM, n_blk = (int64_t)tn * BN;
     const int64_t lda_b = g.a_rs * OP::ELEM, ldb_b = g.b_cs * OP::ELEM;
-    const int KT = (int)(g.K * OP::ELEM / BKB);
-    const __amdgpu_buffer_rsrc_t ra =
-        tile_rsrc((const uint8_t *)g.A + m_blk * lda_b, (g.e.M - m_blk) * lda_b);
-    const __amdgpu_buffer_rsrc_t rb =
-        tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b, (g.e.N - n_blk) * ldb_b);
+    const int64_t kbytes = g.K * OP::ELEM;
+    const int KT = (int)(kbytes / BKB);
+    // bounded by the last byte of the last row: loads past it return zero
+    const __amdgpu_buffer_rsrc_t ra = tile_rsrc((const uint8_t *)g.A + m_blk * lda_b,
+                                                (g.e.M - m_blk - 1) * lda_b + kbytes);
+    const __amdgpu_buffer_rsrc_t rb = tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b,
+                                                (g.e.N - n_blk - 1) * ldb_b + kbytes);
 
     // global -> LDS copy: thread owns chunk `ch` of rows r0 + i*RPP
     const int ch = tid % CH, r0 = tid / CH;
@@ -158,24 +165,27 @@ __global__ __launch_bounds__(256, 1) void k_tiled(GemmArgs g, int tiles_m, int t
     const int va_step = RPP * (int)lda_b, vb_step = RPP * (int)ldb_b;
     const int l0 = r0 * BKB + ((ch ^ swz64(r0)) << 4); // + i*RPP*BKB (swz64 is RPP-periodic)
 
-    u4_t pa[A_LD], pb[B_LD];
-    auto gload = [&](int kt) {
+    // register staging of global tiles, two sets (prefetch distance 2 tiles)
+    u4_t ga[2][A_LD], gb[2][B_LD];
+    auto gload = [&](auto set, int kt) STG_AI {
+        constexpr int S = decltype(set)::value;
         const int soff = kt * BKB;
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
-            pa[i] = buf_load16(ra, va0 + i * va_step, soff);
+            ga[S][i] = buf_load16(ra, va0 + i * va_step, soff);
 #pragma unroll
         for (int i = 0; i < B_LD; ++i)
-            pb[i] = buf_load16(rb, vb0 + i * vb_step, soff);
+            gb[S][i] = buf_load16(rb, vb0 + i * vb_step, soff);
     };
-    auto lstore = [&](int stage) {
+    auto lstore = [&](auto set, int stage) STG_AI {
+        constexpr int S = decltype(set)::value;
         uint8_t *base = lds + stage * STAGE + l0;
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
-            *(u4_t *)(base + i * RPP * BKB) = pa[i];
+            *(u4_t *)(base + i * RPP * BKB) = ga[S][i];
 #pragma unroll
         for (int i = 0; i < B_LD; ++i)
-            *(u4_t *)(base + BM * BKB + i * RPP * BKB) = pb[i];
+            *(u4_t *)(base + BM * BKB + i * RPP * BKB) = gb[S][i];
     };
 
     // fragment reads: lane reads rows arow + 32 i (A) and brow + 32 j (B)
@@ -183,6 +193,25 @@ __global__ __launch_bounds__(256, 1) void k_tiled(GemmArgs g, int tiles_m, int t
     const int arow = wm * WM + (lane & 31), brow = wn * WN + (lane & 31);
     const int half = lane >> 5;
     const int sa = swz64(arow), sb = swz64(brow); // same for every fragment row
+    const int a_off = arow * BKB, b_off = BM * BKB + brow * BKB;
+
+    uint32_t fa[2][FM][FW], fb[2][FN][FW];
+    auto lread = [&](auto set, int stage, int s) STG_AI {
+        constexpr int S = decltype(set)::value;
+        const uint8_t *lsa = lds + stage * STAGE + a_off;
+        const uint8_t *lsb = lds + stage * STAGE + b_off;
+        const int c0 = (s * OP::KB + half * OP::LANE_BYTES) >> 4;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int oa = ((c0 + v) ^ sa) << 4, ob = ((c0 + v) ^ sb) << 4;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                *(u4_t *)&fa[S][i][4 * v] = *(const u4_t *)(lsa + i * 32 * BKB + oa);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                *(u4_t *)&fb[S][j][4 * v] = *(const u4_t *)(lsb + j * 32 * BKB + ob);
+        }
+    };
 
     typename OP::acc_t acc[FM][FN];
 #pragma unroll
@@ -190,44 +219,269 @@ __global__ __launch_bounds__(256, 1) void k_tiled(GemmArgs g, int tiles_m, int t
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             acc[i][j] = typename OP::acc_t{};
+    auto mma = [&](auto set) STG_AI {
+        constexpr int S = decltype(set)::value;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = OP::mma(fa[S][i], fb[S][j], acc[i][j]);
+    };
 
-    gload(0);
-    lstore(0);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // prologue: tiles 0 and 1 in LDS stages 0 and 1, tile 2 in registers set 0
+    gload(I0{}, 0);
+    gload(I1{}, 1);
+    lstore(I0{}, 0);
+    lstore(I1{}, 1);
+    gload(I0{}, 2);
     __syncthreads();
+    lread(I0{}, 0, 0);
 
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more)
-            gload(kt + 1);
-        const uint8_t *lsa = lds + cur * STAGE + arow * BKB;
-        const uint8_t *lsb = lds + cur * STAGE + BM * BKB + brow * BKB;
+    // one K tile: `P` is the parity of the tile index (register sets and the
+    // fragment buffer of its first step are chosen at compile time).
+    // Loads past the last tile read padding or zeros into a stage that is
+    // never consumed, which keeps the loop body branch-free.
+    // Instruction order inside one K tile: each MFMA slot is followed by one
+    // fragment read for the next step, and by one global load (first step)
+    // or one LDS store of the staged tile (last step), so the matrix pipe
+    // stays busy while the memory operations are in flight.
+    constexpr int NM = FM * FN, NR = (FM + FN) * NV, NL = A_LD + B_LD;
+    auto schedule = [&]() STG_AI {
+        [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
+            (
+                [&]() STG_AI {
+                    constexpr int S = Q / NM, m = Q % NM;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                    if constexpr (m < NR)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+                    if constexpr (S == 0 && m < NL)
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
+                    if constexpr (S == KS - 1 && m >= NM - NL)
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // DS write
+                }(),
+                ...);
+        }(std::make_integer_sequence<int, KS * NM>{});
+    };
+
+    int st = 0; // LDS stage of tile t
+    auto iter = [&](auto par, int t) STG_AI {
+        constexpr int P = decltype(par)::value;
+        const int st1 = st == NSTAGE - 1 ? 0 : st + 1;
+        const int st2 = st1 == NSTAGE - 1 ? 0 : st1 + 1;
+        gload(std::integral_constant<int, P ^ 1>{}, t + 3);
+        [&]<int... S>(std::integer_sequence<int, S...>) STG_AI {
+            (
+                [&]() STG_AI {
+                    constexpr int F = (P * KS + S) & 1;
+                    if constexpr (S + 1 < KS)
+                        lread(std::integral_constant<int, F ^ 1>{}, st, S + 1);
+                    else
+                        lread(std::integral_constant<int, F ^ 1>{}, st1, 0);
+                    mma(std::integral_constant<int, F>{});
+                }(),
+                ...);
+        }(std::make_integer_sequence<int, KS>{});
+        lstore(std::integral_constant<int, P>{}, st2);
+        schedule();
+        __syncthreads();
+        st = st1;
+    };
+
+    int t = 0;
+    for (; t + 1 < KT; t += 2) {
+        iter(I0{}, t);
+        iter(I1{}, t + 1);
+    }
+    if (t < KT)
+        iter(I0{}, t);
+
+    __syncthreads(); // every wave is done with the LDS stages
+    epilogue_grid_lds<OP, FM, FN>(g.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
+                                  (uint32_t *)lds + wave * 32 * (WN + 4));
+}
+
+// ---------------------------------------------------------------- tiled, LDS DMA
+
+// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt left free).
+#define STG_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt((((n)&15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
+
+// 16-byte global -> LDS copy for a whole wave: lane l's 16 bytes land at
+// lds_wave + 16 l (lds_wave must be wave-uniform).
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_wave, int voff, int soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds_wave, 16, voff, soff, 0, 0);
+}
+
+// Same tile structure as k_tiled, but global -> LDS copies are direct
+// (buffer_load ... lds): no staging registers and no LDS store instructions,
+// so NSTAGE LDS stages can be in flight.  Tile t+NSTAGE-1 is requested while
+// tile t is multiplied; before the barrier that ends tile t the wave waits for
+// its copies of tile t+2 (vmcnt counts the newer requests still in flight),
+// so the MFMA fragments of tile t+1 can be read during tile t's last K step.
+// Each wave instruction fills 1 KB of LDS = 16 rows of 64 bytes; lane l
+// writes slot l % 4 of row l / 4 and therefore fetches the chunk that the
+// swizzle maps to that slot.
+template <class OP, int BM, int BN, int NSTAGE>
+__global__ __launch_bounds__(256, 1) void k_tiled_dma(GemmArgs g, int tiles_m, int tiles_n)
+{
+    constexpr int BKB = 64, CH = 4;
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int FM = WM / 32, FN = WN / 32;
+    constexpr int STAGE = (BM + BN) * BKB;
+    constexpr int NV = OP::LANE_BYTES / 16;
+    constexpr int FW = OP::LANE_BYTES / 4;
+    constexpr int KS = BKB / OP::KB;
+    constexpr int ROWS_PER_INST = 1024 / BKB;          // 16
+    constexpr int A_INST = BM / ROWS_PER_INST / 4;     // per wave
+    constexpr int B_INST = BN / ROWS_PER_INST / 4;
+    constexpr int NI = A_INST + B_INST;                // DMA instructions per wave per tile
+    static_assert(NSTAGE >= 4, "the fragment prefetch needs tile t+1 two tiles early");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m_blk = (int64_t)tm * BM, n_blk = (int64_t)tn * BN;
+    const int64_t lda_b = g.a_rs * OP::ELEM, ldb_b = g.b_cs * OP::ELEM;
+    const int64_t kbytes = g.K * OP::ELEM;
+    const int KT = (int)(kbytes / BKB);
+    const __amdgpu_buffer_rsrc_t ra = tile_rsrc((const uint8_t *)g.A + m_blk * lda_b,
+                                                (g.e.M - m_blk - 1) * lda_b + kbytes);
+    const __amdgpu_buffer_rsrc_t rb = tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b,
+                                                (g.e.N - n_blk - 1) * ldb_b + kbytes);
+
+    // this lane's source offsets for each of the wave's DMA instructions
+    int voff[NI];
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            uint32_t af[FM][OP::LANE_BYTES / 4], bf[FN][OP::LANE_BYTES / 4];
-            const int c0 = (s * OP::KB + half * OP::LANE_BYTES) >> 4;
+    for (int i = 0; i < NI; ++i) {
+        const bool is_a = i < A_INST;
+        const int blk = is_a ? wave * A_INST + i : wave * B_INST + (i - A_INST);
+        const int row = blk * ROWS_PER_INST + (lane >> 2);
+        const int c = (lane & 3) ^ swz64(row);
+        voff[i] = row * (int)(is_a ? lda_b : ldb_b) + c * 16;
+    }
+    auto dma_tile = [&](int stage, int kt) STG_AI {
+        uint8_t *base = lds + stage * STAGE;
+        const int soff = kt * BKB;
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int oa = ((c0 + v) ^ sa) << 4, ob = ((c0 + v) ^ sb) << 4;
+        for (int i = 0; i < NI; ++i) {
+            const bool is_a = i < A_INST;
+            const int blk = is_a ? wave * A_INST + i : BM / ROWS_PER_INST + wave * B_INST + (i - A_INST);
+            dma16(is_a ? ra : rb, base + blk * 1024, voff[i], soff);
+        }
+    };
+
+    const int wm = wave >> 1, wn = wave & 1;
+    const int arow = wm * WM + (lane & 31), brow = wn * WN + (lane & 31);
+    const int half = lane >> 5;
+    const int sa = swz64(arow), sb = swz64(brow);
+    const int a_off = arow * BKB, b_off = BM * BKB + brow * BKB;
+
+    uint32_t fa[2][FM][FW], fb[2][FN][FW];
+    auto lread = [&](auto set, int stage, int s) STG_AI {
+        constexpr int S = decltype(set)::value;
+        const uint8_t *lsa = lds + stage * STAGE + a_off;
+        const uint8_t *lsb = lds + stage * STAGE + b_off;
+        const int c0 = (s * OP::KB + half * OP::LANE_BYTES) >> 4;
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    *(u4_t *)&af[i][4 * v] = *(const u4_t *)(lsa + i * 32 * BKB + oa);
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    *(u4_t *)&bf[j][4 * v] = *(const u4_t *)(lsb + j * 32 * BKB + ob);
-            }
+        for (int v = 0; v < NV; ++v) {
+            const int oa = ((c0 + v) ^ sa) << 4, ob = ((c0 + v) ^ sb) << 4;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
+                *(u4_t *)&fa[S][i][4 * v] = *(const u4_t *)(lsa + i * 32 * BKB + oa);
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = OP::mma(af[i], bf[j], acc[i][j]);
+            for (int j = 0; j < FN; ++j)
+                *(u4_t *)&fb[S][j][4 * v] = *(const u4_t *)(lsb + j * 32 * BKB + ob);
         }
-        if (more)
-            lstore(cur ^ 1);
-        __syncthreads();
-    }
+    };
 
-    epilogue_grid<OP, FM, FN>(g.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane);
+    typename OP::acc_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = typename OP::acc_t{};
+    auto mma = [&](auto set) STG_AI {
+        constexpr int S = decltype(set)::value;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = OP::mma(fa[S][i], fb[S][j], acc[i][j]);
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // prologue: request tiles 0 .. NSTAGE-2; tiles 0 and 1 complete
+#pragma unroll
+    for (int p = 0; p < NSTAGE - 1; ++p)
+        dma_tile(p, p);
+    STG_WAIT_VMCNT((NSTAGE - 3) * NI);
+    __builtin_amdgcn_s_barrier();
+    lread(I0{}, 0, 0);
+
+    constexpr int NM = FM * FN, NR = (FM + FN) * NV;
+    auto schedule = [&]() STG_AI {
+        [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
+            (
+                [&]() STG_AI {
+                    constexpr int S = Q / NM, m = Q % NM;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                    if constexpr (m < NR)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+                    if constexpr (S == 0 && m < NI)
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
+                }(),
+                ...);
+        }(std::make_integer_sequence<int, KS * NM>{});
+    };
+
+    int st = 0; // LDS stage of tile t
+    auto iter = [&](auto par, int t) STG_AI {
+        constexpr int P = decltype(par)::value;
+        const int st1 = st == NSTAGE - 1 ? 0 : st + 1;
+        const int stn = st == 0 ? NSTAGE - 1 : st - 1; // stage of tile t + NSTAGE - 1
+        dma_tile(stn, t + NSTAGE - 1);
+        [&]<int... S>(std::integer_sequence<int, S...>) STG_AI {
+            (
+                [&]() STG_AI {
+                    constexpr int F = (P * KS + S) & 1;
+                    if constexpr (S + 1 < KS)
+                        lread(std::integral_constant<int, F ^ 1>{}, st, S + 1);
+                    else
+                        lread(std::integral_constant<int, F ^ 1>{}, st1, 0);
+                    mma(std::integral_constant<int, F>{});
+                }(),
+                ...);
+        }(std::make_integer_sequence<int, KS>{});
+        schedule();
+        __builtin_amdgcn_sched_barrier(0);
+        // tile t+2 complete (tiles t+3 .. t+NSTAGE-1 may still be in flight)
+        STG_WAIT_VMCNT((NSTAGE - 3) * NI);
+        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's LDS reads done
+        __builtin_amdgcn_s_barrier();
+        st = st1;
+    };
+
+    int t = 0;
+    for (; t + 1 < KT; t += 2) {
+        iter(I0{}, t);
+        iter(I1{}, t + 1);
+    }
+    if (t < KT)
+        iter(I0{}, t);
+    STG_WAIT_VMCNT(0); // drain the requests past the last tile before exit
+    __syncthreads();   // every wave is done with the LDS stages
+
+    epilogue_grid_lds<OP, FM, FN>(g.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
+                                  (uint32_t *)lds + wave * 32 * (WN + 4));
 }
 
 // ---------------------------------------------------------------- launch
@@ -280,6 +534,30 @@ static dense_launch_fn tiled_table_t(int op)
     }
 }
 
+template <class OP, int BM, int BN, int NS>
+static hipError_t launch_dma_t(const GemmArgs &g, hipStream_t s)
+{
+    const int tiles_m = (int)((g.e.M + BM - 1) / BM), tiles_n = (int)((g.e.N + BN - 1) / BN);
+    hipLaunchKernelGGL((k_tiled_dma<OP, BM, BN, NS>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(256), 0, s, g, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int NS>
+static dense_launch_fn dma_table_t(int op)
+{
+    switch (op) {
+    case OPK_F16: return launch_dma_t<OpF16, BM, BN, NS>;
+    case OPK_BF16: return launch_dma_t<OpBF16, BM, BN, NS>;
+    case OPK_F8_E4E4: return launch_dma_t<OpF8<0, 0>, BM, BN, NS>;
+    case OPK_F8_E4E5: return launch_dma_t<OpF8<0, 1>, BM, BN, NS>;
+    case OPK_F8_E5E4: return launch_dma_t<OpF8<1, 0>, BM, BN, NS>;
+    case OPK_F8_E5E5: return launch_dma_t<OpF8<1, 1>, BM, BN, NS>;
+    case OPK_S8: return launch_dma_t<OpS8, BM, BN, NS>;
+    default: return nullptr;
+    }
+}
+
 hipError_t launch_dense(int family, int op, const GemmArgs &g, hipStream_t s)
 {
     dense_launch_fn fn = nullptr;
@@ -287,6 +565,8 @@ hipError_t launch_dense(int family, int op, const GemmArgs &g, hipStream_t s)
     case KF_GENERIC: fn = generic_table(op); break;
     case KF_TILED_256: fn = tiled_table_t<256, 256>(op); break;
     case KF_TILED_128: fn = tiled_table_t<128, 128>(op); break;
+    case KF_TILED_DMA4: fn = dma_table_t<256, 256, 4>(op); break;
+    case KF_TILED_DMA5: fn = dma_table_t<256, 256, 5>(op); break;
     default: break;
     }
     if (!fn)

@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_tiled(SparseArgs a, int tiles
 
     u4_t pv[AV_LD], pb[B_LD];
     uint2 pm = {0, 0};
-    auto gload = [&](int64_t kt) {
+    auto gload = [&](int64_t kt) STG_AI {
 #pragma unroll
         for (int i = 0; i < AV_LD; ++i)
             pv[i] = *(const u4_t *)(gv[i] + kt * AVB);
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_tiled(SparseArgs a, int tiles
         if (meta_row)
             pm = *(const uint2 *)(gmeta + kt * AMB);
     };
-    auto lstore = [&](int stage) {
+    auto lstore = [&](int stage) STG_AI {
         uint8_t *base = lds + stage * STAGE;
 #pragma unroll
         for (int i = 0; i < AV_LD; ++i)
@@ -290,7 +290,9 @@ __global__ __launch_bounds__(256, 1) void k_sparse_tiled(SparseArgs a, int tiles
         __syncthreads();
     }
 
-    epilogue_grid<OpF16, FM, FN>(a.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane);
+    __syncthreads(); // every wave is done with the LDS stages
+    epilogue_grid_lds<OpF16, FM, FN>(a.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
+                                     (uint32_t *)lds + wave * 32 * (WN + 4));
 }
 
 hipError_t launch_sparse(int family, const SparseArgs &a, hipStream_t s)

@@ -66,6 +66,29 @@ def test_dense_parity(orc, a_type, b_type, algo, shape):
     compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, algo, expect_kernel=algo)
 
 
+@pytest.mark.parametrize("family", ["tiled256dma4", "tiled256dma5"])
+@pytest.mark.parametrize("a_type,b_type", PAIRS)
+@pytest.mark.parametrize("shape", [(600, 520, 256), (256, 256, 64), (300, 700, 448)])
+def test_dense_parity_dma_variants(orc, monkeypatch, family, a_type, b_type, shape):
+    """The direct-to-LDS pipelined kernels (selected through the
+    STGEMM_FORCE_KERNEL tuning override)."""
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", family)
+    M, N, K = shape
+    A, B, C, _ = make(a_type, b_type, M, N, K, seed=zlib.crc32(repr((family, a_type, shape)).encode()))
+    d_type = "s32" if a_type == "s8" else "f32"
+    compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, "auto", expect_kernel=family)
+
+
+@pytest.mark.parametrize("family", ["tiled256dma5"])
+@pytest.mark.parametrize("d_type", ["f16", "bf16"])
+def test_dma_epilogue(orc, monkeypatch, family, d_type):
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", family)
+    M, N, K = 520, 390, 320
+    A, B, C, bias = make("e4m3", "e5m2", M, N, K, seed=17, bias=True)
+    compare(orc, A, B, C, bias, M, N, K, "e4m3", "e5m2", d_type, "auto", expect_kernel=family,
+            alpha=1.0 / 512, relu=True)
+
+
 @pytest.mark.parametrize("a_type,b_type", [("bf16", "bf16"), ("f16", "f16"), ("e4m3", "e5m2")])
 @pytest.mark.parametrize("d_type", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("algo", ["tiled128", "generic"])
@@ -83,21 +106,24 @@ def test_epilogue_variants(orc, a_type, b_type, d_type, algo, epi):
             alpha=epi.get("alpha", 1.0), relu=epi.get("relu", False))
 
 
-@pytest.mark.parametrize("algo", ["tiled256", "tiled128", "generic"])
+@pytest.mark.parametrize("algo", ["tiled256", "tiled128", "generic", "tiled256dma5"])
 @pytest.mark.parametrize("a_type,b_type,d_type", [("bf16", "bf16", "bf16"), ("f16", "f16", "f16"),
                                                   ("e4m3", "e5m2", "f16"),
                                                   ("e4m3", "e5m2", "bf16")])
-def test_epilogue_bit_exact(orc, algo, a_type, b_type, d_type):
+def test_epilogue_bit_exact(orc, monkeypatch, algo, a_type, b_type, d_type):
     """The fused epilogue equals the oracle's fp32 epilogue applied to the
     same kernel's fp32 accumulator output, bit for bit (same plan family, so
     the same summation order)."""
+    if algo.startswith("tiled256dma"):
+        monkeypatch.setenv("STGEMM_FORCE_KERNEL", algo)
+        algo = "tiled256"
     M, N, K = 384, 320, 256
     A, B, C, bias = make(a_type, b_type, M, N, K, seed=11, bias=True)
     alpha = 0.3 if not a_type.startswith("e") else 0.3 / 256.0
     T, n1 = gpu_gemm(A, B, C, None, M, N, K, a_type, b_type, "f32", algo=algo)
     D, n2 = gpu_gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, algo=algo, alpha=alpha,
                      relu=True)
-    assert n1.split("_")[0] == n2.split("_")[0] == algo
+    assert n1 == n2 and n1.startswith(algo), (n1, n2)
     ref = orc.epilogue_f32(T, alpha, bias, True, d_type)
     mism = int((D != ref).sum())
     say("epilogue", algo, a_type, d_type, "mismatches", mism)
@@ -141,14 +167,20 @@ def test_padded_leading_dimensions(orc):
     Ap = inputs.to_bf16(rng.standard_normal((M, lda)))
     Bp = inputs.to_bf16(rng.standard_normal((N, ldb)))
     Cp = rng.uniform(-1, 1, (M, ldc)).astype(np.float32)
-    for algo in ["tiled128", "tiled256", "generic"]:
+    for algo in ["tiled128", "tiled256", "generic", "tiled256dma5"]:
         say("padded", algo)
+        if algo.startswith("tiled256dma"):
+            import os
+            os.environ["STGEMM_FORCE_KERNEL"] = algo
+            algo = "tiled256"
         D, name = gpu_gemm(Ap, Bp, Cp, None, M, N, K, "bf16", "bf16", "bf16", algo=algo,
                            lda=lda, ldb=ldb, ldc=ldc, ldd=ldd)
         assert name.startswith(algo)
         Dr, Y, S = orc.gemm(np.ascontiguousarray(Ap[:, :K]), np.ascontiguousarray(Bp[:, :K]),
                             np.ascontiguousarray(Cp[:, :N]), None, M, N, K, "bf16", "bf16", "bf16")
         r = check(D, "bf16", Dr, Y, S, "bf16")
+        import os
+        os.environ.pop("STGEMM_FORCE_KERNEL", None)
         assert r.ok, r
 
 
