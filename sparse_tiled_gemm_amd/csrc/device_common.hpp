@@ -92,6 +92,52 @@ struct OpS8 {
     }
 };
 
+// 16x16 MFMA forms (skinny kernel).  Lane l holds row (or column) l % 16 and
+// LANE_BYTES K bytes; accumulator register i of lane l is row 4 (l / 16) + i,
+// column l % 16.  KB16 = K bytes one instruction consumes (4 lane groups).
+struct Op16F16 {
+    static constexpr int ELEM = 2, LANE_BYTES = 16;
+    static constexpr bool INT = false;
+    typedef f4_t acc_t;
+    __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, *(const u4_t *)a),
+                                                      __builtin_bit_cast(h8_t, *(const u4_t *)b),
+                                                      c, 0, 0, 0);
+    }
+};
+struct Op16BF16 {
+    static constexpr int ELEM = 2, LANE_BYTES = 16;
+    static constexpr bool INT = false;
+    typedef f4_t acc_t;
+    __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf8_t, *(const u4_t *)a), __builtin_bit_cast(bf8_t, *(const u4_t *)b),
+            c, 0, 0, 0);
+    }
+};
+template <int AFMT, int BFMT>
+struct Op16F8 {
+    static constexpr int ELEM = 1, LANE_BYTES = 32;
+    static constexpr bool INT = false;
+    typedef f4_t acc_t;
+    __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(*(const i8_t *)a, *(const i8_t *)b,
+                                                                c, AFMT, BFMT, 0, 127, 0, 127);
+    }
+};
+struct Op16S8 {
+    static constexpr int ELEM = 1, LANE_BYTES = 16;
+    static constexpr bool INT = true;
+    typedef i4_t acc_t;
+    __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
+    {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(*(const i4_t *)a, *(const i4_t *)b, c, 0, 0, 0);
+    }
+};
+
 // ---------------------------------------------------------------- epilogue
 
 __device__ inline uint16_t f32_to_f16_bits(float x)

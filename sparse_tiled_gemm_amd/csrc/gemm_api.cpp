@@ -165,6 +165,16 @@ const char *family_name(int f)
     }
 }
 
+// Skinny kernel: M <= 16, K-contiguous operands, whole 256-byte K chunks.
+bool skinny_ok(const gemm_desc_t &d)
+{
+    const int eb = elem_bytes(d.a_type);
+    const int64_t lim = (int64_t)1 << 30;
+    return d.M <= 16 && d.a_layout == GEMM_ROW_MAJOR && d.b_layout == GEMM_COL_MAJOR && d.K > 0 &&
+           (d.K * eb) % 256 == 0 && (d.lda * eb) % 16 == 0 && (d.ldb * eb) % 16 == 0 &&
+           d.lda * eb * 16 < lim && d.ldb * eb * 32 < lim;
+}
+
 bool is_tiled(int f) { return f == KF_TILED_256 || f == KF_TILED_128 || f == KF_TILED_DMA4 || f == KF_TILED_DMA5; }
 
 } // namespace
@@ -295,11 +305,13 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     }
 
     const bool tiled = tiled_ok(d);
+    const bool skinny = skinny_ok(d);
     int fam = -1;
     const int64_t big_tiles = ceil_div(d.M, 256) * ceil_div(d.N, 256);
     const int auto_tiled = big_tiles >= di.num_cu ? KF_TILED_256 : KF_TILED_128;
     switch (d.algo) {
-    case GEMM_ALGO_AUTO: fam = tiled ? auto_tiled : KF_GENERIC; break;
+    case GEMM_ALGO_AUTO: fam = skinny ? KF_SKINNY : tiled ? auto_tiled : KF_GENERIC; break;
+    case GEMM_ALGO_SKINNY: fam = skinny ? KF_SKINNY : -1; break;
     case GEMM_ALGO_TILED: fam = tiled ? auto_tiled : -1; break;
     case GEMM_ALGO_TILED_128: fam = tiled ? KF_TILED_128 : -1; break;
     case GEMM_ALGO_TILED_256: fam = tiled ? KF_TILED_256 : -1; break;
@@ -314,7 +326,8 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     // for descriptors that family can serve (ignored otherwise).
     if (const char *force = getenv("STGEMM_FORCE_KERNEL")) {
         for (int f = 0; f < KF_COUNT; ++f)
-            if (strcmp(force, family_name(f)) == 0 && (f == KF_GENERIC || (tiled && is_tiled(f))))
+            if (strcmp(force, family_name(f)) == 0 &&
+                (f == KF_GENERIC || (tiled && is_tiled(f)) || (skinny && f == KF_SKINNY)))
                 fam = f;
     }
     p->family = fam;

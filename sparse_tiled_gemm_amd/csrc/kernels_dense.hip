@@ -22,8 +22,8 @@
 //     first) fragments are read from LDS during the current step's MFMAs;
 //     one barrier per K tile;
 //   - 16-byte chunks are XOR-swizzled within a row (chunk c of row r sits at
-//     slot c ^ (((r >> 1) ^ (r >> 3)) & 3)) so the 32 rows that one fragment
-//     read touches spread over all banks - the bank-conflict remedy of the same page's
+//     slot c ^ ((r >> 2) & 3)) so the 32 rows that one fragment read touches
+//     spread over all banks - the bank-conflict remedy of the same page's
 //     section "Avoiding bank conflicts" (its swizzle figure did not survive;
 //     this function is this library's own);
 //   - each wave owns a (BM/2) x (BN/2) sub-tile of 32x32 MFMA fragments; per
@@ -108,10 +108,19 @@ __device__ inline u4_t buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
 }
 
 // 16-byte chunk slot inside a 64-byte LDS row: chunk c of row r sits at slot
-// c ^ swz64(r).  Any 8 consecutive rows (32 banks x 4 B) and any 16
-// consecutive rows (64 banks x 4 B) reading the same chunk hit distinct
-// bank groups.  swz64(r + 32 i) == swz64(r).
-__device__ inline int swz64(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// c ^ swz64(r).  Chosen by measurement on gfx950 (LDS bank-conflict counter
+// over the fragment-read pattern of 32 consecutive rows): rotating the slot
+// every 4 rows is conflict-free, while the textbook 32-bank XOR patterns
+// ((r >> 1) & 3, r & 3, and mixes of them) stall 2- to 4-way.
+// swz64(r + 32 i) == swz64(r).
+__device__ inline int swz64(int r) { return (r >> 2) & 3; }
+
+// Number of the `total` memory instructions that follow MFMA slot q of
+// `slots` when they are spread evenly.
+constexpr int spread(int q, int total, int slots)
+{
+    return (q + 1) * total / slots - q * total / slots;
+}
 
 // Workgroup id -> (tile_m, tile_n): XCD-contiguous renumbering, then groups
 // of GM tile rows walked column by column.
@@ -177,9 +186,9 @@ __global__ __launch_bounds__(256, 1) void k_tiled(GemmArgs g, int tiles_m, int t
         for (int i = 0; i < B_LD; ++i)
             gb[S][i] = buf_load16(rb, vb0 + i * vb_step, soff);
     };
-    auto lstore = [&](auto set, int stage) STG_AI {
+    auto lstore = [&](auto set, uint8_t *__restrict__ stage_base) STG_AI {
         constexpr int S = decltype(set)::value;
-        uint8_t *base = lds + stage * STAGE + l0;
+        uint8_t *base = stage_base + l0;
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
             *(u4_t *)(base + i * RPP * BKB) = ga[S][i];
@@ -196,10 +205,10 @@ __global__ __launch_bounds__(256, 1) void k_tiled(GemmArgs g, int tiles_m, int t
     const int a_off = arow * BKB, b_off = BM * BKB + brow * BKB;
 
     uint32_t fa[2][FM][FW], fb[2][FN][FW];
-    auto lread = [&](auto set, int stage, int s) STG_AI {
+    auto lread = [&](auto set, const uint8_t *__restrict__ stage_base, int s) STG_AI {
         constexpr int S = decltype(set)::value;
-        const uint8_t *lsa = lds + stage * STAGE + a_off;
-        const uint8_t *lsb = lds + stage * STAGE + b_off;
+        const uint8_t *lsa = stage_base + a_off;
+        const uint8_t *lsb = stage_base + b_off;
         const int c0 = (s * OP::KB + half * OP::LANE_BYTES) >> 4;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
@@ -234,36 +243,41 @@ __global__ __launch_bounds__(256, 1) void k_tiled(GemmArgs g, int tiles_m, int t
     // prologue: tiles 0 and 1 in LDS stages 0 and 1, tile 2 in registers set 0
     gload(I0{}, 0);
     gload(I1{}, 1);
-    lstore(I0{}, 0);
-    lstore(I1{}, 1);
+    lstore(I0{}, lds);
+    lstore(I1{}, lds + STAGE);
     gload(I0{}, 2);
     __syncthreads();
-    lread(I0{}, 0, 0);
+    lread(I0{}, lds, 0);
 
     // one K tile: `P` is the parity of the tile index (register sets and the
     // fragment buffer of its first step are chosen at compile time).
     // Loads past the last tile read padding or zeros into a stage that is
     // never consumed, which keeps the loop body branch-free.
-    // Instruction order inside one K tile: each MFMA slot is followed by one
-    // fragment read for the next step, and by one global load (first step)
-    // or one LDS store of the staged tile (last step), so the matrix pipe
-    // stays busy while the memory operations are in flight.
+    // Instruction order inside one K tile: the fragment reads of each step
+    // are spread evenly over that step's MFMAs, and the tile's global loads
+    // and LDS stores are spread evenly over all of the tile's MFMAs (a load
+    // every VM_EVERY MFMAs, a store half-way between), so neither the vector
+    // memory pipe (64 B/clk per CU) nor the LDS write path (about half the
+    // LDS read rate) backs up and stalls MFMA issue.
     constexpr int NM = FM * FN, NR = (FM + FN) * NV, NL = A_LD + B_LD;
+    constexpr int NMT = KS * NM;
     auto schedule = [&]() STG_AI {
         [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
             (
                 [&]() STG_AI {
-                    constexpr int S = Q / NM, m = Q % NM;
+                    constexpr int m = Q % NM;
+                    constexpr int nr = spread(m, NR, NM), nl = spread(Q, NL, NMT);
+                    constexpr int nw = spread((Q + NMT / 2) % NMT, NL, NMT);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-                    if constexpr (m < NR)
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
-                    if constexpr (S == 0 && m < NL)
-                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
-                    if constexpr (S == KS - 1 && m >= NM - NL)
-                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // DS write
+                    if constexpr (nr > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x100, nr, 0); // DS read
+                    if constexpr (nl > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x020, nl, 0); // VMEM read
+                    if constexpr (nw > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x200, nw, 0); // DS write
                 }(),
                 ...);
-        }(std::make_integer_sequence<int, KS * NM>{});
+        }(std::make_integer_sequence<int, NMT>{});
     };
 
     int st = 0; // LDS stage of tile t
@@ -271,21 +285,28 @@ __global__ __launch_bounds__(256, 1) void k_tiled(GemmArgs g, int tiles_m, int t
         constexpr int P = decltype(par)::value;
         const int st1 = st == NSTAGE - 1 ? 0 : st + 1;
         const int st2 = st1 == NSTAGE - 1 ? 0 : st1 + 1;
-        gload(std::integral_constant<int, P ^ 1>{}, t + 3);
-        [&]<int... S>(std::integer_sequence<int, S...>) STG_AI {
-            (
-                [&]() STG_AI {
-                    constexpr int F = (P * KS + S) & 1;
-                    if constexpr (S + 1 < KS)
-                        lread(std::integral_constant<int, F ^ 1>{}, st, S + 1);
-                    else
-                        lread(std::integral_constant<int, F ^ 1>{}, st1, 0);
-                    mma(std::integral_constant<int, F>{});
-                }(),
-                ...);
-        }(std::make_integer_sequence<int, KS>{});
-        lstore(std::integral_constant<int, P>{}, st2);
-        schedule();
+        // the three stages are distinct: the tile is read from `cur`, the
+        // next tile's first fragments from `nxt`, and tile t+2 is written to
+        // `wr`; restrict lets the scheduler interleave the stores with reads
+        auto body = [&](const uint8_t *__restrict__ cur, const uint8_t *__restrict__ nxt,
+                        uint8_t *__restrict__ wr) STG_AI {
+            gload(std::integral_constant<int, P ^ 1>{}, t + 3);
+            [&]<int... S>(std::integer_sequence<int, S...>) STG_AI {
+                (
+                    [&]() STG_AI {
+                        constexpr int F = (P * KS + S) & 1;
+                        if constexpr (S + 1 < KS)
+                            lread(std::integral_constant<int, F ^ 1>{}, cur, S + 1);
+                        else
+                            lread(std::integral_constant<int, F ^ 1>{}, nxt, 0);
+                        mma(std::integral_constant<int, F>{});
+                    }(),
+                    ...);
+            }(std::make_integer_sequence<int, KS>{});
+            lstore(std::integral_constant<int, P>{}, wr);
+            schedule();
+        };
+        body(lds + st * STAGE, lds + st1 * STAGE, lds + st2 * STAGE);
         __syncthreads();
         st = st1;
     };
@@ -427,20 +448,24 @@ __global__ __launch_bounds__(256, 1) void k_tiled_dma(GemmArgs g, int tiles_m, i
     __builtin_amdgcn_s_barrier();
     lread(I0{}, 0, 0);
 
+    // fragment reads spread over each step's MFMAs, DMA requests spread over
+    // the whole tile (see k_tiled)
     constexpr int NM = FM * FN, NR = (FM + FN) * NV;
+    constexpr int NMT = KS * NM;
     auto schedule = [&]() STG_AI {
         [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
             (
                 [&]() STG_AI {
-                    constexpr int S = Q / NM, m = Q % NM;
+                    constexpr int m = Q % NM;
+                    constexpr int nr = spread(m, NR, NM), nl = spread(Q, NI, NMT);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-                    if constexpr (m < NR)
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
-                    if constexpr (S == 0 && m < NI)
-                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
+                    if constexpr (nr > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x100, nr, 0); // DS read
+                    if constexpr (nl > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x020, nl, 0); // VMEM read
                 }(),
                 ...);
-        }(std::make_integer_sequence<int, KS * NM>{});
+        }(std::make_integer_sequence<int, NMT>{});
     };
 
     int st = 0; // LDS stage of tile t
@@ -482,6 +507,123 @@ __global__ __launch_bounds__(256, 1) void k_tiled_dma(GemmArgs g, int tiles_m, i
 
     epilogue_grid_lds<OP, FM, FN>(g.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
                                   (uint32_t *)lds + wave * 32 * (WN + 4));
+}
+
+// ---------------------------------------------------------------- skinny
+
+// Small-M GEMM (M <= 16), bound by streaming B once from HBM.  One workgroup
+// owns 32 output columns (two 16x16 MFMA fragments); its 4 waves split K
+// (chunk c of 256 K bytes goes to wave c % 4), feed 16x16 MFMAs directly from
+// global memory and reduce their partial sums through LDS before the
+// epilogue.  Within a chunk, lane l (group g = l / 16) loads 64 contiguous
+// bytes of its row at byte 64 g, and MFMA step j uses bytes 16 j.. of every
+// lane's 64 (32 j.. for fp8): A and B use the same lane <-> K assignment, so
+// each product pairs equal K.  Each row's 256 bytes are fetched by 4 lanes as
+// whole cache lines; two chunks are kept in flight per wave.
+template <class OP>
+__global__ __launch_bounds__(256, 1) void k_skinny(GemmArgs g)
+{
+    constexpr int CB = 256;                      // K bytes per chunk
+    constexpr int LB = 64;                       // bytes per lane per chunk
+    constexpr int NLD = LB / 16;                 // 16-byte loads per row-fragment per chunk
+    constexpr int STEPS = LB / OP::LANE_BYTES;   // MFMAs per fragment per chunk
+    constexpr int FW = OP::LANE_BYTES / 4;
+    __shared__ __attribute__((aligned(16))) uint32_t red[4][2][64][4];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t n_blk = (int64_t)blockIdx.x * 32;
+    const int64_t lda_b = g.a_rs * OP::ELEM, ldb_b = g.b_cs * OP::ELEM;
+    const int64_t kbytes = g.K * OP::ELEM;
+    const int NC = (int)(kbytes / CB);
+    const __amdgpu_buffer_rsrc_t ra = tile_rsrc(g.A, (g.e.M - 1) * lda_b + kbytes);
+    const __amdgpu_buffer_rsrc_t rb =
+        tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b, (g.e.N - n_blk - 1) * ldb_b + kbytes);
+    const int row = lane & 15, grp = lane >> 4;
+    const int va = row * (int)lda_b + grp * LB;
+    const int vb0 = row * (int)ldb_b + grp * LB, vb1 = vb0 + 16 * (int)ldb_b;
+
+    u4_t pa[2][NLD], pb[2][2][NLD];
+    auto load = [&](auto set, int c) STG_AI {
+        constexpr int S = decltype(set)::value;
+        const int soff = c * CB;
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            pa[S][j] = buf_load16(ra, va + 16 * j, soff);
+            pb[S][0][j] = buf_load16(rb, vb0 + 16 * j, soff);
+            pb[S][1][j] = buf_load16(rb, vb1 + 16 * j, soff);
+        }
+    };
+    typename OP::acc_t acc[2] = {typename OP::acc_t{}, typename OP::acc_t{}};
+    auto compute = [&](auto set) STG_AI {
+        constexpr int S = decltype(set)::value;
+        const uint32_t *a = (const uint32_t *)pa[S];
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+                acc[f] = OP::mma(a + st * FW, (const uint32_t *)pb[S][f] + st * FW, acc[f]);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    int c = wave;
+    if (c < NC)
+        load(I0{}, c);
+    for (; c < NC; c += 8) {
+        if (c + 4 < NC)
+            load(I1{}, c + 4);
+        compute(I0{});
+        if (c + 4 >= NC)
+            break;
+        if (c + 8 < NC)
+            load(I0{}, c + 8);
+        compute(I1{});
+    }
+
+    // reduce the four waves' partial sums, then one wave stores 16 x 32
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const auto x = acc[f][i];
+            red[wave][f][lane][i] = __builtin_bit_cast(uint32_t, x);
+        }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            typename OP::acc_t t = acc[f];
+#pragma unroll
+            for (int w = 1; w < 4; ++w)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t u = red[w][f][lane][i];
+                    if constexpr (OP::INT)
+                        t[i] = (int)((uint32_t)t[i] + u);
+                    else
+                        t[i] += __builtin_bit_cast(float, u);
+                }
+            const int64_t col = n_blk + 16 * f + (lane & 15);
+            auto store = [&](auto kind) STG_AI {
+                constexpr int KD = decltype(kind)::value;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t r = 4 * (lane >> 4) + i;
+                    if (r < g.e.M && col < g.e.N)
+                        epilogue_store<KD>(g.e, r, col, t[i]);
+                }
+            };
+            if constexpr (OP::INT) {
+                store(std::integral_constant<int, OUT_S32>{});
+            } else {
+                switch (g.e.d_kind) {
+                case OUT_F32: store(std::integral_constant<int, OUT_F32>{}); break;
+                case OUT_F16: store(std::integral_constant<int, OUT_F16>{}); break;
+                default: store(std::integral_constant<int, OUT_BF16>{}); break;
+                }
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------- launch
@@ -534,6 +676,28 @@ static dense_launch_fn tiled_table_t(int op)
     }
 }
 
+template <class OP>
+static hipError_t launch_skinny_t(const GemmArgs &g, hipStream_t s)
+{
+    const unsigned blocks = (unsigned)((g.e.N + 31) / 32);
+    hipLaunchKernelGGL(k_skinny<OP>, dim3(blocks), dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
+static dense_launch_fn skinny_table(int op)
+{
+    switch (op) {
+    case OPK_F16: return launch_skinny_t<Op16F16>;
+    case OPK_BF16: return launch_skinny_t<Op16BF16>;
+    case OPK_F8_E4E4: return launch_skinny_t<Op16F8<0, 0>>;
+    case OPK_F8_E4E5: return launch_skinny_t<Op16F8<0, 1>>;
+    case OPK_F8_E5E4: return launch_skinny_t<Op16F8<1, 0>>;
+    case OPK_F8_E5E5: return launch_skinny_t<Op16F8<1, 1>>;
+    case OPK_S8: return launch_skinny_t<Op16S8>;
+    default: return nullptr;
+    }
+}
+
 template <class OP, int BM, int BN, int NS>
 static hipError_t launch_dma_t(const GemmArgs &g, hipStream_t s)
 {
@@ -565,6 +729,7 @@ hipError_t launch_dense(int family, int op, const GemmArgs &g, hipStream_t s)
     case KF_GENERIC: fn = generic_table(op); break;
     case KF_TILED_256: fn = tiled_table_t<256, 256>(op); break;
     case KF_TILED_128: fn = tiled_table_t<128, 128>(op); break;
+    case KF_SKINNY: fn = skinny_table(op); break;
     case KF_TILED_DMA4: fn = dma_table_t<256, 256, 4>(op); break;
     case KF_TILED_DMA5: fn = dma_table_t<256, 256, 5>(op); break;
     default: break;

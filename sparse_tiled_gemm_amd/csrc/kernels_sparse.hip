@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void k_sparse_generic(SparseArgs a)
 
 // Chunk swizzles: 128-byte rows (B tile) and 64-byte rows (compressed A).
 __device__ inline int swz128(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ inline int swz64(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ inline int swz64(int r) { return (r >> 2) & 3; }
 
 __device__ inline void tile_coords_sp(int id, int tiles_m, int tiles_n, int &tm, int &tn)
 {
@@ -213,7 +213,15 @@ __global__ __launch_bounds__(256, 1) void k_sparse_tiled(SparseArgs a, int tiles
 
     u4_t pv[AV_LD], pb[B_LD];
     uint2 pm = {0, 0};
-    auto gload = [&](int64_t kt) STG_AI {
+    // K-tile rotation: workgroup w starts its K loop at tile 2 (w / 8) mod KT
+    // and wraps, so workgroups running side by side on an XCD read different
+    // K slices (with power-of-two row pitches one K slice of all rows falls
+    // into few L2 channels).  Measured faster here; the dense kernels, whose
+    // workgroups share A and B slices in L2, are faster without it.  Each
+    // tile's summation order stays fixed.
+    const int rot = KT > 0 ? (int)(((blockIdx.x >> 3) * 2) % (unsigned)KT) : 0;
+    auto gload = [&](int64_t kt0) STG_AI {
+        const int64_t kt = kt0 + rot >= KT ? kt0 + rot - KT : kt0 + rot;
 #pragma unroll
         for (int i = 0; i < AV_LD; ++i)
             pv[i] = *(const u4_t *)(gv[i] + kt * AVB);

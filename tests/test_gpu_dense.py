@@ -79,6 +79,36 @@ def test_dense_parity_dma_variants(orc, monkeypatch, family, a_type, b_type, sha
     compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, "auto", expect_kernel=family)
 
 
+@pytest.mark.parametrize("a_type,b_type", PAIRS)
+@pytest.mark.parametrize("shape", [(16, 1024, 2048), (1, 300, 512), (7, 96, 1024), (16, 33, 256),
+                                   (12, 8192, 768)])
+def test_skinny_parity(orc, a_type, b_type, shape):
+    """Small-M kernel: M <= 16, K split over the workgroup's waves."""
+    M, N, K = shape
+    A, B, C, _ = make(a_type, b_type, M, N, K, seed=zlib.crc32(repr(("skinny", a_type, shape)).encode()))
+    d_type = "s32" if a_type == "s8" else "f32"
+    compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, "skinny", expect_kernel="skinny")
+
+
+@pytest.mark.parametrize("a_type,b_type,d_type", [("bf16", "bf16", "bf16"), ("e4m3", "e5m2", "f16"),
+                                                  ("f16", "f16", "f16")])
+def test_skinny_epilogue(orc, a_type, b_type, d_type):
+    M, N, K = 16, 520, 1024
+    A, B, C, bias = make(a_type, b_type, M, N, K, seed=23, bias=True)
+    alpha = 0.5 if not a_type.startswith("e") else 1.0 / 512
+    compare(orc, A, B, C, bias, M, N, K, a_type, b_type, d_type, "skinny", expect_kernel="skinny",
+            alpha=alpha, relu=True)
+    T, _ = gpu_gemm(A, B, C, None, M, N, K, a_type, b_type, "f32", algo="skinny")
+    D, _ = gpu_gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, algo="skinny", alpha=alpha,
+                    relu=True)
+    assert (D != orc.epilogue_f32(T, alpha, bias, True, d_type)).sum() == 0
+
+
+def test_skinny_is_chosen_for_small_m():
+    assert G.gemm_plan(G.make_desc(16, 8192, 8192, "bf16", "bf16", "bf16")).name == "skinny_bf16"
+    assert G.gemm_plan(G.make_desc(17, 8192, 8192, "bf16", "bf16", "bf16")).name != "skinny_bf16"
+
+
 @pytest.mark.parametrize("family", ["tiled256dma5"])
 @pytest.mark.parametrize("d_type", ["f16", "bf16"])
 def test_dma_epilogue(orc, monkeypatch, family, d_type):
