@@ -133,6 +133,31 @@ def run_workload(name, steps, warmup, rotate_b=1):
     return out, p
 
 
+def kernel_source_hash():
+    """Hash of the sources the dense, skinny and sparse kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_tiled_gemm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the kernel sources as they are now (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t["fetch_bytes_scaled"] + t["write_bytes_scaled"]
+
+
 def cpu_baseline(p, rows=4096):
     """The CPU oracle on rows 0..rows-1 of the workload (bounded sample)."""
     from oracle import oracle
@@ -157,6 +182,9 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(_workloads().keys()))
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (x3), the reference kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--force-kernel", default=None,
                     help="kernel family to force (tuning: sets STGEMM_FORCE_KERNEL)")
     args = ap.parse_args()
@@ -165,6 +193,16 @@ def main():
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        import torch
+        torch.cuda.set_device(0)
+        a = torch.ones(1 << 28, device="cuda")  # 1 GiB of fp32
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": a.numel() * 4, "copies": 3}))
+        return
     if args.force_kernel:
         os.environ["STGEMM_FORCE_KERNEL"] = args.force_kernel
     import torch
@@ -180,7 +218,7 @@ def main():
     achieved = value
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK[kind],
                 "unit": "TOP/s" if kind == "s8" else "TFLOP/s", "frac": achieved / PEAK[kind],
-                "traffic": None, "kernel": head["kernel"],
+                "traffic": measured_traffic(args.workload), "kernel": head["kernel"],
                 "algorithmic_flops_per_launch": 2.0 * p["M"] * p["N"] * p["K"]}
     result = {
         "metric": "TFLOPS (TOPS int8) at M=N=K=8192 per dtype; % of MFMA peak",

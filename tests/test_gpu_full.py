@@ -1,0 +1,166 @@
+"""Parity at the workloads' full sizes, through the plan bench.py times.
+
+Every output cannot be checked against the oracle at 8192^3, so each test
+checks (1) a sample of entries - random positions plus a whole row and a
+whole column - each computed by the oracle on its own, and (2) a property
+that covers every output: the column sums of D.  For int8 the column sums
+are exact (sum_m D[m,n] = sum_k (sum_m A[m,k]) B[k,n] + sum_m C[m,n] modulo
+2^32); for float outputs without a nonlinear epilogue they must agree within
+the sum of the per-element bounds.  The 2:4 compressor's output is compared
+byte for byte with the oracle's over the whole matrix, and the fp8
+workload's fused epilogue is pinned bit for bit against the oracle's fp32
+epilogue applied to the same kernel's fp32 accumulator output."""
+import numpy as np
+import pytest
+import torch
+
+from checks import TOL, check, ulp16
+from exact import lib_decode
+from gpu_util import OUT_NP, say, to_dev
+from sparse_tiled_gemm_amd import gemm as G
+from sparse_tiled_gemm_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+NS = 4096  # random sampled entries per workload
+
+
+def _run(p, d_type=None, alpha=None, bias=True, relu=None, sparse_dev=None):
+    M, N, K = p["M"], p["N"], p["K"]
+    d_type = d_type or p["d_type"]
+    use_bias = bias and p["bias"] is not None
+    desc = G.make_desc(M, N, K, p["a_type"], p["b_type"], d_type, has_c=p["C"] is not None,
+                       has_bias=use_bias, alpha=p["alpha"] if alpha is None else alpha,
+                       act="relu" if (p["relu"] if relu is None else relu) else "none",
+                       sparse_a=sparse_dev is not None)
+    plan = G.gemm_plan(desc)
+    tB = to_dev(p["B"])
+    tC = to_dev(p["C"]) if p["C"] is not None else None
+    tb = to_dev(p["bias"]) if use_bias else None
+    D = torch.empty(M * N * G.ELEM_BYTES[d_type], dtype=torch.uint8, device="cuda")
+    if sparse_dev is not None:
+        G.gemm_sparse24_run(plan, sparse_dev[0], sparse_dev[1], tB, tC, tb, D)
+    else:
+        G.gemm_run(plan, to_dev(p["A"]), tB, tC, tb, D)
+    torch.cuda.synchronize()
+    out = D.cpu().numpy().view(OUT_NP[d_type]).reshape(M, N)
+    say("  ran", plan.name, d_type)
+    return out, plan.name
+
+
+def _samples(M, N, seed):
+    rng = np.random.default_rng(seed)
+    r = rng.integers(0, M, NS)
+    c = rng.integers(0, N, NS)
+    rr = np.concatenate([r, np.full(N, M - 1), np.arange(M)])
+    cc = np.concatenate([c, np.arange(N), np.full(M, N // 2)])
+    return rr, cc
+
+
+def _check_samples(orc, p, D, a_logical=None, seed=0):
+    M, N, K = p["M"], p["N"], p["K"]
+    rows, cols = _samples(M, N, seed)
+    A = p["A"] if a_logical is None else a_logical
+    Dr, Y, S = orc.gemm_entries(A, p["B"], p["C"], p["bias"], M, N, K, p["a_type"], p["b_type"],
+                                p["d_type"], rows, cols, alpha=p["alpha"], relu=p["relu"])
+    r = check(D[rows, cols], p["d_type"], Dr, Y, S, p["a_type"], p["alpha"])
+    say("  sampled", r)
+    assert r.ok, r
+
+
+def _float_colsum_check(p, D, a_logical=None):
+    """sum_m D[m,n] vs sum_k (sum_m A[m,k]) B[k,n] + sum_m C[m,n] (fp64)."""
+    M, N, K = p["M"], p["N"], p["K"]
+    A = lib_decode(p["a_type"], p["A"] if a_logical is None else a_logical)
+    B = lib_decode(p["b_type"], p["B"])  # [N, K]
+    C = p["C"].astype(np.float64) if p["C"] is not None else np.zeros((M, N))
+    ref = B @ A.sum(axis=0) + C.sum(axis=0)
+    sabs = np.abs(B) @ np.abs(A).sum(axis=0) + np.abs(C).sum(axis=0)
+    if p["d_type"] == "f32":
+        d = D.astype(np.float64)
+        slack = np.abs(d).sum(axis=0) * 2.0 ** -23
+    else:
+        d = lib_decode(p["d_type"], D)
+        slack = ulp16(d, p["d_type"]).sum(axis=0) * 2
+    got = d.sum(axis=0)
+    bound = TOL[p["a_type"]] * sabs + slack
+    bad = np.abs(got - ref) > bound
+    say("  column sums: max |diff|/bound = %.3g" % float((np.abs(got - ref) / bound).max()))
+    assert not bad.any(), np.flatnonzero(bad)[:10]
+
+
+def test_full_f16_128(orc):
+    say("workload f16 128^3 (full oracle)")
+    p = inputs.dense_f16(128, 128, 128)
+    D, name = _run(p)
+    Dr, Y, S = orc.gemm(p["A"], p["B"], p["C"], None, 128, 128, 128, "f16", "f16", "f32")
+    r = check(D, "f32", Dr, Y, S, "f16")
+    say("  ", name, r)
+    assert r.ok, r
+
+
+def test_full_bf16_8192(orc):
+    say("workload bf16 8192^3 -> bf16")
+    p = inputs.dense_bf16(8192, 8192, 8192)
+    D, name = _run(p)
+    assert name.startswith("tiled256")
+    _check_samples(orc, p, D, seed=1)
+    _float_colsum_check(p, D)
+
+
+def test_full_bf16_skinny(orc):
+    say("workload bf16 16x8192x8192 -> bf16 (full oracle)")
+    p = inputs.dense_bf16(16, 8192, 8192)
+    D, name = _run(p)
+    assert name.startswith("skinny")
+    Dr, Y, S = orc.gemm(p["A"], p["B"], p["C"], None, 16, 8192, 8192, "bf16", "bf16", "bf16")
+    r = check(D, "bf16", Dr, Y, S, "bf16")
+    say("  ", r)
+    assert r.ok, r
+
+
+def test_full_s8_8192(orc):
+    say("workload s8 8192^3 -> s32")
+    p = inputs.dense_s8(8192, 8192, 8192)
+    D, name = _run(p)
+    _check_samples(orc, p, D, seed=3)
+    # exact column sums modulo 2^32
+    colA = p["A"].astype(np.int64).sum(axis=0)                 # [K]
+    ref = p["B"].astype(np.int64) @ colA + p["C"].astype(np.int64).sum(axis=0)
+    got = D.astype(np.int64).sum(axis=0)
+    assert np.array_equal(np.mod(got, 2 ** 32), np.mod(ref, 2 ** 32))
+    say("  column sums exact")
+
+
+def test_full_fp8_8192(orc):
+    say("workload fp8 e4m3 x e5m2 8192^3 -> relu(alpha acc + bias) f16")
+    p = inputs.dense_fp8(8192, 8192, 8192)
+    D, name = _run(p)
+    _check_samples(orc, p, D, seed=4)
+    # the fused epilogue, bit for bit, against the same kernel's fp32 output
+    T, name32 = _run(p, d_type="f32", alpha=1.0, bias=False, relu=False)
+    assert name32.split("_")[0] == name.split("_")[0]
+    ref = orc.epilogue_f32(T, p["alpha"], p["bias"], True, "f16")
+    mism = int((D != ref).sum())
+    say("  fused epilogue mismatches:", mism)
+    assert mism == 0
+
+
+def test_full_sparse24_8192(orc):
+    say("workload 2:4 f16 8192^3 -> f32")
+    p = inputs.sparse24_f16(8192, 8192, 8192)
+    M, K = 8192, 8192
+    vb, mb = G.gemm_sparse24_sizes(M, K)
+    vals = torch.empty(vb, dtype=torch.uint8, device="cuda")
+    meta = torch.empty(mb, dtype=torch.uint8, device="cuda")
+    G.gemm_sparse24_compress(M, K, "f16", to_dev(p["A_logical"]), vals, meta)
+    rv, rm = orc.sparse24_compress(p["A_logical"])
+    assert np.array_equal(vals.cpu().numpy().view(np.uint16).reshape(rv.shape), rv)
+    assert np.array_equal(meta.cpu().numpy().view(np.uint32).reshape(rm.shape), rm)
+    say("  compressor bytes identical to the oracle's")
+    D, name = _run(p, sparse_dev=(vals, meta))
+    assert name.startswith("sparse24_tiled")
+    pd = dict(p)
+    pd["A"] = p["A_logical"]
+    _check_samples(orc, pd, D, a_logical=p["A_logical"], seed=5)
+    _float_colsum_check(pd, D, a_logical=p["A_logical"])
