@@ -19,9 +19,9 @@
 
 #include "kernel_args.hpp"
 
-// Lambdas in the kernels are always inlined: a lambda left as a call would
-// force everything it captures by reference (the accumulators, the kernel
-// arguments) into scratch memory.
+// Device helpers and the lambdas in the kernels are always inlined: a call
+// left in place would force everything passed or captured by reference (the
+// accumulators, the kernel arguments) into scratch memory.
 #define STG_AI __attribute__((always_inline))
 
 namespace stg {
@@ -140,13 +140,13 @@ struct Op16S8 {
 
 // ---------------------------------------------------------------- epilogue
 
-__device__ inline uint16_t f32_to_f16_bits(float x)
+__device__ STG_AI inline uint16_t f32_to_f16_bits(float x)
 {
     _Float16 h = (_Float16)x; // v_cvt_f16_f32: round to nearest even
     return __builtin_bit_cast(uint16_t, h);
 }
 
-__device__ inline uint16_t f32_to_bf16_bits(float x)
+__device__ STG_AI inline uint16_t f32_to_bf16_bits(float x)
 {
     __bf16 h = (__bf16)x; // gfx950 v_cvt_pk_bf16_f32: round to nearest even
     return __builtin_bit_cast(uint16_t, h);
@@ -156,7 +156,7 @@ __device__ inline uint16_t f32_to_bf16_bits(float x)
 // kind KIND: t = acc (+C); y = has_bias ? fmaf(alpha, t, bias[col]) : alpha*t;
 // relu; round-to-nearest-even cast and store.  Integer: D = acc + C mod 2^32.
 template <int KIND>
-__device__ inline void epilogue_store(const EpiArgs &e, int64_t row, int64_t col, float acc)
+__device__ STG_AI inline void epilogue_store(const EpiArgs &e, int64_t row, int64_t col, float acc)
 {
     float t = acc;
     if (e.C)
@@ -174,7 +174,7 @@ __device__ inline void epilogue_store(const EpiArgs &e, int64_t row, int64_t col
 }
 
 template <int KIND>
-__device__ inline void epilogue_store(const EpiArgs &e, int64_t row, int64_t col, int acc)
+__device__ STG_AI inline void epilogue_store(const EpiArgs &e, int64_t row, int64_t col, int acc)
 {
     uint32_t t = (uint32_t)acc;
     if (e.C)
@@ -184,7 +184,7 @@ __device__ inline void epilogue_store(const EpiArgs &e, int64_t row, int64_t col
 
 // Store one 32x32 accumulator fragment whose top-left output is (m0, n0).
 template <class OP, int KIND>
-__device__ inline void epilogue_fragment_k(const EpiArgs &e, const typename OP::acc_t &acc,
+__device__ STG_AI inline void epilogue_fragment_k(const EpiArgs &e, const typename OP::acc_t &acc,
                                            int64_t m0, int64_t n0, int lane)
 {
     const int64_t col = n0 + (lane & 31);
@@ -201,7 +201,7 @@ __device__ inline void epilogue_fragment_k(const EpiArgs &e, const typename OP::
 // Store an FM x FN grid of 32x32 fragments (fragment (i,j) at
 // (m0 + 32 i, n0 + 32 j)); the output-type switch sits outside the loops.
 template <class OP, int FM, int FN>
-__device__ inline void epilogue_grid(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
+__device__ STG_AI inline void epilogue_grid(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
                                      int64_t m0, int64_t n0, int lane)
 {
     auto run = [&](auto kind) STG_AI {
@@ -225,71 +225,139 @@ __device__ inline void epilogue_grid(const EpiArgs &e, typename OP::acc_t (&acc)
 
 // ---------------------------------------------------------------- LDS-staged epilogue
 
-// Four consecutive columns of one output row, col .. col+3 (all < N), with
-// 16-byte aligned C / bias rows and an output row aligned to 4 elements.
-template <int KIND>
-__device__ inline void epilogue_store4(const EpiArgs &e, int64_t row, int64_t col, f4_t v)
+// A 64-bit value that is equal in all active lanes, as a scalar.
+__device__ STG_AI inline int64_t wave_uniform(int64_t x)
 {
-    if (e.C)
-        v += *(const f4_t *)((const float *)e.C + row * e.ldc + col);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (clamped to 2^31 - 1);
+// loads outside the range read zero and stores outside it are dropped.
+__device__ STG_AI inline __amdgpu_buffer_rsrc_t epi_rsrc(const void *base, int64_t bytes)
+{
+    const int n = bytes <= 0 ? 0 : bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+}
+
+// alpha * t (+ bias), then relu, for four fp32 values; the bias form is one
+// fused multiply-add per element, the same operation the oracle's fp32
+// epilogue performs.
+__device__ STG_AI inline f4_t epi_affine(const EpiArgs &e, f4_t t, f4_t b)
+{
     f4_t y;
     if (e.bias) {
-        const f4_t b = *(const f4_t *)(e.bias + col);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            y[q] = __builtin_fmaf(e.alpha, v[q], b[q]);
+            y[q] = __builtin_fmaf(e.alpha, t[q], b[q]);
     } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            y[q] = e.alpha * v[q];
+            y[q] = e.alpha * t[q];
     }
     if (e.relu) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             y[q] = (y[q] > 0.0f) ? y[q] : 0.0f;
     }
-    const int64_t o = row * e.ldd + col;
-    if constexpr (KIND == OUT_F32) {
-        *(f4_t *)((float *)e.D + o) = y;
-    } else {
-        uint2 packed;
-        if constexpr (KIND == OUT_F16) {
-            packed.x = f32_to_f16_bits(y[0]) | ((uint32_t)f32_to_f16_bits(y[1]) << 16);
-            packed.y = f32_to_f16_bits(y[2]) | ((uint32_t)f32_to_f16_bits(y[3]) << 16);
-        } else {
-            packed.x = f32_to_bf16_bits(y[0]) | ((uint32_t)f32_to_bf16_bits(y[1]) << 16);
-            packed.y = f32_to_bf16_bits(y[2]) | ((uint32_t)f32_to_bf16_bits(y[3]) << 16);
-        }
-        *(uint2 *)((uint16_t *)e.D + o) = packed;
-    }
+    return y;
 }
 
+// Store four finished values at byte offset voff + soff of the D resource.
 template <int KIND>
-__device__ inline void epilogue_store4(const EpiArgs &e, int64_t row, int64_t col, i4_t v)
+__device__ STG_AI inline void epi_store4(__amdgpu_buffer_rsrc_t rd, int voff, int soff, f4_t y)
 {
-    if (e.C) {
-        const i4_t c = *(const i4_t *)((const int32_t *)e.C + row * e.ldc + col);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            v[q] = (int)((uint32_t)v[q] + (uint32_t)c[q]);
+    if constexpr (KIND == OUT_F32) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, y), rd, voff, soff, 0);
+    } else {
+        typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+        u2_t w;
+        if constexpr (KIND == OUT_F16) {
+            w[0] = f32_to_f16_bits(y[0]) | ((uint32_t)f32_to_f16_bits(y[1]) << 16);
+            w[1] = f32_to_f16_bits(y[2]) | ((uint32_t)f32_to_f16_bits(y[3]) << 16);
+        } else {
+            w[0] = f32_to_bf16_bits(y[0]) | ((uint32_t)f32_to_bf16_bits(y[1]) << 16);
+            w[1] = f32_to_bf16_bits(y[2]) | ((uint32_t)f32_to_bf16_bits(y[3]) << 16);
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(w, rd, voff, soff, 0);
     }
-    *(i4_t *)((int32_t *)e.D + row * e.ldd + col) = v;
 }
 
-// Epilogue of a wave's (32 FM) x (32 FN) accumulator block at (m0, n0),
+// acc + C, four elements: fp32 addition, or int32 addition modulo 2^32
+__device__ STG_AI inline f4_t add_c(f4_t v, f4_t c) { return v + c; }
+__device__ STG_AI inline i4_t add_c(i4_t v, i4_t c)
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        v[q] = (int)((uint32_t)v[q] + (uint32_t)c[q]);
+    return v;
+}
+
+// Epilogue of a wave's (32 FM) x (32 FN) accumulator block at (m0, n0)
+// (the same in every lane),
 // staged through `lds_wave` (32 * (32 FN + 4) words of LDS owned by this
 // wave): for each 32-row slab, the fragments are written to LDS in row-major
 // order, then read back four consecutive columns per lane, so C and bias are
-// read and D is written with 8- or 16-byte accesses along the rows.
+// read and D is written with 16- or 8-byte accesses along the rows.
+//
+// When every column of the block is inside the matrix and the host marked
+// the operands as vector-aligned (e.vec), C and D are addressed through
+// buffer resources that start at the block's first row and end at row M:
+// rows past M read as zero and their stores are dropped, so no lane
+// branches, the row step between passes is a scalar offset, and all C loads
+// of a slab are issued before the slab is staged (their latency is paid
+// once per slab).  Other blocks take an element-by-element path.
 template <class OP, int FM, int FN, int KIND>
-__device__ inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
+__device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
                                       int64_t m0, int64_t n0, int lane, uint32_t *lds_wave)
 {
     constexpr int COLS = 32 * FN, PITCH = COLS + 4, LPR = COLS / 4; // lanes per row
     constexpr int RPP = 64 / LPR;                                    // rows per pass
+    constexpr int NP = 32 / RPP;                                     // passes per slab
+    constexpr int DB = KIND == OUT_F32 || KIND == OUT_S32 ? 4 : 2;  // D element bytes
     typedef std::conditional_t<OP::INT, i4_t, f4_t> v4_t;
+    // m0 and n0 are the same in every lane; saying so keeps the buffer
+    // resources built from them in scalar registers
+    m0 = wave_uniform(m0);
+    n0 = wave_uniform(n0);
+    const int c4 = (lane % LPR) * 4;
+    const int rl = lane / LPR;          // row of this lane within a pass
+    const int64_t col = n0 + c4;
+    const bool has_c = e.C != nullptr;
+    const bool fast = e.vec && n0 + COLS <= e.N; // uniform across the wave
+
+    // the host enables e.vec only when 257 rows of C and of D span less
+    // than 2^31 bytes, so every offset below fits in 32 bits (the resources
+    // are empty when unused)
+    const int ldd_b = (int)(e.ldd * DB);
+    const int ldc_b = has_c ? (int)(e.ldc * 4) : 0;
+    const __amdgpu_buffer_rsrc_t rd =
+        epi_rsrc((uint8_t *)e.D + m0 * e.ldd * DB, fast ? (e.M - m0) * e.ldd * DB : 0);
+    const __amdgpu_buffer_rsrc_t rc =
+        epi_rsrc(has_c ? (const uint8_t *)e.C + m0 * e.ldc * 4 : (const uint8_t *)e.D,
+                 fast && has_c ? (e.M - m0) * e.ldc * 4 : 0);
+    const int vd = rl * ldd_b + (int)(col * DB);
+    const int vc = rl * ldc_b + (int)(col * 4);
+    f4_t bv{};
+    if constexpr (!OP::INT) {
+        if (fast && e.bias)
+            bv = *(const f4_t *)(e.bias + col);
+    }
+
+    // fully unrolled, so the accumulator indices are constants
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+        // keep each slab's C loads from being hoisted above earlier slabs
+        // (that would need C registers for the whole block at once)
+        __builtin_amdgcn_sched_barrier(0);
+        u4_t cv[NP];
+        if (fast && has_c) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+                cv[p] = __builtin_bit_cast(
+                    u4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, vc, (32 * i + p * RPP) * ldc_b, 0));
+        }
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -302,16 +370,25 @@ __device__ inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_t (&acc
             }
         __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): the slab is in LDS
         __builtin_amdgcn_wave_barrier();
-        const int c4 = (lane % LPR) * 4;
-        const int64_t col = n0 + c4;
-        for (int p = 0; p < 32 / RPP; ++p) {
-            const int rr = p * RPP + lane / LPR;
-            const int64_t row = m0 + 32 * i + rr;
-            const v4_t v = __builtin_bit_cast(v4_t, *(const u4_t *)(lds_wave + rr * PITCH + c4));
-            if (row < e.M) {
-                if (e.vec && col + 3 < e.N) {
-                    epilogue_store4<KIND>(e, row, col, v);
-                } else {
+        if (fast) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int rr = p * RPP + rl;
+                v4_t v = __builtin_bit_cast(v4_t, *(const u4_t *)(lds_wave + rr * PITCH + c4));
+                if (has_c)
+                    v = add_c(v, __builtin_bit_cast(v4_t, cv[p]));
+                const int soff = (32 * i + p * RPP) * ldd_b;
+                if constexpr (OP::INT)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v), rd, vd, soff, 0);
+                else
+                    epi_store4<KIND>(rd, vd, soff, epi_affine(e, v, bv));
+            }
+        } else {
+            for (int p = 0; p < NP; ++p) {
+                const int rr = p * RPP + rl;
+                const int64_t row = m0 + 32 * i + rr;
+                const v4_t v = __builtin_bit_cast(v4_t, *(const u4_t *)(lds_wave + rr * PITCH + c4));
+                if (row < e.M) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
                         if (col + q < e.N)
@@ -324,8 +401,9 @@ __device__ inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_t (&acc
     }
 }
 
+
 template <class OP, int FM, int FN>
-__device__ inline void epilogue_grid_lds(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
+__device__ STG_AI inline void epilogue_grid_lds(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
                                          int64_t m0, int64_t n0, int lane, uint32_t *lds_wave)
 {
     if constexpr (OP::INT) {

@@ -161,6 +161,10 @@ const char *family_name(int f)
     case KF_SPARSE_TILED: return "sparse24_tiled";
     case KF_TILED_DMA4: return "tiled256dma4";
     case KF_TILED_DMA5: return "tiled256dma5";
+    case KF_TILED_256W8: return "tiled256w8";
+    case KF_TILED_256W8T: return "tiled256w8t";
+    case KF_PINGPONG4: return "pingpong4";
+    case KF_PINGPONG5: return "pingpong5";
     default: return "?";
     }
 }
@@ -175,7 +179,12 @@ bool skinny_ok(const gemm_desc_t &d)
            d.lda * eb * 16 < lim && d.ldb * eb * 32 < lim;
 }
 
-bool is_tiled(int f) { return f == KF_TILED_256 || f == KF_TILED_128 || f == KF_TILED_DMA4 || f == KF_TILED_DMA5; }
+bool is_tiled(int f)
+{
+    return f == KF_TILED_256 || f == KF_TILED_128 || f == KF_TILED_DMA4 || f == KF_TILED_DMA5 ||
+           f == KF_TILED_256W8 || f == KF_TILED_256W8T || f == KF_PINGPONG4 ||
+           f == KF_PINGPONG5;
+}
 
 } // namespace
 
@@ -308,13 +317,20 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     const bool skinny = skinny_ok(d);
     int fam = -1;
     const int64_t big_tiles = ceil_div(d.M, 256) * ceil_div(d.N, 256);
-    const int auto_tiled = big_tiles >= di.num_cu ? KF_TILED_256 : KF_TILED_128;
+    // 256 x 256 tiles: the fastest variant measured per operand type on
+    // MI355X at 8192^3 (16-bit: 8 waves of 128 x 64; int8: 8 waves of
+    // 64 x 128; fp8: 4 waves of 128 x 128, whose 8-wave forms run short of
+    // registers)
+    const int op = op_kind(d.a_type, d.b_type);
+    const int fam256 = op == OPK_S8 ? KF_TILED_256W8T
+                       : (op == OPK_F16 || op == OPK_BF16) ? KF_TILED_256W8 : KF_TILED_256;
+    const int auto_tiled = big_tiles >= di.num_cu ? fam256 : KF_TILED_128;
     switch (d.algo) {
     case GEMM_ALGO_AUTO: fam = skinny ? KF_SKINNY : tiled ? auto_tiled : KF_GENERIC; break;
     case GEMM_ALGO_SKINNY: fam = skinny ? KF_SKINNY : -1; break;
     case GEMM_ALGO_TILED: fam = tiled ? auto_tiled : -1; break;
     case GEMM_ALGO_TILED_128: fam = tiled ? KF_TILED_128 : -1; break;
-    case GEMM_ALGO_TILED_256: fam = tiled ? KF_TILED_256 : -1; break;
+    case GEMM_ALGO_TILED_256: fam = tiled ? fam256 : -1; break;
     case GEMM_ALGO_GENERIC: fam = KF_GENERIC; break;
     default: fam = -1;
     }
@@ -381,8 +397,12 @@ static EpiArgs make_epi(const gemm_desc_t &d, const void *C, const void *bias, v
     e.D = D;
     e.ldd = d.ldd;
     const int db = elem_bytes(d.d_type);
-    e.vec = (!d.has_c || (aligned(C, 16) && d.ldc % 4 == 0)) &&
-            (!d.has_bias || aligned(bias, 16)) && aligned(D, 4 * db) && d.ldd % 4 == 0;
+    // the vector epilogue addresses a block's C and D rows with 32-bit
+    // offsets: 257 rows of each must span less than 2^31 bytes
+    const int64_t lim = 0x7fffffff / 257;
+    e.vec = (!d.has_c || (aligned(C, 16) && d.ldc % 4 == 0 && d.ldc * 4 < lim)) &&
+            (!d.has_bias || aligned(bias, 16)) && aligned(D, 4 * db) && d.ldd % 4 == 0 &&
+            d.ldd * db < lim;
     return e;
 }
 

@@ -30,6 +30,10 @@ enum KernelFamily {
     KF_SPARSE_TILED,
     KF_TILED_DMA4, // 256 x 256, direct global -> LDS copies, 4 LDS stages
     KF_TILED_DMA5, // same with 5 LDS stages (160 KB)
+    KF_TILED_256W8,  // 256 x 256, 8 waves (2 per SIMD) as 2 x 4, 128 x 64 per wave
+    KF_TILED_256W8T, // 256 x 256, 8 waves as 4 x 2, 64 x 128 per wave
+    KF_PINGPONG4,    // 256 x 256, 8 waves in two out-of-phase groups, 4 LDS stages
+    KF_PINGPONG5,    // same with 5 LDS stages
     KF_COUNT
 };
 

@@ -40,7 +40,7 @@ namespace stg {
 // ---------------------------------------------------------------- generic
 
 template <int ELEM, int LE>
-__device__ inline void load_frag_strided(uint32_t *out, const void *base, bool row_ok,
+__device__ STG_AI inline void load_frag_strided(uint32_t *out, const void *base, bool row_ok,
                                          int64_t row_off, int64_t kstride, int64_t k0, int64_t K)
 {
     if constexpr (ELEM == 2) {
@@ -96,13 +96,13 @@ __global__ __launch_bounds__(256) void k_generic(GemmArgs g)
 
 // Tile-local buffer resource: loads at byte offsets >= `bytes` return zero,
 // so rows past the edge of the matrix need no clamping or masking.
-__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, int64_t bytes)
+__device__ STG_AI inline __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, int64_t bytes)
 {
     const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
 }
 
-__device__ inline u4_t buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+__device__ STG_AI inline u4_t buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
 {
     return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
@@ -113,7 +113,7 @@ __device__ inline u4_t buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
 // every 4 rows is conflict-free, while the textbook 32-bank XOR patterns
 // ((r >> 1) & 3, r & 3, and mixes of them) stall 2- to 4-way.
 // swz64(r + 32 i) == swz64(r).
-__device__ inline int swz64(int r) { return (r >> 2) & 3; }
+__device__ STG_AI inline int swz64(int r) { return (r >> 2) & 3; }
 
 // Number of the `total` memory instructions that follow MFMA slot q of
 // `slots` when they are spread evenly.
@@ -124,7 +124,7 @@ constexpr int spread(int q, int total, int slots)
 
 // Workgroup id -> (tile_m, tile_n): XCD-contiguous renumbering, then groups
 // of GM tile rows walked column by column.
-__device__ inline void tile_coords(int id, int tiles_m, int tiles_n, int &tm, int &tn)
+__device__ STG_AI inline void tile_coords(int id, int tiles_m, int tiles_n, int &tm, int &tn)
 {
     constexpr int GM = 8;
     const int total = tiles_m * tiles_n;
@@ -139,21 +139,27 @@ __device__ inline void tile_coords(int id, int tiles_m, int tiles_n, int &tm, in
     tn = in / gsize;
 }
 
-template <class OP, int BM, int BN>
-__global__ __launch_bounds__(256, 1) void k_tiled(GemmArgs g, int tiles_m, int tiles_n)
+template <class OP, int BM, int BN, int GM = 2, int GN = 2>
+__global__ __launch_bounds__(64 * GM * GN, 1) void k_tiled(GemmArgs g, int tiles_m, int tiles_n)
 {
+    constexpr int NT = 64 * GM * GN;        // GM x GN waves
     constexpr int BKB = 64;                 // K bytes per tile
     constexpr int CH = BKB / 16;            // 16-byte chunks per row
-    constexpr int RPP = 256 / CH;           // rows covered per load pass
+    constexpr int RPP = NT / CH;            // rows covered per load pass
     constexpr int A_LD = BM / RPP, B_LD = BN / RPP;
-    constexpr int WM = BM / 2, WN = BN / 2; // wave sub-tile (2 x 2 waves)
+    constexpr int WM = BM / GM, WN = BN / GN; // wave sub-tile
     constexpr int FM = WM / 32, FN = WN / 32;
     constexpr int NSTAGE = 3;
     constexpr int STAGE = (BM + BN) * BKB;
     constexpr int NV = OP::LANE_BYTES / 16; // 16-byte LDS reads per operand
     constexpr int FW = OP::LANE_BYTES / 4;  // 32-bit words per operand fragment
     constexpr int KS = BKB / OP::KB;        // MFMA K steps per tile
-    __shared__ __attribute__((aligned(16))) uint8_t lds[NSTAGE * STAGE];
+    // LDS holds the stages during the K loop and the epilogue's per-wave
+    // 32-row staging slabs afterwards
+    constexpr int EPI = GM * GN * 32 * (WN + 4) * 4;
+    constexpr int LDS_BYTES = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int tm, tn;
@@ -198,7 +204,7 @@ __global__ __launch_bounds__(256, 1) void k_tiled(GemmArgs g, int tiles_m, int t
     };
 
     // fragment reads: lane reads rows arow + 32 i (A) and brow + 32 j (B)
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / GN, wn = wave % GN;
     const int arow = wm * WM + (lane & 31), brow = wn * WN + (lane & 31);
     const int half = lane >> 5;
     const int sa = swz64(arow), sb = swz64(brow); // same for every fragment row
@@ -332,7 +338,7 @@ __global__ __launch_bounds__(256, 1) void k_tiled(GemmArgs g, int tiles_m, int t
 
 // 16-byte global -> LDS copy for a whole wave: lane l's 16 bytes land at
 // lds_wave + 16 l (lds_wave must be wave-uniform).
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_wave, int voff, int soff)
+__device__ STG_AI inline void dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_wave, int voff, int soff)
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void *)lds_wave, 16, voff, soff, 0, 0);
@@ -362,6 +368,7 @@ __global__ __launch_bounds__(256, 1) void k_tiled_dma(GemmArgs g, int tiles_m, i
     constexpr int B_INST = BN / ROWS_PER_INST / 4;
     constexpr int NI = A_INST + B_INST;                // DMA instructions per wave per tile
     static_assert(NSTAGE >= 4, "the fragment prefetch needs tile t+1 two tiles early");
+    static_assert(4 * 32 * (WN + 4) * 4 <= NSTAGE * STAGE, "epilogue staging fits in LDS");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -509,6 +516,152 @@ __global__ __launch_bounds__(256, 1) void k_tiled_dma(GemmArgs g, int tiles_m, i
                                   (uint32_t *)lds + wave * 32 * (WN + 4));
 }
 
+// ---------------------------------------------------------------- ping-pong
+
+// 256 x 256 tile, 8 waves in two groups of four (one wave of each group per
+// SIMD): group 0 owns output columns 0..127 of the tile, group 1 columns
+// 128..255, each wave a 128 x 64 block of 32x32 fragments.  The groups run
+// out of phase: in phase 1 of K tile t group 0 multiplies tile t while group
+// 1 reads its fragments of tile t from LDS and issues direct global -> LDS
+// copies of a future tile; in phase 2 the roles swap (group 1 multiplies,
+// group 0 reads tile t+1's fragments and issues copies).  One barrier ends
+// each phase, so each SIMD always has one wave issuing MFMAs from registers
+// while the other wave's memory work is in flight.
+// Copies: tile u's A operand is requested by group 0 in phase 2 of tile
+// u - NSTAGE, its B operand by group 1 in phase 1 of tile u - NSTAGE + 1;
+// both are waited for (by the requesting waves) before the barrier that ends
+// phase 1 of tile u - 1, the last point before tile u is first read.
+template <class OP, int NSTAGE>
+__global__ __launch_bounds__(512, 1) void k_pingpong(GemmArgs g, int tiles_m, int tiles_n)
+{
+    constexpr int BM = 256, BN = 256, BKB = 64;
+    constexpr int WM = 128, WN = 64, FM = WM / 32, FN = WN / 32;
+    constexpr int STAGE = (BM + BN) * BKB;
+    constexpr int NV = OP::LANE_BYTES / 16;
+    constexpr int FW = OP::LANE_BYTES / 4;
+    constexpr int KS = BKB / OP::KB;
+    constexpr int NI = (BM * BKB / 1024) / 4; // copy instructions per wave per operand half
+    constexpr int EPI = 8 * 32 * (WN + 4) * 4;
+    constexpr int LDS_BYTES = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
+    static_assert(NSTAGE >= 3 && LDS_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wq = wave & 3;
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m_blk = (int64_t)tm * BM, n_blk = (int64_t)tn * BN;
+    const int64_t lda_b = g.a_rs * OP::ELEM, ldb_b = g.b_cs * OP::ELEM;
+    const int64_t kbytes = g.K * OP::ELEM;
+    const int KT = (int)(kbytes / BKB);
+    const __amdgpu_buffer_rsrc_t ra = tile_rsrc((const uint8_t *)g.A + m_blk * lda_b,
+                                                (g.e.M - m_blk - 1) * lda_b + kbytes);
+    const __amdgpu_buffer_rsrc_t rb = tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b,
+                                                (g.e.N - n_blk - 1) * ldb_b + kbytes);
+
+    // copies: group 0 fills the A half of a stage, group 1 the B half; wave
+    // wq of a group owns 1 KB blocks wq*NI .. wq*NI+NI-1 (16 rows each)
+    const __amdgpu_buffer_rsrc_t rsrc = grp == 0 ? ra : rb;
+    const int64_t ld_b = grp == 0 ? lda_b : ldb_b;
+    int voff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int row = (wq * NI + i) * 16 + (lane >> 2);
+        voff[i] = row * (int)ld_b + (((lane & 3) ^ swz64(row)) << 4);
+    }
+    const int half_off = grp * BM * BKB;
+    auto copy_tile = [&](int stage, int kt) STG_AI {
+        uint8_t *base = lds + stage * STAGE + half_off + wq * NI * 1024;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            dma16(rsrc, base + i * 1024, voff[i], kt * BKB);
+    };
+
+    // fragments of this wave: rows wm*128 + 32 i of A, columns grp*128 + wn*64 + 32 j of B
+    const int wm = wq >> 1, wn = wq & 1;
+    const int arow = wm * WM + (lane & 31), brow = grp * 128 + wn * WN + (lane & 31);
+    const int half = lane >> 5;
+    const int sa = swz64(arow), sb = swz64(brow);
+    const int a_off = arow * BKB, b_off = BM * BKB + brow * BKB;
+    uint32_t fa[KS][FM][FW], fb[KS][FN][FW];
+    auto lread = [&](const uint8_t *__restrict__ stage_base) STG_AI {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int c0 = (s * OP::KB + half * OP::LANE_BYTES) >> 4;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int oa = ((c0 + v) ^ sa) << 4, ob = ((c0 + v) ^ sb) << 4;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    *(u4_t *)&fa[s][i][4 * v] = *(const u4_t *)(stage_base + a_off + i * 32 * BKB + oa);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    *(u4_t *)&fb[s][j][4 * v] = *(const u4_t *)(stage_base + b_off + j * 32 * BKB + ob);
+            }
+        }
+    };
+    typename OP::acc_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = typename OP::acc_t{};
+    auto compute = [&]() STG_AI {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = OP::mma(fa[s][i], fb[s][j], acc[i][j]);
+    };
+    auto stage_of = [&](int kt) STG_AI { return kt % NSTAGE; };
+
+    // prologue: tiles 0 .. NSTAGE-2 (both halves) and the A half of tile
+    // NSTAGE-1, in the same per-group order the loop continues
+#pragma unroll
+    for (int u = 0; u < NSTAGE - 1; ++u)
+        copy_tile(u, u);
+    if (grp == 0)
+        copy_tile(NSTAGE - 1, NSTAGE - 1);
+    STG_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    if (grp == 0)
+        lread(lds);
+
+    for (int t = 0; t < KT; ++t) {
+        // ---- phase 1: group 0 multiplies tile t; group 1 reads tile t and
+        // requests the B half of tile t + NSTAGE - 1
+        if (grp == 0) {
+            compute();
+            // this wave's requests up to tile t+1 complete (tiles t+2 ..
+            // t+NSTAGE-1 may still be in flight)
+            STG_WAIT_VMCNT((NSTAGE - 2) * NI);
+        } else {
+            lread(lds + stage_of(t) * STAGE);
+            copy_tile(stage_of(t + NSTAGE - 1), t + NSTAGE - 1);
+            STG_WAIT_VMCNT((NSTAGE - 2) * NI);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        // ---- phase 2: group 1 multiplies tile t; group 0 reads tile t+1 and
+        // requests the A half of tile t + NSTAGE
+        if (grp == 1) {
+            compute();
+        } else {
+            lread(lds + stage_of(t + 1) * STAGE);
+            copy_tile(stage_of(t + NSTAGE), t + NSTAGE);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+    }
+    STG_WAIT_VMCNT(0);
+    __syncthreads();
+    epilogue_grid_lds<OP, FM, FN>(g.e, acc, m_blk + wm * WM, n_blk + grp * 128 + wn * WN, lane,
+                                  (uint32_t *)lds + wave * 32 * (WN + 4));
+}
+
 // ---------------------------------------------------------------- skinny
 
 // Small-M GEMM (M <= 16), bound by streaming B once from HBM.  One workgroup
@@ -636,12 +789,12 @@ static hipError_t launch_generic_t(const GemmArgs &g, hipStream_t s)
     return hipGetLastError();
 }
 
-template <class OP, int BM, int BN>
+template <class OP, int BM, int BN, int GM = 2, int GN = 2>
 static hipError_t launch_tiled_t(const GemmArgs &g, hipStream_t s)
 {
     const int tiles_m = (int)((g.e.M + BM - 1) / BM), tiles_n = (int)((g.e.N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_tiled<OP, BM, BN>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
-                       s, g, tiles_m, tiles_n);
+    hipLaunchKernelGGL((k_tiled<OP, BM, BN, GM, GN>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(64 * GM * GN), 0, s, g, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -661,17 +814,41 @@ static dense_launch_fn generic_table(int op)
     }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int GM = 2, int GN = 2>
 static dense_launch_fn tiled_table_t(int op)
 {
     switch (op) {
-    case OPK_F16: return launch_tiled_t<OpF16, BM, BN>;
-    case OPK_BF16: return launch_tiled_t<OpBF16, BM, BN>;
-    case OPK_F8_E4E4: return launch_tiled_t<OpF8<0, 0>, BM, BN>;
-    case OPK_F8_E4E5: return launch_tiled_t<OpF8<0, 1>, BM, BN>;
-    case OPK_F8_E5E4: return launch_tiled_t<OpF8<1, 0>, BM, BN>;
-    case OPK_F8_E5E5: return launch_tiled_t<OpF8<1, 1>, BM, BN>;
-    case OPK_S8: return launch_tiled_t<OpS8, BM, BN>;
+    case OPK_F16: return launch_tiled_t<OpF16, BM, BN, GM, GN>;
+    case OPK_BF16: return launch_tiled_t<OpBF16, BM, BN, GM, GN>;
+    case OPK_F8_E4E4: return launch_tiled_t<OpF8<0, 0>, BM, BN, GM, GN>;
+    case OPK_F8_E4E5: return launch_tiled_t<OpF8<0, 1>, BM, BN, GM, GN>;
+    case OPK_F8_E5E4: return launch_tiled_t<OpF8<1, 0>, BM, BN, GM, GN>;
+    case OPK_F8_E5E5: return launch_tiled_t<OpF8<1, 1>, BM, BN, GM, GN>;
+    case OPK_S8: return launch_tiled_t<OpS8, BM, BN, GM, GN>;
+    default: return nullptr;
+    }
+}
+
+template <class OP, int NS>
+static hipError_t launch_pingpong_t(const GemmArgs &g, hipStream_t s)
+{
+    const int tiles_m = (int)((g.e.M + 255) / 256), tiles_n = (int)((g.e.N + 255) / 256);
+    hipLaunchKernelGGL((k_pingpong<OP, NS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, s,
+                       g, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+template <int NS>
+static dense_launch_fn pingpong_table(int op)
+{
+    switch (op) {
+    case OPK_F16: return launch_pingpong_t<OpF16, NS>;
+    case OPK_BF16: return launch_pingpong_t<OpBF16, NS>;
+    case OPK_F8_E4E4: return launch_pingpong_t<OpF8<0, 0>, NS>;
+    case OPK_F8_E4E5: return launch_pingpong_t<OpF8<0, 1>, NS>;
+    case OPK_F8_E5E4: return launch_pingpong_t<OpF8<1, 0>, NS>;
+    case OPK_F8_E5E5: return launch_pingpong_t<OpF8<1, 1>, NS>;
+    case OPK_S8: return launch_pingpong_t<OpS8, NS>;
     default: return nullptr;
     }
 }
@@ -730,6 +907,10 @@ hipError_t launch_dense(int family, int op, const GemmArgs &g, hipStream_t s)
     case KF_TILED_256: fn = tiled_table_t<256, 256>(op); break;
     case KF_TILED_128: fn = tiled_table_t<128, 128>(op); break;
     case KF_SKINNY: fn = skinny_table(op); break;
+    case KF_TILED_256W8: fn = tiled_table_t<256, 256, 2, 4>(op); break;
+    case KF_TILED_256W8T: fn = tiled_table_t<256, 256, 4, 2>(op); break;
+    case KF_PINGPONG4: fn = pingpong_table<4>(op); break;
+    case KF_PINGPONG5: fn = pingpong_table<5>(op); break;
     case KF_TILED_DMA4: fn = dma_table_t<256, 256, 4>(op); break;
     case KF_TILED_DMA5: fn = dma_table_t<256, 256, 5>(op); break;
     default: break;

@@ -26,7 +26,7 @@ typedef _Float16 h16v_t __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- compress
 
-__device__ inline bool f16_nonzero(uint32_t h) { return (h & 0x7FFFu) != 0; }
+__device__ STG_AI inline bool f16_nonzero(uint32_t h) { return (h & 0x7FFFu) != 0; }
 
 // One thread per (row, metadata word): groups 8w .. 8w+7 of row m.
 __global__ __launch_bounds__(256) void k_sparse24_compress(int64_t M, int64_t K,
@@ -126,10 +126,10 @@ __global__ __launch_bounds__(256) void k_sparse_generic(SparseArgs a)
 // ---------------------------------------------------------------- tiled
 
 // Chunk swizzles: 128-byte rows (B tile) and 64-byte rows (compressed A).
-__device__ inline int swz128(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ inline int swz64(int r) { return (r >> 2) & 3; }
+__device__ STG_AI inline int swz128(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ STG_AI inline int swz64(int r) { return (r >> 2) & 3; }
 
-__device__ inline void tile_coords_sp(int id, int tiles_m, int tiles_n, int &tm, int &tn)
+__device__ STG_AI inline void tile_coords_sp(int id, int tiles_m, int tiles_n, int &tm, int &tn)
 {
     constexpr int GM = 8;
     const int total = tiles_m * tiles_n;
@@ -152,7 +152,7 @@ __device__ inline void tile_coords_sp(int id, int tiles_m, int tiles_n, int &tm,
 // column l % 32 of B it supplies K 8h .. 8h+7 in elements 0..7 and
 // 16+8h .. 16+8h+7 in elements 8..15.  (Measured on gfx950 with single-
 // instruction probes; it is exactly this library's nibble packing.)
-__device__ inline f16_t smfmac32(const uint32_t *a, const uint32_t *b, int idx, f16_t c)
+__device__ STG_AI inline f16_t smfmac32(const uint32_t *a, const uint32_t *b, int idx, f16_t c)
 {
     h8_t va = __builtin_bit_cast(h8_t, *(const u4_t *)a);
     h16v_t vb = __builtin_bit_cast(h16v_t, *(const i8_t *)b);
@@ -172,6 +172,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_tiled(SparseArgs a, int tiles
     constexpr int AV_LD = BM * (AVB / 16) / 256; // 16-byte chunks per thread
     constexpr int B_LD = BN * (BB / 16) / 256;
     static_assert(BM <= 256, "one metadata row per thread");
+    static_assert(4 * 32 * (WN + 4) * 4 <= 2 * STAGE, "epilogue staging fits in LDS");
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

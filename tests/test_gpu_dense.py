@@ -66,12 +66,14 @@ def test_dense_parity(orc, a_type, b_type, algo, shape):
     compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, algo, expect_kernel=algo)
 
 
-@pytest.mark.parametrize("family", ["tiled256dma4", "tiled256dma5"])
+@pytest.mark.parametrize("family", ["tiled256", "tiled256dma4", "tiled256dma5", "tiled256w8",
+                                    "tiled256w8t", "pingpong4", "pingpong5"])
 @pytest.mark.parametrize("a_type,b_type", PAIRS)
 @pytest.mark.parametrize("shape", [(600, 520, 256), (256, 256, 64), (300, 700, 448)])
 def test_dense_parity_dma_variants(orc, monkeypatch, family, a_type, b_type, shape):
-    """The direct-to-LDS pipelined kernels (selected through the
-    STGEMM_FORCE_KERNEL tuning override)."""
+    """Every 256 x 256 kernel variant, each selected through the
+    STGEMM_FORCE_KERNEL tuning override (the automatic choice takes one of
+    them per operand type)."""
     monkeypatch.setenv("STGEMM_FORCE_KERNEL", family)
     M, N, K = shape
     A, B, C, _ = make(a_type, b_type, M, N, K, seed=zlib.crc32(repr((family, a_type, shape)).encode()))
@@ -190,27 +192,25 @@ def test_k_zero_gives_epilogue_of_c(orc, a_type):
     assert np.array_equal(D, C)
 
 
-def test_padded_leading_dimensions(orc):
+def test_padded_leading_dimensions(orc, monkeypatch):
     M, N, K = 300, 200, 256
     lda, ldb, ldc, ldd = K + 64, K + 32, N + 8, N + 24
     rng = np.random.default_rng(21)
     Ap = inputs.to_bf16(rng.standard_normal((M, lda)))
     Bp = inputs.to_bf16(rng.standard_normal((N, ldb)))
     Cp = rng.uniform(-1, 1, (M, ldc)).astype(np.float32)
-    for algo in ["tiled128", "tiled256", "generic", "tiled256dma5"]:
+    Dr, Y, S = orc.gemm(np.ascontiguousarray(Ap[:, :K]), np.ascontiguousarray(Bp[:, :K]),
+                        np.ascontiguousarray(Cp[:, :N]), None, M, N, K, "bf16", "bf16", "bf16")
+    for algo in ["tiled128", "tiled256", "generic", "tiled256dma5", "tiled256w8"]:
         say("padded", algo)
-        if algo.startswith("tiled256dma"):
-            import os
-            os.environ["STGEMM_FORCE_KERNEL"] = algo
-            algo = "tiled256"
-        D, name = gpu_gemm(Ap, Bp, Cp, None, M, N, K, "bf16", "bf16", "bf16", algo=algo,
+        monkeypatch.delenv("STGEMM_FORCE_KERNEL", raising=False)
+        if algo.startswith("tiled256") and algo != "tiled256":
+            monkeypatch.setenv("STGEMM_FORCE_KERNEL", algo)
+        D, name = gpu_gemm(Ap, Bp, Cp, None, M, N, K, "bf16", "bf16", "bf16",
+                           algo="tiled256" if algo.startswith("tiled256") else algo,
                            lda=lda, ldb=ldb, ldc=ldc, ldd=ldd)
         assert name.startswith(algo)
-        Dr, Y, S = orc.gemm(np.ascontiguousarray(Ap[:, :K]), np.ascontiguousarray(Bp[:, :K]),
-                            np.ascontiguousarray(Cp[:, :N]), None, M, N, K, "bf16", "bf16", "bf16")
         r = check(D, "bf16", Dr, Y, S, "bf16")
-        import os
-        os.environ.pop("STGEMM_FORCE_KERNEL", None)
         assert r.ok, r
 
 
