@@ -24,7 +24,39 @@
 // accumulators, the kernel arguments) into scratch memory.
 #define STG_AI __attribute__((always_inline))
 
+// Compiler-only memory barrier: emits nothing, but no load or store is moved
+// across it.  The kernels order the hardware with explicit s_waitcnt,
+// s_barrier and wave barriers; the builtins that emit those are not memory
+// operations to the compiler, which may otherwise move an LDS access across
+// them when it can prove, from one lane's point of view, that two addresses
+// differ (lanes exchange data through LDS exactly there).  A workgroup-scope
+// fence would do the same but also wait for the direct global -> LDS copies
+// that the pipelines keep in flight across barriers.
+#define STG_COMPILER_FENCE() asm volatile("" ::: "memory")
+
 namespace stg {
+
+// A point where this wave's lanes exchange data through LDS: earlier LDS
+// accesses of the wave are complete and no LDS access moves across it.
+__device__ STG_AI inline void wave_lds_sync()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+    STG_COMPILER_FENCE();
+    __builtin_amdgcn_wave_barrier();
+    STG_COMPILER_FENCE();
+}
+
+// Workgroup barrier for pipelines that manage their own waits: the caller has
+// already waited for what must be complete; this adds lgkmcnt(0) (this
+// wave's LDS reads and stores done) and keeps the compiler from moving LDS
+// accesses across the barrier.
+__device__ STG_AI inline void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+    STG_COMPILER_FENCE();
+    __builtin_amdgcn_s_barrier();
+    STG_COMPILER_FENCE();
+}
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
@@ -162,6 +194,7 @@ __device__ STG_AI inline void epilogue_store(const EpiArgs &e, int64_t row, int6
     if (e.C)
         t += ((const float *)e.C)[row * e.ldc + col];
     float y = e.bias ? __builtin_fmaf(e.alpha, t, e.bias[col]) : e.alpha * t;
+    asm("" : "+v"(y)); // keep y an fp32 value: no fused multiply-add-convert
     if (e.relu)
         y = (y > 0.0f) ? y : 0.0f;
     const int64_t o = row * e.ldd + col;
@@ -223,6 +256,57 @@ __device__ STG_AI inline void epilogue_grid(const EpiArgs &e, typename OP::acc_t
     }
 }
 
+// ---------------------------------------------------------------- tile helpers
+
+// Tile-local buffer resource: loads at byte offsets >= `bytes` return zero,
+// so rows past the edge of the matrix need no clamping or masking.
+__device__ STG_AI inline __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, int64_t bytes)
+{
+    const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+}
+
+__device__ STG_AI inline u4_t buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Number of the `total` memory instructions that follow MFMA slot q of
+// `slots` when they are spread evenly.
+constexpr int spread(int q, int total, int slots)
+{
+    return (q + 1) * total / slots - q * total / slots;
+}
+
+// Workgroup id -> (tile_m, tile_n): XCD-contiguous renumbering, then groups
+// of GM tile rows walked column by column.
+__device__ STG_AI inline void tile_coords(int id, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    constexpr int GM = 8;
+    const int total = tiles_m * tiles_n;
+    if ((total & 7) == 0)
+        id = (id & 7) * (total >> 3) + (id >> 3);
+    const int per_group = GM * tiles_n;
+    const int group = id / per_group;
+    const int first_m = group * GM;
+    const int gsize = min(tiles_m - first_m, GM);
+    const int in = id - group * per_group;
+    tm = first_m + in % gsize;
+    tn = in / gsize;
+}
+
+// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt left free).
+#define STG_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt((((n)&15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
+
+// 16-byte global -> LDS copy for a whole wave: lane l's 16 bytes land at
+// lds_wave + 16 l (lds_wave must be wave-uniform).
+__device__ STG_AI inline void dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_wave, int voff, int soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds_wave, 16, voff, soff, 0, 0);
+}
+
 // ---------------------------------------------------------------- LDS-staged epilogue
 
 // A 64-bit value that is equal in all active lanes, as a scalar.
@@ -243,7 +327,10 @@ __device__ STG_AI inline __amdgpu_buffer_rsrc_t epi_rsrc(const void *base, int64
 
 // alpha * t (+ bias), then relu, for four fp32 values; the bias form is one
 // fused multiply-add per element, the same operation the oracle's fp32
-// epilogue performs.
+// epilogue performs.  Each fp32 result passes through an empty asm:
+// otherwise the compiler may fuse the multiply-add with a following f16
+// conversion (v_fma_mixlo_f16), which rounds once to f16 instead of to fp32
+// and then to f16.
 __device__ STG_AI inline f4_t epi_affine(const EpiArgs &e, f4_t t, f4_t b)
 {
     f4_t y;
@@ -256,6 +343,9 @@ __device__ STG_AI inline f4_t epi_affine(const EpiArgs &e, f4_t t, f4_t b)
         for (int q = 0; q < 4; ++q)
             y[q] = e.alpha * t[q];
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        asm("" : "+v"(y[q]));
     if (e.relu) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -368,8 +458,7 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
                 const auto x = acc[i][j][r];
                 lds_wave[row * PITCH + j * 32 + (lane & 31)] = __builtin_bit_cast(uint32_t, x);
             }
-        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): the slab is in LDS
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync(); // the slab is in LDS
         if (fast) {
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
@@ -396,8 +485,7 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
                 }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F); // reads done before the next slab overwrites
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync(); // reads done before the next slab overwrites
     }
 }
 

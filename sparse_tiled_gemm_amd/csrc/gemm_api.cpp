@@ -159,6 +159,7 @@ const char *family_name(int f)
     case KF_SKINNY: return "skinny";
     case KF_SPARSE_GENERIC: return "sparse24_generic";
     case KF_SPARSE_TILED: return "sparse24_tiled";
+    case KF_SPARSE_DMA8: return "sparse24_dma8";
     case KF_TILED_DMA4: return "tiled256dma4";
     case KF_TILED_DMA5: return "tiled256dma5";
     case KF_TILED_256W8: return "tiled256w8";
@@ -292,12 +293,17 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     p->fallback = KF_GENERIC;
 
     if (d.sparse_a) {
-        const bool fast = d.b_layout == GEMM_COL_MAJOR && d.K % 64 == 0 && d.ldb % 8 == 0;
+        // 64-logical-K tiles; 32-bit buffer offsets cover 256 rows of values
+        // (K bytes each) and of B
+        const int64_t lim = (int64_t)1 << 30;
+        const bool fast = d.b_layout == GEMM_COL_MAJOR && d.K % 64 == 0 && d.ldb % 8 == 0 &&
+                          d.K * 256 < lim && d.ldb * 2 * 256 < lim;
         int fam = -1;
         switch (d.algo) {
-        case GEMM_ALGO_AUTO: fam = fast ? KF_SPARSE_TILED : KF_SPARSE_GENERIC; break;
+        // the 8-wave kernel with direct copies measured fastest (2:4 f16, 8192^3)
+        case GEMM_ALGO_AUTO: fam = fast ? KF_SPARSE_DMA8 : KF_SPARSE_GENERIC; break;
         case GEMM_ALGO_TILED:
-        case GEMM_ALGO_TILED_256: fam = fast ? KF_SPARSE_TILED : -1; break;
+        case GEMM_ALGO_TILED_256: fam = fast ? KF_SPARSE_DMA8 : -1; break;
         case GEMM_ALGO_GENERIC: fam = KF_SPARSE_GENERIC; break;
         default: fam = -1;
         }
@@ -305,10 +311,14 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
             delete p;
             return fail(GEMM_ERR_UNSUPPORTED, "requested algorithm cannot serve this sparse problem");
         }
+        if (const char *force = getenv("STGEMM_FORCE_KERNEL")) { // tuning override
+            for (int f : {KF_SPARSE_TILED, KF_SPARSE_DMA8, KF_SPARSE_GENERIC})
+                if (strcmp(force, family_name(f)) == 0 && (fast || f == KF_SPARSE_GENERIC))
+                    fam = f;
+        }
         p->family = fam;
         p->fallback = KF_SPARSE_GENERIC;
-        snprintf(p->name, sizeof p->name, "%s_f16",
-                 fam == KF_SPARSE_TILED ? "sparse24_tiled" : "sparse24_generic");
+        snprintf(p->name, sizeof p->name, "%s_f16", family_name(fam));
         *out = p;
         return ok();
     }
@@ -544,7 +554,7 @@ gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, con
     }
     a.e = make_epi(d, C, bias, D);
     int fam = plan->family;
-    if (fam == KF_SPARSE_TILED && (!aligned(values, 16) || !aligned(B, 16) || !aligned(meta, 16)))
+    if (fam != KF_SPARSE_GENERIC && (!aligned(values, 16) || !aligned(B, 16) || !aligned(meta, 16)))
         fam = plan->fallback;
     hipError_t e = launch_sparse(fam, a, (hipStream_t)stream);
     if (e != hipSuccess)

@@ -34,6 +34,7 @@ enum KernelFamily {
     KF_TILED_256W8T, // 256 x 256, 8 waves as 4 x 2, 64 x 128 per wave
     KF_PINGPONG4,    // 256 x 256, 8 waves in two out-of-phase groups, 4 LDS stages
     KF_PINGPONG5,    // same with 5 LDS stages
+    KF_SPARSE_DMA8,  // 2:4 A, 256 x 256, 8 waves, direct global -> LDS copies, 3 stages
     KF_COUNT
 };
 

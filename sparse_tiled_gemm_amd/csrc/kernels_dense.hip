@@ -94,19 +94,6 @@ __global__ __launch_bounds__(256) void k_generic(GemmArgs g)
 
 // ---------------------------------------------------------------- tiled
 
-// Tile-local buffer resource: loads at byte offsets >= `bytes` return zero,
-// so rows past the edge of the matrix need no clamping or masking.
-__device__ STG_AI inline __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, int64_t bytes)
-{
-    const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
-}
-
-__device__ STG_AI inline u4_t buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
-{
-    return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
 // 16-byte chunk slot inside a 64-byte LDS row: chunk c of row r sits at slot
 // c ^ swz64(r).  Chosen by measurement on gfx950 (LDS bank-conflict counter
 // over the fragment-read pattern of 32 consecutive rows): rotating the slot
@@ -115,32 +102,9 @@ __device__ STG_AI inline u4_t buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int
 // swz64(r + 32 i) == swz64(r).
 __device__ STG_AI inline int swz64(int r) { return (r >> 2) & 3; }
 
-// Number of the `total` memory instructions that follow MFMA slot q of
-// `slots` when they are spread evenly.
-constexpr int spread(int q, int total, int slots)
-{
-    return (q + 1) * total / slots - q * total / slots;
-}
-
-// Workgroup id -> (tile_m, tile_n): XCD-contiguous renumbering, then groups
-// of GM tile rows walked column by column.
-__device__ STG_AI inline void tile_coords(int id, int tiles_m, int tiles_n, int &tm, int &tn)
-{
-    constexpr int GM = 8;
-    const int total = tiles_m * tiles_n;
-    if ((total & 7) == 0)
-        id = (id & 7) * (total >> 3) + (id >> 3);
-    const int per_group = GM * tiles_n;
-    const int group = id / per_group;
-    const int first_m = group * GM;
-    const int gsize = min(tiles_m - first_m, GM);
-    const int in = id - group * per_group;
-    tm = first_m + in % gsize;
-    tn = in / gsize;
-}
-
-template <class OP, int BM, int BN, int GM = 2, int GN = 2>
-__global__ __launch_bounds__(64 * GM * GN, 1) void k_tiled(GemmArgs g, int tiles_m, int tiles_n)
+template <class OP, int BM, int BN, int GM = 2, int GN = 2, int WG_PER_CU = 1>
+__global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, int tiles_m,
+                                                                   int tiles_n)
 {
     constexpr int NT = 64 * GM * GN;        // GM x GN waves
     constexpr int BKB = 64;                 // K bytes per tile
@@ -332,18 +296,6 @@ __global__ __launch_bounds__(64 * GM * GN, 1) void k_tiled(GemmArgs g, int tiles
 
 // ---------------------------------------------------------------- tiled, LDS DMA
 
-// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt left free).
-#define STG_WAIT_VMCNT(n) \
-    __builtin_amdgcn_s_waitcnt((((n)&15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
-
-// 16-byte global -> LDS copy for a whole wave: lane l's 16 bytes land at
-// lds_wave + 16 l (lds_wave must be wave-uniform).
-__device__ STG_AI inline void dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_wave, int voff, int soff)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)lds_wave, 16, voff, soff, 0, 0);
-}
-
 // Same tile structure as k_tiled, but global -> LDS copies are direct
 // (buffer_load ... lds): no staging registers and no LDS store instructions,
 // so NSTAGE LDS stages can be in flight.  Tile t+NSTAGE-1 is requested while
@@ -452,7 +404,7 @@ __global__ __launch_bounds__(256, 1) void k_tiled_dma(GemmArgs g, int tiles_m, i
     for (int p = 0; p < NSTAGE - 1; ++p)
         dma_tile(p, p);
     STG_WAIT_VMCNT((NSTAGE - 3) * NI);
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     lread(I0{}, 0, 0);
 
     // fragment reads spread over each step's MFMAs, DMA requests spread over
@@ -497,8 +449,7 @@ __global__ __launch_bounds__(256, 1) void k_tiled_dma(GemmArgs g, int tiles_m, i
         __builtin_amdgcn_sched_barrier(0);
         // tile t+2 complete (tiles t+3 .. t+NSTAGE-1 may still be in flight)
         STG_WAIT_VMCNT((NSTAGE - 3) * NI);
-        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's LDS reads done
-        __builtin_amdgcn_s_barrier();
+        lds_barrier();
         st = st1;
     };
 
@@ -626,7 +577,7 @@ __global__ __launch_bounds__(512, 1) void k_pingpong(GemmArgs g, int tiles_m, in
     if (grp == 0)
         copy_tile(NSTAGE - 1, NSTAGE - 1);
     STG_WAIT_VMCNT(0);
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     if (grp == 0)
         lread(lds);
 
@@ -643,8 +594,7 @@ __global__ __launch_bounds__(512, 1) void k_pingpong(GemmArgs g, int tiles_m, in
             copy_tile(stage_of(t + NSTAGE - 1), t + NSTAGE - 1);
             STG_WAIT_VMCNT((NSTAGE - 2) * NI);
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_s_barrier();
+        lds_barrier();
         // ---- phase 2: group 1 multiplies tile t; group 0 reads tile t+1 and
         // requests the A half of tile t + NSTAGE
         if (grp == 1) {
@@ -653,8 +603,7 @@ __global__ __launch_bounds__(512, 1) void k_pingpong(GemmArgs g, int tiles_m, in
             lread(lds + stage_of(t + 1) * STAGE);
             copy_tile(stage_of(t + NSTAGE), t + NSTAGE);
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_s_barrier();
+        lds_barrier();
     }
     STG_WAIT_VMCNT(0);
     __syncthreads();
@@ -789,11 +738,11 @@ static hipError_t launch_generic_t(const GemmArgs &g, hipStream_t s)
     return hipGetLastError();
 }
 
-template <class OP, int BM, int BN, int GM = 2, int GN = 2>
+template <class OP, int BM, int BN, int GM = 2, int GN = 2, int WPC = 1>
 static hipError_t launch_tiled_t(const GemmArgs &g, hipStream_t s)
 {
     const int tiles_m = (int)((g.e.M + BM - 1) / BM), tiles_n = (int)((g.e.N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_tiled<OP, BM, BN, GM, GN>), dim3((unsigned)(tiles_m * tiles_n)),
+    hipLaunchKernelGGL((k_tiled<OP, BM, BN, GM, GN, WPC>), dim3((unsigned)(tiles_m * tiles_n)),
                        dim3(64 * GM * GN), 0, s, g, tiles_m, tiles_n);
     return hipGetLastError();
 }
@@ -814,17 +763,17 @@ static dense_launch_fn generic_table(int op)
     }
 }
 
-template <int BM, int BN, int GM = 2, int GN = 2>
+template <int BM, int BN, int GM = 2, int GN = 2, int WPC = 1>
 static dense_launch_fn tiled_table_t(int op)
 {
     switch (op) {
-    case OPK_F16: return launch_tiled_t<OpF16, BM, BN, GM, GN>;
-    case OPK_BF16: return launch_tiled_t<OpBF16, BM, BN, GM, GN>;
-    case OPK_F8_E4E4: return launch_tiled_t<OpF8<0, 0>, BM, BN, GM, GN>;
-    case OPK_F8_E4E5: return launch_tiled_t<OpF8<0, 1>, BM, BN, GM, GN>;
-    case OPK_F8_E5E4: return launch_tiled_t<OpF8<1, 0>, BM, BN, GM, GN>;
-    case OPK_F8_E5E5: return launch_tiled_t<OpF8<1, 1>, BM, BN, GM, GN>;
-    case OPK_S8: return launch_tiled_t<OpS8, BM, BN, GM, GN>;
+    case OPK_F16: return launch_tiled_t<OpF16, BM, BN, GM, GN, WPC>;
+    case OPK_BF16: return launch_tiled_t<OpBF16, BM, BN, GM, GN, WPC>;
+    case OPK_F8_E4E4: return launch_tiled_t<OpF8<0, 0>, BM, BN, GM, GN, WPC>;
+    case OPK_F8_E4E5: return launch_tiled_t<OpF8<0, 1>, BM, BN, GM, GN, WPC>;
+    case OPK_F8_E5E4: return launch_tiled_t<OpF8<1, 0>, BM, BN, GM, GN, WPC>;
+    case OPK_F8_E5E5: return launch_tiled_t<OpF8<1, 1>, BM, BN, GM, GN, WPC>;
+    case OPK_S8: return launch_tiled_t<OpS8, BM, BN, GM, GN, WPC>;
     default: return nullptr;
     }
 }

@@ -129,21 +129,6 @@ __global__ __launch_bounds__(256) void k_sparse_generic(SparseArgs a)
 __device__ STG_AI inline int swz128(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ STG_AI inline int swz64(int r) { return (r >> 2) & 3; }
 
-__device__ STG_AI inline void tile_coords_sp(int id, int tiles_m, int tiles_n, int &tm, int &tn)
-{
-    constexpr int GM = 8;
-    const int total = tiles_m * tiles_n;
-    if ((total & 7) == 0)
-        id = (id & 7) * (total >> 3) + (id >> 3);
-    const int per_group = GM * tiles_n;
-    const int group = id / per_group;
-    const int first_m = group * GM;
-    const int gsize = min(tiles_m - first_m, GM);
-    const int in = id - group * per_group;
-    tm = first_m + in % gsize;
-    tn = in / gsize;
-}
-
 // v_smfmac_f32_32x32x32_f16 covers 32 logical K positions k0..k0+31.  Lane l
 // (h = l / 32) supplies, for row l % 32 of A, the 8 kept values of logical K
 // 16h .. 16h+15 (4 groups, in group order) and their position code in the
@@ -177,7 +162,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_tiled(SparseArgs a, int tiles
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int tm, tn;
-    tile_coords_sp(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int64_t m_blk = (int64_t)tm * BM, n_blk = (int64_t)tn * BN;
     const int64_t K = a.K, KT = K / BK;
     const int64_t vpitch = K, mpitch = K / 8; // bytes per row of values / meta
@@ -304,11 +289,245 @@ __global__ __launch_bounds__(256, 1) void k_sparse_tiled(SparseArgs a, int tiles
                                      (uint32_t *)lds + wave * 32 * (WN + 4));
 }
 
+// ---------------------------------------------------------------- 8 waves, LDS DMA
+
+// 256 x 256 workgroup tile, 8 waves (two per SIMD) as 2 x 4, each a 128 x 64
+// block of 32x32 fragments.  A K tile is 64 logical K: compressed values
+// (64 B per row), metadata (8 B per row) and B (128 B per row), 50 KB in
+// all; NSTAGE such LDS stages are filled by direct global -> LDS copies of
+// values and B (tile t+NSTAGE-1 is requested while tile t is multiplied, and
+// at the barrier that ends tile t each wave has waited for its copies of
+// tile t+1).  The metadata goes through a register instead (one word per
+// thread, loaded a tile ahead of its LDS store): with 4-byte direct copies
+// pending the compiler waits for all of them before every LDS read.
+// An SMFMAC of the same cost as a dense MFMA reads twice the B bytes per
+// lane, which makes LDS reads the busiest resource of this kernel; gfx950
+// delivers about twice the LDS read rate with two waves per SIMD as with one
+// (measured), and the second wave also covers the first's fragment-read
+// latency at the start of each tile.  Within a tile the fragments of the
+// second K step are read while the first step's SMFMACs run.
+template <int NSTAGE>
+__global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_m, int tiles_n)
+{
+    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int AVB = BK, AMB = BK / 8, BB = BK * 2; // bytes per row per tile
+    constexpr int WM = 128, WN = 64, FM = WM / 32, FN = WN / 32, GN = BN / WN;
+    constexpr int OFF_M = BM * AVB, OFF_B = OFF_M + BM * AMB;
+    constexpr int STAGE = OFF_B + BN * BB;
+    constexpr int V_I = BM * AVB / 1024 / 8; // 16-byte copies per wave per tile: values
+    constexpr int B_I = BN * BB / 1024 / 8;  // B
+    constexpr int NI = V_I + B_I;
+    constexpr int NL = NI + 1; // vector memory requests per tile: copies + metadata
+    static_assert(V_I * 8 * 1024 == BM * AVB && B_I * 8 * 1024 == BN * BB && BM * AMB == 512 * 4,
+                  "copies divide evenly over the waves; one metadata word per thread");
+    static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024, "LDS budget");
+    static_assert(8 * 32 * (WN + 4) * 4 <= NSTAGE * STAGE, "epilogue staging fits in LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m_blk = (int64_t)tm * BM, n_blk = (int64_t)tn * BN;
+    const int64_t K = a.K;
+    const int KT = (int)(K / BK);
+    const int64_t vpitch = K, mpitch = K / 8, bpitch = a.b_cs * 2; // bytes per row
+    // bounded by the last byte of the last row: copies past it read zero
+    // (zero values with position code 0 contribute nothing)
+    const __amdgpu_buffer_rsrc_t rv =
+        tile_rsrc((const uint8_t *)a.values + m_blk * vpitch, (a.e.M - m_blk - 1) * vpitch + K);
+    const __amdgpu_buffer_rsrc_t rm =
+        tile_rsrc((const uint8_t *)a.meta + m_blk * mpitch, (a.e.M - m_blk - 1) * mpitch + mpitch);
+    const __amdgpu_buffer_rsrc_t rb =
+        tile_rsrc((const uint8_t *)a.B + n_blk * bpitch, (a.e.N - n_blk - 1) * bpitch + 2 * K);
+
+    // this lane's source offsets: a 16-byte copy instruction fills 1 KB of
+    // LDS (16 value rows or 8 B rows), lane l writing slot l of it, so the
+    // lane fetches the chunk that the row's swizzle maps to that slot
+    int voff[NI];
+#pragma unroll
+    for (int i = 0; i < V_I; ++i) {
+        const int row = (wave * V_I + i) * 16 + (lane >> 2);
+        voff[i] = row * (int)vpitch + (((lane & 3) ^ swz64(row)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < B_I; ++j) {
+        const int row = (wave * B_I + j) * 8 + (lane >> 3);
+        voff[V_I + j] = row * (int)bpitch + (((lane & 7) ^ swz128(row)) << 4);
+    }
+    // metadata: thread tid moves word tid % 2 of row tid / 2
+    const int moff = (tid >> 1) * (int)mpitch + (tid & 1) * 4;
+    // K-tile rotation as in k_sparse_tiled (each tile's summation order is
+    // fixed); tiles requested past the end of the loop are never read
+    const int rot = KT > 0 ? (int)(((blockIdx.x >> 3) * 2) % (unsigned)KT) : 0;
+    auto ktile = [&](int t) STG_AI {
+        const int kt = t + rot;
+        return kt >= KT ? kt - KT : kt;
+    };
+    auto dma_tile = [&](int stage, int t) STG_AI {
+        const int kt = ktile(t);
+        uint8_t *base = lds + stage * STAGE;
+#pragma unroll
+        for (int i = 0; i < V_I; ++i)
+            dma16(rv, base + (wave * V_I + i) * 1024, voff[i], kt * AVB);
+#pragma unroll
+        for (int j = 0; j < B_I; ++j)
+            dma16(rb, base + OFF_B + (wave * B_I + j) * 1024, voff[V_I + j], kt * BB);
+    };
+    auto load_meta = [&](int t) STG_AI {
+        return __builtin_amdgcn_raw_buffer_load_b32(rm, moff, ktile(t) * AMB, 0);
+    };
+    // The metadata store into LDS is an opaque instruction: the compiler
+    // orders every LDS store after all pending direct copies into LDS (it
+    // cannot tell that this one never overlaps them), which would wait for
+    // the copies of later tiles.  It still waits for `w`'s load, and the
+    // lgkmcnt(0) before each barrier completes the store.
+    auto store_meta = [&](int stage, uint32_t w) STG_AI {
+        const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)(
+            lds + stage * STAGE + OFF_M + tid * 4);
+        asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(w) : "memory");
+    };
+
+    const int wm = wave / GN, wn = wave % GN;
+    const int arow = wm * WM + (lane & 31), brow = wn * WN + (lane & 31);
+    const int half = lane >> 5;
+    const int sa = swz64(arow); // swz64 is 32-row periodic; swz128 is not
+    int sb[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+        sb[j] = swz128(brow + 32 * j);
+
+    uint32_t af[2][FM][4], bf[2][FN][8];
+    uint2 mw[FM]; // metadata words of both K steps of a fragment row
+    // fragment reads of K step S (step 0 also reads both steps' metadata)
+    auto lread = [&](auto set, const uint8_t *st) STG_AI {
+        constexpr int S = decltype(set)::value;
+        const int ca = 2 * S + half; // value chunk: byte S*32 + half*16
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int r = arow + 32 * i;
+            *(u4_t *)af[S][i] = *(const u4_t *)(st + r * AVB + ((ca ^ sa) << 4));
+            if constexpr (S == 0) { // two 4-byte reads: with one 8-byte read the
+                                    // compiler waited for every pending copy
+                mw[i].x = *(const uint32_t *)(st + OFF_M + r * AMB);
+                mw[i].y = *(const uint32_t *)(st + OFF_M + r * AMB + 4);
+            }
+        }
+        const int cb = 4 * S + half; // B chunks 4S + half and 4S + half + 2
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int r = brow + 32 * j;
+            *(u4_t *)&bf[S][j][0] = *(const u4_t *)(st + OFF_B + r * BB + ((cb ^ sb[j]) << 4));
+            *(u4_t *)&bf[S][j][4] =
+                *(const u4_t *)(st + OFF_B + r * BB + (((cb + 2) ^ sb[j]) << 4));
+        }
+    };
+    // this lane's 16-bit half of step S's metadata word
+    auto index = [&](int i, auto set) STG_AI {
+        constexpr int S = decltype(set)::value;
+        const uint32_t w = S == 0 ? mw[i].x : mw[i].y;
+        return (int)((w >> (16 * half)) & 0xFFFFu);
+    };
+
+    f16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = f16_t{};
+    auto mma = [&](auto set) STG_AI {
+        constexpr int S = decltype(set)::value;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = smfmac32(af[S][i], bf[S][j], index(i, set), acc[i][j]);
+    };
+
+    // one tile: the first step's fragment reads, then the SMFMACs with the
+    // second step's reads spread over the first step's SMFMACs and the
+    // copies of a future tile spread over all of them
+    constexpr int NM = FM * FN;
+    constexpr int NR0 = 2 * FM + 2 * FN, NR1 = FM + 2 * FN; // DS reads of steps 0 and 1
+    auto schedule = [&]() STG_AI {
+        __builtin_amdgcn_sched_group_barrier(0x100, NR0, 0); // step 0 DS reads
+        [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
+            (
+                [&]() STG_AI {
+                    constexpr int nr = Q < NM ? spread(Q, NR1, NM) : 0;
+                    constexpr int nl = spread(Q, NI, 2 * NM);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                    if constexpr (nr > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x100, nr, 0); // DS read
+                    if constexpr (nl > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x020, nl, 0); // VMEM read
+                }(),
+                ...);
+        }(std::make_integer_sequence<int, 2 * NM>{});
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // prologue: tiles 0 .. NSTAGE-2 requested (their metadata stored), the
+    // metadata of tile NSTAGE-1 in flight; wait for tile 0
+    // (the last metadata load goes out before the last copies, as in the
+    // loop, so that its first store waits for it alone)
+    uint32_t mw_next = 0;
+#pragma unroll
+    for (int p = 0; p < NSTAGE - 1; ++p) {
+        const uint32_t w = load_meta(p);
+        if (p == NSTAGE - 2)
+            mw_next = load_meta(NSTAGE - 1);
+        dma_tile(p, p);
+        store_meta(p, w);
+    }
+    STG_WAIT_VMCNT((NSTAGE - 2) * NL + 1);
+    lds_barrier();
+
+    int st = 0; // LDS stage of tile t
+    for (int t = 0; t < KT; ++t) {
+        const uint8_t *cur = lds + st * STAGE;
+        const int stn = st == 0 ? NSTAGE - 1 : st - 1; // stage of tile t + NSTAGE - 1
+        // tile t+NSTAGE-1: metadata (loaded during the previous tile) into
+        // LDS, its copies requested; the next tile's metadata loaded
+        store_meta(stn, mw_next);
+        mw_next = load_meta(t + NSTAGE);
+        // the metadata load goes out ahead of the copies, so that storing it
+        // at the next tile waits only for it and not for them
+        __builtin_amdgcn_sched_barrier(0);
+        dma_tile(stn, t + NSTAGE - 1);
+        lread(I0{}, cur);
+        lread(I1{}, cur);
+        mma(I0{});
+        mma(I1{});
+        schedule();
+        __builtin_amdgcn_sched_barrier(0);
+        // tile t+1 complete (the requests of later tiles may be in flight);
+        // this wave's LDS reads and metadata store done
+        STG_WAIT_VMCNT((NSTAGE - 2) * NL);
+        lds_barrier();
+        st = st == NSTAGE - 1 ? 0 : st + 1;
+    }
+    STG_WAIT_VMCNT(0); // drain the requests past the last tile before the LDS is reused
+    __syncthreads();
+
+    epilogue_grid_lds<OpF16, FM, FN>(a.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
+                                     (uint32_t *)lds + wave * 32 * (WN + 4));
+}
+
 hipError_t launch_sparse(int family, const SparseArgs &a, hipStream_t s)
 {
     if (family == KF_SPARSE_GENERIC) {
         dim3 grid((unsigned)((a.e.N + 63) / 64), (unsigned)((a.e.M + 63) / 64));
         hipLaunchKernelGGL(k_sparse_generic, grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    if (family == KF_SPARSE_DMA8) {
+        constexpr int BM = 256, BN = 256;
+        const int tiles_m = (int)((a.e.M + BM - 1) / BM), tiles_n = (int)((a.e.N + BN - 1) / BN);
+        hipLaunchKernelGGL((k_sparse_dma8<3>), dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0,
+                           s, a, tiles_m, tiles_n);
         return hipGetLastError();
     }
     if (family == KF_SPARSE_TILED) {

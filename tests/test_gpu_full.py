@@ -159,7 +159,7 @@ def test_full_sparse24_8192(orc):
     assert np.array_equal(meta.cpu().numpy().view(np.uint32).reshape(rm.shape), rm)
     say("  compressor bytes identical to the oracle's")
     D, name = _run(p, sparse_dev=(vals, meta))
-    assert name.startswith("sparse24_tiled")
+    assert name.startswith("sparse24_dma8")
     pd = dict(p)
     pd["A"] = p["A_logical"]
     _check_samples(orc, pd, D, a_logical=p["A_logical"], seed=5)

@@ -62,7 +62,7 @@ def test_sparse_parity(orc, algo, shape):
     D, name = gpu_sparse_gemm(vals, meta, p["B"], p["C"], M, N, K, algo=algo)
     say("  ", name)
     if algo != "auto":
-        assert name.startswith("sparse24_" + algo)
+        assert name.startswith({"tiled": "sparse24_dma8", "generic": "sparse24_generic"}[algo]), name
     Dr, Y, S = orc.gemm(p["A_logical"], p["B"], p["C"], None, M, N, K, "f16", "f16", "f32")
     r = check(D, "f32", Dr, Y, S, "f16")
     say("  ", r)
@@ -94,3 +94,42 @@ def test_sparse_row_major_b(orc):
     Dr, Y, S = orc.gemm(p["A_logical"], Brow, p["C"], None, M, N, K, "f16", "f16", "f32",
                         b_col_major=False)
     assert check(D, "f32", Dr, Y, S, "f16").ok
+
+
+@pytest.mark.parametrize("family", ["sparse24_tiled", "sparse24_dma8"])
+@pytest.mark.parametrize("shape", [(600, 520, 256), (256, 256, 64), (300, 700, 448),
+                                   (512, 264, 1024), (40, 1000, 192)])
+def test_sparse_parity_variants(orc, monkeypatch, family, shape):
+    """Each 256 x 256 SMFMAC kernel (selected through the STGEMM_FORCE_KERNEL
+    tuning override): ragged M and N, one K tile, odd and even K tile counts."""
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", family)
+    M, N, K = shape
+    p = inputs.sparse24_f16(M=M, N=N, K=K)
+    say("sparse", family, shape)
+    vals, meta, _, _ = gpu_compress(p["A_logical"])
+    D, name = gpu_sparse_gemm(vals, meta, p["B"], p["C"], M, N, K, algo="auto")
+    assert name.startswith(family), name
+    Dr, Y, S = orc.gemm(p["A_logical"], p["B"], p["C"], None, M, N, K, "f16", "f16", "f32")
+    r = check(D, "f32", Dr, Y, S, "f16")
+    say("  ", r)
+    assert r.ok, r
+
+
+@pytest.mark.parametrize("family", ["sparse24_tiled", "sparse24_dma8"])
+@pytest.mark.parametrize("d_type", ["bf16", "f16"])
+def test_sparse_epilogue_bit_exact(orc, monkeypatch, family, d_type):
+    """The fused epilogue of the SMFMAC kernels equals the oracle's fp32
+    epilogue applied to the same kernel's fp32 output, bit for bit."""
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", family)
+    M, N, K = 384, 320, 256
+    p = inputs.sparse24_f16(M=M, N=N, K=K)
+    bias = np.random.default_rng(4).standard_normal(N).astype(np.float32)
+    vals, meta, _, _ = gpu_compress(p["A_logical"])
+    T, n1 = gpu_sparse_gemm(vals, meta, p["B"], p["C"], M, N, K, "f32", algo="auto")
+    D, n2 = gpu_sparse_gemm(vals, meta, p["B"], p["C"], M, N, K, d_type, algo="auto", bias=bias,
+                            alpha=0.3, relu=True)
+    assert n1.startswith(family) and n2.startswith(family), (n1, n2)
+    ref = orc.epilogue_f32(T, 0.3, bias, True, d_type)
+    mism = int((D != ref).sum())
+    say("sparse epilogue", family, d_type, "mismatches", mism)
+    assert mism == 0
