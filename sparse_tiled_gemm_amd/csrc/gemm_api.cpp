@@ -298,12 +298,15 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
         const int64_t lim = (int64_t)1 << 30;
         const bool fast = d.b_layout == GEMM_COL_MAJOR && d.K % 64 == 0 && d.ldb % 8 == 0 &&
                           d.K * 256 < lim && d.ldb * 2 * 256 < lim;
+        // the 8-wave kernel with direct copies measured fastest (2:4 f16,
+        // 8192^3); it takes K in whole groups of four 64-wide K tiles
+        const bool dma8 = fast && d.K % 256 == 0;
+        const int tiled_fam = dma8 ? KF_SPARSE_DMA8 : KF_SPARSE_TILED;
         int fam = -1;
         switch (d.algo) {
-        // the 8-wave kernel with direct copies measured fastest (2:4 f16, 8192^3)
-        case GEMM_ALGO_AUTO: fam = fast ? KF_SPARSE_DMA8 : KF_SPARSE_GENERIC; break;
+        case GEMM_ALGO_AUTO: fam = fast ? tiled_fam : KF_SPARSE_GENERIC; break;
         case GEMM_ALGO_TILED:
-        case GEMM_ALGO_TILED_256: fam = fast ? KF_SPARSE_DMA8 : -1; break;
+        case GEMM_ALGO_TILED_256: fam = fast ? tiled_fam : -1; break;
         case GEMM_ALGO_GENERIC: fam = KF_SPARSE_GENERIC; break;
         default: fam = -1;
         }
@@ -313,7 +316,8 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
         }
         if (const char *force = getenv("STGEMM_FORCE_KERNEL")) { // tuning override
             for (int f : {KF_SPARSE_TILED, KF_SPARSE_DMA8, KF_SPARSE_GENERIC})
-                if (strcmp(force, family_name(f)) == 0 && (fast || f == KF_SPARSE_GENERIC))
+                if (strcmp(force, family_name(f)) == 0 &&
+                    (f == KF_SPARSE_GENERIC || (fast && (f != KF_SPARSE_DMA8 || dma8))))
                     fam = f;
         }
         p->family = fam;

@@ -293,36 +293,44 @@ __global__ __launch_bounds__(256, 1) void k_sparse_tiled(SparseArgs a, int tiles
 
 // 256 x 256 workgroup tile, 8 waves (two per SIMD) as 2 x 4, each a 128 x 64
 // block of 32x32 fragments.  A K tile is 64 logical K: compressed values
-// (64 B per row), metadata (8 B per row) and B (128 B per row), 50 KB in
-// all; NSTAGE such LDS stages are filled by direct global -> LDS copies of
-// values and B (tile t+NSTAGE-1 is requested while tile t is multiplied, and
-// at the barrier that ends tile t each wave has waited for its copies of
-// tile t+1).  The metadata goes through a register instead (one word per
-// thread, loaded a tile ahead of its LDS store): with 4-byte direct copies
-// pending the compiler waits for all of them before every LDS read.
+// (64 B per row) and B (128 B per row), 48 KB; three such LDS stages are
+// filled by direct global -> LDS copies (tile t+2 is requested while tile t
+// is multiplied, and at the barrier that ends tile t each wave has waited
+// for its copies of tile t+1).  The metadata (8 B per row per tile) has a
+// ring of its own: two slots of four tiles (32 B per row, 8 KB a slot), the
+// next slot requested at the first tile of each group of four.  Copying the
+// metadata four tiles at a time cuts its L2 requests fourfold (each row's
+// bytes are a separate request however few they are); 3 x 48 KB + 16 KB is
+// the whole 160 KB of LDS.  Within a slot, each wave's 1 KB copy holds rows
+// 32 w .. 32 w + 31 as two 512-byte chunks (tiles 0-1, tiles 2-3) of 16
+// bytes per row.
 // An SMFMAC of the same cost as a dense MFMA reads twice the B bytes per
-// lane, which makes LDS reads the busiest resource of this kernel; gfx950
-// delivers about twice the LDS read rate with two waves per SIMD as with one
-// (measured), and the second wave also covers the first's fragment-read
-// latency at the start of each tile.  Within a tile the fragments of the
-// second K step are read while the first step's SMFMACs run.
-template <int NSTAGE>
+// lane; gfx950 delivers about twice the LDS read rate with two waves per
+// SIMD as with one (measured), and the second wave also covers the first's
+// fragment-read latency at the start of each tile.  Within a tile the
+// fragments of the second K step are read while the first step's SMFMACs
+// run.  Requires K % 256 == 0 (whole groups of four tiles, 32-byte aligned
+// metadata rows).
 __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_m, int tiles_n)
 {
+    constexpr int NSTAGE = 3, MG = 4; // LDS stages; metadata tiles per ring slot
     constexpr int BM = 256, BN = 256, BK = 64;
     constexpr int AVB = BK, AMB = BK / 8, BB = BK * 2; // bytes per row per tile
     constexpr int WM = 128, WN = 64, FM = WM / 32, FN = WN / 32, GN = BN / WN;
-    constexpr int OFF_M = BM * AVB, OFF_B = OFF_M + BM * AMB;
+    constexpr int OFF_B = BM * AVB;
     constexpr int STAGE = OFF_B + BN * BB;
-    constexpr int V_I = BM * AVB / 1024 / 8; // 16-byte copies per wave per tile: values
-    constexpr int B_I = BN * BB / 1024 / 8;  // B
+    constexpr int MROW = MG * AMB;             // metadata bytes per row per slot
+    constexpr int OFF_META = NSTAGE * STAGE;   // two slots of BM * MROW bytes
+    constexpr int LDS_BYTES = OFF_META + 2 * BM * MROW;
+    constexpr int V_I = BM * AVB / 1024 / 8;   // 16-byte copies per wave per tile: values
+    constexpr int B_I = BN * BB / 1024 / 8;    // B
     constexpr int NI = V_I + B_I;
-    constexpr int NL = NI + 1; // vector memory requests per tile: copies + metadata
-    static_assert(V_I * 8 * 1024 == BM * AVB && B_I * 8 * 1024 == BN * BB && BM * AMB == 512 * 4,
-                  "copies divide evenly over the waves; one metadata word per thread");
-    static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024, "LDS budget");
-    static_assert(8 * 32 * (WN + 4) * 4 <= NSTAGE * STAGE, "epilogue staging fits in LDS");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * STAGE];
+    static_assert(V_I * 8 * 1024 == BM * AVB && B_I * 8 * 1024 == BN * BB &&
+                      BM * MROW == 8 * 1024,
+                  "copies divide evenly over the waves; one metadata copy per wave per slot");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(8 * 32 * (WN + 4) * 4 <= LDS_BYTES, "epilogue staging fits in LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -342,8 +350,9 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
         tile_rsrc((const uint8_t *)a.B + n_blk * bpitch, (a.e.N - n_blk - 1) * bpitch + 2 * K);
 
     // this lane's source offsets: a 16-byte copy instruction fills 1 KB of
-    // LDS (16 value rows or 8 B rows), lane l writing slot l of it, so the
-    // lane fetches the chunk that the row's swizzle maps to that slot
+    // LDS (16 value rows, 8 B rows or 32 metadata rows), lane l writing slot
+    // l of it, so the lane fetches the chunk that the row's swizzle maps to
+    // that slot (metadata rows are not swizzled)
     int voff[NI];
 #pragma unroll
     for (int i = 0; i < V_I; ++i) {
@@ -355,17 +364,17 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
         const int row = (wave * B_I + j) * 8 + (lane >> 3);
         voff[V_I + j] = row * (int)bpitch + (((lane & 7) ^ swz128(row)) << 4);
     }
-    // metadata: thread tid moves word tid % 2 of row tid / 2
-    const int moff = (tid >> 1) * (int)mpitch + (tid & 1) * 4;
-    // K-tile rotation as in k_sparse_tiled (each tile's summation order is
-    // fixed); tiles requested past the end of the loop are never read
-    const int rot = KT > 0 ? (int)(((blockIdx.x >> 3) * 2) % (unsigned)KT) : 0;
-    auto ktile = [&](int t) STG_AI {
-        const int kt = t + rot;
-        return kt >= KT ? kt - KT : kt;
-    };
-    auto dma_tile = [&](int stage, int t) STG_AI {
-        const int kt = ktile(t);
+    // metadata: the wave's copy covers rows 32 w .. 32 w + 31; lane l moves
+    // 16-byte chunk l / 32 (two tiles) of row 32 w + l % 32, so in LDS each
+    // chunk's 32 rows sit 16 bytes apart (the fragment reads of 32
+    // consecutive rows then meet each LDS bank at most twice)
+    const int moff = (wave * 32 + (lane & 31)) * (int)mpitch + (lane >> 5) * 16;
+    // Every workgroup walks K from the start: workgroups of one XCD that share
+    // A or B rows then read the same K slices at about the same time and hit
+    // in L2.  (Starting each workgroup at a different K group measured up to
+    // 25 % slower here.)  Tiles requested past the end of the loop read
+    // bytes that are never used (or zeros past the end of a resource).
+    auto dma_tile = [&](int stage, int kt) STG_AI {
         uint8_t *base = lds + stage * STAGE;
 #pragma unroll
         for (int i = 0; i < V_I; ++i)
@@ -374,18 +383,9 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
         for (int j = 0; j < B_I; ++j)
             dma16(rb, base + OFF_B + (wave * B_I + j) * 1024, voff[V_I + j], kt * BB);
     };
-    auto load_meta = [&](int t) STG_AI {
-        return __builtin_amdgcn_raw_buffer_load_b32(rm, moff, ktile(t) * AMB, 0);
-    };
-    // The metadata store into LDS is an opaque instruction: the compiler
-    // orders every LDS store after all pending direct copies into LDS (it
-    // cannot tell that this one never overlaps them), which would wait for
-    // the copies of later tiles.  It still waits for `w`'s load, and the
-    // lgkmcnt(0) before each barrier completes the store.
-    auto store_meta = [&](int stage, uint32_t w) STG_AI {
-        const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)(
-            lds + stage * STAGE + OFF_M + tid * 4);
-        asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(w) : "memory");
+    // metadata of tiles t .. t+3 (t a multiple of 4) into ring slot (t / 4) % 2
+    auto dma_meta = [&](int t) STG_AI {
+        dma16(rm, lds + OFF_META + ((t / MG) & 1) * (BM * MROW) + wave * 1024, moff, t * AMB);
     };
 
     const int wm = wave / GN, wn = wave % GN;
@@ -399,18 +399,26 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
 
     uint32_t af[2][FM][4], bf[2][FN][8];
     uint2 mw[FM]; // metadata words of both K steps of a fragment row
-    // fragment reads of K step S (step 0 also reads both steps' metadata)
-    auto lread = [&](auto set, const uint8_t *st) STG_AI {
+    // fragment reads of K step S of tile t from stage `st` (step 0 also
+    // reads both steps' metadata)
+    auto lread = [&](auto set, const uint8_t *st, int t) STG_AI {
         constexpr int S = decltype(set)::value;
+        // row r, tile t of the group: block r / 32, chunk (t % 4) / 2, row
+        // r % 32 of the chunk, half t % 2 of the row's 16 bytes
+        const uint8_t *meta = lds + OFF_META + ((t / MG) & 1) * (BM * MROW) +
+                              ((t % MG) >> 1) * 512 + (t & 1) * AMB;
         const int ca = 2 * S + half; // value chunk: byte S*32 + half*16
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int r = arow + 32 * i;
             *(u4_t *)af[S][i] = *(const u4_t *)(st + r * AVB + ((ca ^ sa) << 4));
-            if constexpr (S == 0) { // two 4-byte reads: with one 8-byte read the
-                                    // compiler waited for every pending copy
-                mw[i].x = *(const uint32_t *)(st + OFF_M + r * AMB);
-                mw[i].y = *(const uint32_t *)(st + OFF_M + r * AMB + 4);
+            if constexpr (S == 0) {
+                // two 4-byte reads, which the compiler merges into one: with
+                // an 8-byte read written as such it first waits for every
+                // pending direct copy into LDS
+                const int mo = (r >> 5) * 1024 + (r & 31) * 16;
+                mw[i].x = *(const uint32_t *)(meta + mo);
+                mw[i].y = *(const uint32_t *)(meta + mo + 4);
             }
         }
         const int cb = 4 * S + half; // B chunks 4S + half and 4S + half + 2
@@ -422,12 +430,6 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
                 *(const u4_t *)(st + OFF_B + r * BB + (((cb + 2) ^ sb[j]) << 4));
         }
     };
-    // this lane's 16-bit half of step S's metadata word
-    auto index = [&](int i, auto set) STG_AI {
-        constexpr int S = decltype(set)::value;
-        const uint32_t w = S == 0 ? mw[i].x : mw[i].y;
-        return (int)((w >> (16 * half)) & 0xFFFFu);
-    };
 
     f16_t acc[FM][FN];
 #pragma unroll
@@ -438,17 +440,22 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
     auto mma = [&](auto set) STG_AI {
         constexpr int S = decltype(set)::value;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i) {
+            // this lane's 16-bit half of the step's metadata word
+            const uint32_t w = S == 0 ? mw[i].x : mw[i].y;
+            const int idx = (int)((w >> (16 * half)) & 0xFFFFu);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = smfmac32(af[S][i], bf[S][j], index(i, set), acc[i][j]);
+                acc[i][j] = smfmac32(af[S][i], bf[S][j], idx, acc[i][j]);
+        }
     };
 
     // one tile: the first step's fragment reads, then the SMFMACs with the
     // second step's reads spread over the first step's SMFMACs and the
     // copies of a future tile spread over all of them
     constexpr int NM = FM * FN;
-    constexpr int NR0 = 2 * FM + 2 * FN, NR1 = FM + 2 * FN; // DS reads of steps 0 and 1
+    // DS reads of steps 0 and 1 (the two metadata words of a row merge into one)
+    constexpr int NR0 = 2 * FM + 2 * FN, NR1 = FM + 2 * FN;
     auto schedule = [&]() STG_AI {
         __builtin_amdgcn_sched_group_barrier(0x100, NR0, 0); // step 0 DS reads
         [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
@@ -469,43 +476,40 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
 
-    // prologue: tiles 0 .. NSTAGE-2 requested (their metadata stored), the
-    // metadata of tile NSTAGE-1 in flight; wait for tile 0
-    // (the last metadata load goes out before the last copies, as in the
-    // loop, so that its first store waits for it alone)
-    uint32_t mw_next = 0;
+    // prologue: metadata group 0, tiles 0 and 1 requested; wait for group 0
+    // and tile 0 (tile 1's copies may be in flight)
+    // (the compiler fences keep the copies in program order: the waits below
+    // count requests in that order)
+    dma_meta(0);
+    STG_COMPILER_FENCE();
 #pragma unroll
-    for (int p = 0; p < NSTAGE - 1; ++p) {
-        const uint32_t w = load_meta(p);
-        if (p == NSTAGE - 2)
-            mw_next = load_meta(NSTAGE - 1);
+    for (int p = 0; p < NSTAGE - 1; ++p)
         dma_tile(p, p);
-        store_meta(p, w);
-    }
-    STG_WAIT_VMCNT((NSTAGE - 2) * NL + 1);
+    STG_WAIT_VMCNT((NSTAGE - 2) * NI);
     lds_barrier();
 
     int st = 0; // LDS stage of tile t
     for (int t = 0; t < KT; ++t) {
         const uint8_t *cur = lds + st * STAGE;
-        const int stn = st == 0 ? NSTAGE - 1 : st - 1; // stage of tile t + NSTAGE - 1
-        // tile t+NSTAGE-1: metadata (loaded during the previous tile) into
-        // LDS, its copies requested; the next tile's metadata loaded
-        store_meta(stn, mw_next);
-        mw_next = load_meta(t + NSTAGE);
-        // the metadata load goes out ahead of the copies, so that storing it
-        // at the next tile waits only for it and not for them
-        __builtin_amdgcn_sched_barrier(0);
-        dma_tile(stn, t + NSTAGE - 1);
-        lread(I0{}, cur);
-        lread(I1{}, cur);
+        // at the first tile of a group: the next group's metadata, into the
+        // slot whose tiles ended with the barrier before this tile
+        const bool meta_now = (t % MG) == 0;
+        if (meta_now)
+            dma_meta(t + MG);
+        STG_COMPILER_FENCE();
+        dma_tile(st == 0 ? NSTAGE - 1 : st - 1, t + NSTAGE - 1);
+        lread(I0{}, cur, t);
+        lread(I1{}, cur, t);
         mma(I0{});
         mma(I1{});
         schedule();
         __builtin_amdgcn_sched_barrier(0);
-        // tile t+1 complete (the requests of later tiles may be in flight);
-        // this wave's LDS reads and metadata store done
-        STG_WAIT_VMCNT((NSTAGE - 2) * NL);
+        // tile t+1 complete (the requests of this tile may be in flight: the
+        // copies of tile t+2, and the metadata group requested at its start)
+        if (meta_now)
+            STG_WAIT_VMCNT((NSTAGE - 2) * NI + 1);
+        else
+            STG_WAIT_VMCNT((NSTAGE - 2) * NI);
         lds_barrier();
         st = st == NSTAGE - 1 ? 0 : st + 1;
     }
@@ -526,7 +530,7 @@ hipError_t launch_sparse(int family, const SparseArgs &a, hipStream_t s)
     if (family == KF_SPARSE_DMA8) {
         constexpr int BM = 256, BN = 256;
         const int tiles_m = (int)((a.e.M + BM - 1) / BM), tiles_n = (int)((a.e.N + BN - 1) / BN);
-        hipLaunchKernelGGL((k_sparse_dma8<3>), dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0,
+        hipLaunchKernelGGL(k_sparse_dma8, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0,
                            s, a, tiles_m, tiles_n);
         return hipGetLastError();
     }

@@ -62,7 +62,8 @@ def test_sparse_parity(orc, algo, shape):
     D, name = gpu_sparse_gemm(vals, meta, p["B"], p["C"], M, N, K, algo=algo)
     say("  ", name)
     if algo != "auto":
-        assert name.startswith({"tiled": "sparse24_dma8", "generic": "sparse24_generic"}[algo]), name
+        tiled = "sparse24_dma8" if K % 256 == 0 else "sparse24_tiled"
+        assert name.startswith({"tiled": tiled, "generic": "sparse24_generic"}[algo]), name
     Dr, Y, S = orc.gemm(p["A_logical"], p["B"], p["C"], None, M, N, K, "f16", "f16", "f32")
     r = check(D, "f32", Dr, Y, S, "f16")
     say("  ", r)
@@ -96,12 +97,18 @@ def test_sparse_row_major_b(orc):
     assert check(D, "f32", Dr, Y, S, "f16").ok
 
 
-@pytest.mark.parametrize("family", ["sparse24_tiled", "sparse24_dma8"])
-@pytest.mark.parametrize("shape", [(600, 520, 256), (256, 256, 64), (300, 700, 448),
-                                   (512, 264, 1024), (40, 1000, 192)])
+@pytest.mark.parametrize("family,shape", [
+    ("sparse24_tiled", (600, 520, 256)), ("sparse24_tiled", (256, 256, 64)),
+    ("sparse24_tiled", (300, 700, 448)), ("sparse24_tiled", (40, 1000, 192)),
+    # the 8-wave kernel takes K in multiples of 256: one metadata group, odd
+    # and even group counts, group counts that do and do not divide the
+    # workgroup's K rotation
+    ("sparse24_dma8", (600, 520, 256)), ("sparse24_dma8", (256, 256, 512)),
+    ("sparse24_dma8", (300, 700, 768)), ("sparse24_dma8", (512, 264, 1024)),
+    ("sparse24_dma8", (40, 1000, 1280)), ("sparse24_dma8", (2100, 300, 2304))])
 def test_sparse_parity_variants(orc, monkeypatch, family, shape):
     """Each 256 x 256 SMFMAC kernel (selected through the STGEMM_FORCE_KERNEL
-    tuning override): ragged M and N, one K tile, odd and even K tile counts."""
+    tuning override): ragged M and N, one and several K tiles."""
     monkeypatch.setenv("STGEMM_FORCE_KERNEL", family)
     M, N, K = shape
     p = inputs.sparse24_f16(M=M, N=N, K=K)
@@ -133,3 +140,11 @@ def test_sparse_epilogue_bit_exact(orc, monkeypatch, family, d_type):
     mism = int((D != ref).sum())
     say("sparse epilogue", family, d_type, "mismatches", mism)
     assert mism == 0
+
+
+def test_sparse_dma8_needs_whole_metadata_groups():
+    """K not a multiple of 256 goes to the 4-wave SMFMAC kernel."""
+    for K, name in [(256, "sparse24_dma8"), (512, "sparse24_dma8"), (192, "sparse24_tiled"),
+                    (320, "sparse24_tiled")]:
+        plan = G.gemm_plan(G.make_desc(512, 512, K, "f16", "f16", "f32", sparse_a=True))
+        assert plan.name.startswith(name), (K, plan.name)
