@@ -271,6 +271,19 @@ __device__ STG_AI inline u4_t buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int
     return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// 16-byte chunk slot inside a 64-byte LDS row: chunk c of row r sits at slot
+// c ^ swz64(r).  Chosen by measurement on gfx950 (LDS bank-conflict counter
+// over the fragment-read pattern of 32 consecutive rows): rotating the slot
+// every 4 rows is conflict-free, while the textbook 32-bank XOR patterns
+// ((r >> 1) & 3, r & 3, and mixes of them) stall 2- to 4-way.
+// swz64(r + 32 i) == swz64(r).
+__device__ STG_AI inline int swz64(int r) { return (r >> 2) & 3; }
+
+// 16-byte chunk slot inside a 128-byte LDS row: chunk c of row r sits at
+// slot c ^ swz128(r) (conflict-free for 16-byte fragment reads of 32
+// consecutive rows, measured the same way).
+__device__ STG_AI inline int swz128(int r) { return (r ^ (r >> 3)) & 7; }
+
 // Number of the `total` memory instructions that follow MFMA slot q of
 // `slots` when they are spread evenly.
 constexpr int spread(int q, int total, int slots)

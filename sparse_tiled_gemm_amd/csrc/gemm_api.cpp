@@ -160,6 +160,7 @@ const char *family_name(int f)
     case KF_SPARSE_GENERIC: return "sparse24_generic";
     case KF_SPARSE_TILED: return "sparse24_tiled";
     case KF_SPARSE_DMA8: return "sparse24_dma8";
+    case KF_TILED_256W8L: return "tiled256w8l";
     case KF_TILED_DMA4: return "tiled256dma4";
     case KF_TILED_DMA5: return "tiled256dma5";
     case KF_TILED_256W8: return "tiled256w8";
@@ -184,7 +185,7 @@ bool is_tiled(int f)
 {
     return f == KF_TILED_256 || f == KF_TILED_128 || f == KF_TILED_DMA4 || f == KF_TILED_DMA5 ||
            f == KF_TILED_256W8 || f == KF_TILED_256W8T || f == KF_PINGPONG4 ||
-           f == KF_PINGPONG5;
+           f == KF_PINGPONG5 || f == KF_TILED_256W8L;
 }
 
 } // namespace
@@ -328,6 +329,8 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     }
 
     const bool tiled = tiled_ok(d);
+    // K in whole 128-byte tiles (the 128-byte-K-tile kernel)
+    const bool long_k = tiled && (d.K * elem_bytes(d.a_type)) % 128 == 0;
     const bool skinny = skinny_ok(d);
     int fam = -1;
     const int64_t big_tiles = ceil_div(d.M, 256) * ceil_div(d.N, 256);
@@ -357,7 +360,8 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     if (const char *force = getenv("STGEMM_FORCE_KERNEL")) {
         for (int f = 0; f < KF_COUNT; ++f)
             if (strcmp(force, family_name(f)) == 0 &&
-                (f == KF_GENERIC || (tiled && is_tiled(f)) || (skinny && f == KF_SKINNY)))
+                (f == KF_GENERIC || (tiled && is_tiled(f) && (f != KF_TILED_256W8L || long_k)) ||
+                 (skinny && f == KF_SKINNY)))
                 fam = f;
     }
     p->family = fam;

@@ -35,6 +35,7 @@ enum KernelFamily {
     KF_PINGPONG4,    // 256 x 256, 8 waves in two out-of-phase groups, 4 LDS stages
     KF_PINGPONG5,    // same with 5 LDS stages
     KF_SPARSE_DMA8,  // 2:4 A, 256 x 256, 8 waves, direct global -> LDS copies, 3 stages
+    KF_TILED_256W8L, // 256 x 256, 8 waves of 128 x 64, 128-byte K tiles, 2 direct-copy stages
     KF_COUNT
 };
 

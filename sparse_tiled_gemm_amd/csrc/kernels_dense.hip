@@ -94,13 +94,6 @@ __global__ __launch_bounds__(256) void k_generic(GemmArgs g)
 
 // ---------------------------------------------------------------- tiled
 
-// 16-byte chunk slot inside a 64-byte LDS row: chunk c of row r sits at slot
-// c ^ swz64(r).  Chosen by measurement on gfx950 (LDS bank-conflict counter
-// over the fragment-read pattern of 32 consecutive rows): rotating the slot
-// every 4 rows is conflict-free, while the textbook 32-bank XOR patterns
-// ((r >> 1) & 3, r & 3, and mixes of them) stall 2- to 4-way.
-// swz64(r + 32 i) == swz64(r).
-__device__ STG_AI inline int swz64(int r) { return (r >> 2) & 3; }
 
 template <class OP, int BM, int BN, int GM = 2, int GN = 2, int WG_PER_CU = 1>
 __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, int tiles_m,
@@ -467,6 +460,170 @@ __global__ __launch_bounds__(256, 1) void k_tiled_dma(GemmArgs g, int tiles_m, i
                                   (uint32_t *)lds + wave * 32 * (WN + 4));
 }
 
+// ---------------------------------------------------------------- 128-byte K tiles
+
+// 256 x 256 tile, 8 waves (two per SIMD) as 2 x 4, each a 128 x 64 block of
+// 32x32 fragments, with K tiles of 128 bytes per row: every row of a tile is
+// one whole 128-byte line.  With 64-byte K tiles each line is requested twice,
+// half at a time, one K tile apart; measured on MI355X with the operand
+// pattern of an 8192^3 GEMM, L2 delivers 21.5 TB/s to the CUs for whole-line
+// rows against 13.2 TB/s for half lines (a tile-packed copy of the operands
+// would give 23.2).  A stage is then 64 KB, so there are two, filled by
+// direct global -> LDS copies: tile t+1 is requested at the start of tile t
+// into the stage tile t-1 used, and waited for at the end of tile t.
+// Fragments are double-buffered within a tile; the first step's fragment
+// reads of each tile are covered by the other wave on the SIMD.
+template <class OP>
+__global__ __launch_bounds__(512, 1) void k_tiled_w8l(GemmArgs g, int tiles_m, int tiles_n)
+{
+    constexpr int BM = 256, BN = 256, BKB = 128, NSTAGE = 2;
+    constexpr int WM = 128, WN = 64, FM = WM / 32, FN = WN / 32, GN = BN / WN;
+    constexpr int STAGE = (BM + BN) * BKB;
+    constexpr int NV = OP::LANE_BYTES / 16; // 16-byte LDS reads per operand fragment
+    constexpr int FW = OP::LANE_BYTES / 4;  // 32-bit words per operand fragment
+    constexpr int KS = BKB / OP::KB;        // MFMA K steps per tile
+    constexpr int ROWS_PER_INST = 1024 / BKB;            // 8
+    constexpr int A_I = BM / ROWS_PER_INST / 8;          // copies per wave per tile (4)
+    constexpr int B_I = BN / ROWS_PER_INST / 8;
+    constexpr int NI = A_I + B_I;
+    constexpr int EPI = 8 * 32 * (WN + 4) * 4;
+    constexpr int LDS_BYTES = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m_blk = (int64_t)tm * BM, n_blk = (int64_t)tn * BN;
+    const int64_t lda_b = g.a_rs * OP::ELEM, ldb_b = g.b_cs * OP::ELEM;
+    const int64_t kbytes = g.K * OP::ELEM;
+    const int KT = (int)(kbytes / BKB);
+    const __amdgpu_buffer_rsrc_t ra = tile_rsrc((const uint8_t *)g.A + m_blk * lda_b,
+                                                (g.e.M - m_blk - 1) * lda_b + kbytes);
+    const __amdgpu_buffer_rsrc_t rb = tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b,
+                                                (g.e.N - n_blk - 1) * ldb_b + kbytes);
+
+    // a copy instruction fills 1 KB of LDS = 8 rows of 128 bytes; lane l
+    // writes slot l % 8 of row l / 8 and fetches the chunk the swizzle maps
+    // there
+    int voff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const bool is_a = i < A_I;
+        const int blk = is_a ? wave * A_I + i : wave * B_I + (i - A_I);
+        const int row = blk * ROWS_PER_INST + (lane >> 3);
+        voff[i] = row * (int)(is_a ? lda_b : ldb_b) + (((lane & 7) ^ swz128(row)) << 4);
+    }
+    auto dma_tile = [&](int stage, int kt) STG_AI {
+        uint8_t *base = lds + stage * STAGE;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const bool is_a = i < A_I;
+            const int blk = is_a ? wave * A_I + i : BM / ROWS_PER_INST + wave * B_I + (i - A_I);
+            dma16(is_a ? ra : rb, base + blk * 1024, voff[i], kt * BKB);
+        }
+    };
+
+    const int wm = wave / GN, wn = wave % GN;
+    const int arow = wm * WM + (lane & 31), brow = wn * WN + (lane & 31);
+    const int half = lane >> 5;
+    int sa[FM], sb[FN]; // swz128 is not 32-row periodic
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+        sa[i] = swz128(arow + 32 * i);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+        sb[j] = swz128(brow + 32 * j);
+    const int a_off = arow * BKB, b_off = BM * BKB + brow * BKB;
+
+    uint32_t fa[2][FM][FW], fb[2][FN][FW];
+    auto lread = [&](auto set, const uint8_t *stage_base, int s) STG_AI {
+        constexpr int S = decltype(set)::value;
+        const uint8_t *lsa = stage_base + a_off;
+        const uint8_t *lsb = stage_base + b_off;
+        const int c0 = (s * OP::KB + half * OP::LANE_BYTES) >> 4;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                *(u4_t *)&fa[S][i][4 * v] =
+                    *(const u4_t *)(lsa + i * 32 * BKB + (((c0 + v) ^ sa[i]) << 4));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                *(u4_t *)&fb[S][j][4 * v] =
+                    *(const u4_t *)(lsb + j * 32 * BKB + (((c0 + v) ^ sb[j]) << 4));
+        }
+    };
+
+    typename OP::acc_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = typename OP::acc_t{};
+    auto mma = [&](auto set) STG_AI {
+        constexpr int S = decltype(set)::value;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = OP::mma(fa[S][i], fb[S][j], acc[i][j]);
+    };
+
+    // the first step's fragment reads, then each step's MFMAs with the next
+    // step's reads spread over them, and the copies of the next tile spread
+    // over the whole tile
+    constexpr int NM = FM * FN, NR = (FM + FN) * NV, NMT = KS * NM;
+    auto schedule = [&]() STG_AI {
+        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0); // step 0 DS reads
+        [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
+            (
+                [&]() STG_AI {
+                    constexpr int m = Q % NM;
+                    constexpr int nr = Q < NMT - NM ? spread(m, NR, NM) : 0;
+                    constexpr int nl = spread(Q, NI, NMT);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                    if constexpr (nr > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x100, nr, 0); // DS read
+                    if constexpr (nl > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x020, nl, 0); // VMEM read
+                }(),
+                ...);
+        }(std::make_integer_sequence<int, NMT>{});
+    };
+
+    // prologue: tile 0 into stage 0
+    dma_tile(0, 0);
+    STG_WAIT_VMCNT(0);
+    lds_barrier();
+
+    for (int t = 0; t < KT; ++t) {
+        const uint8_t *cur = lds + (t & 1) * STAGE;
+        // tile t+1 into the stage of tile t-1 (the copy past the last tile
+        // reads bytes that are never used, or zeros past the resource)
+        dma_tile((t + 1) & 1, t + 1);
+        lread(std::integral_constant<int, 0>{}, cur, 0);
+        [&]<int... S>(std::integer_sequence<int, S...>) STG_AI {
+            (
+                [&]() STG_AI {
+                    if constexpr (S + 1 < KS)
+                        lread(std::integral_constant<int, (S + 1) & 1>{}, cur, S + 1);
+                    mma(std::integral_constant<int, S & 1>{});
+                }(),
+                ...);
+        }(std::make_integer_sequence<int, KS>{});
+        schedule();
+        __builtin_amdgcn_sched_barrier(0);
+        STG_WAIT_VMCNT(0); // this wave's copies of tile t+1 complete
+        lds_barrier();     // ... and every wave's; tile t's stage is free
+    }
+
+    __syncthreads(); // every wave is done with the LDS stages
+    epilogue_grid_lds<OP, FM, FN>(g.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
+                                  (uint32_t *)lds + wave * 32 * (WN + 4));
+}
+
 // ---------------------------------------------------------------- ping-pong
 
 // 256 x 256 tile, 8 waves in two groups of four (one wave of each group per
@@ -778,6 +935,29 @@ static dense_launch_fn tiled_table_t(int op)
     }
 }
 
+template <class OP>
+static hipError_t launch_w8l_t(const GemmArgs &g, hipStream_t s)
+{
+    const int tiles_m = (int)((g.e.M + 255) / 256), tiles_n = (int)((g.e.N + 255) / 256);
+    hipLaunchKernelGGL(k_tiled_w8l<OP>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, s, g,
+                       tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+static dense_launch_fn w8l_table(int op)
+{
+    switch (op) {
+    case OPK_F16: return launch_w8l_t<OpF16>;
+    case OPK_BF16: return launch_w8l_t<OpBF16>;
+    case OPK_F8_E4E4: return launch_w8l_t<OpF8<0, 0>>;
+    case OPK_F8_E4E5: return launch_w8l_t<OpF8<0, 1>>;
+    case OPK_F8_E5E4: return launch_w8l_t<OpF8<1, 0>>;
+    case OPK_F8_E5E5: return launch_w8l_t<OpF8<1, 1>>;
+    case OPK_S8: return launch_w8l_t<OpS8>;
+    default: return nullptr;
+    }
+}
+
 template <class OP, int NS>
 static hipError_t launch_pingpong_t(const GemmArgs &g, hipStream_t s)
 {
@@ -860,6 +1040,7 @@ hipError_t launch_dense(int family, int op, const GemmArgs &g, hipStream_t s)
     case KF_TILED_256W8T: fn = tiled_table_t<256, 256, 4, 2>(op); break;
     case KF_PINGPONG4: fn = pingpong_table<4>(op); break;
     case KF_PINGPONG5: fn = pingpong_table<5>(op); break;
+    case KF_TILED_256W8L: fn = w8l_table(op); break;
     case KF_TILED_DMA4: fn = dma_table_t<256, 256, 4>(op); break;
     case KF_TILED_DMA5: fn = dma_table_t<256, 256, 5>(op); break;
     default: break;

@@ -125,9 +125,6 @@ __global__ __launch_bounds__(256) void k_sparse_generic(SparseArgs a)
 
 // ---------------------------------------------------------------- tiled
 
-// Chunk swizzles: 128-byte rows (B tile) and 64-byte rows (compressed A).
-__device__ STG_AI inline int swz128(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ STG_AI inline int swz64(int r) { return (r >> 2) & 3; }
 
 // v_smfmac_f32_32x32x32_f16 covers 32 logical K positions k0..k0+31.  Lane l
 // (h = l / 32) supplies, for row l % 32 of A, the 8 kept values of logical K

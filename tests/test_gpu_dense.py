@@ -82,6 +82,26 @@ def test_dense_parity_dma_variants(orc, monkeypatch, family, a_type, b_type, sha
 
 
 @pytest.mark.parametrize("a_type,b_type", PAIRS)
+@pytest.mark.parametrize("shape", [(600, 520, 256), (256, 256, 128), (300, 700, 384),
+                                   (520, 264, 1152)])
+def test_dense_parity_long_k_tiles(orc, monkeypatch, a_type, b_type, shape):
+    """The 256 x 256 kernel with 128-byte K tiles (K bytes a multiple of 128;
+    selected through the STGEMM_FORCE_KERNEL tuning override)."""
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", "tiled256w8l")
+    M, N, K = shape
+    A, B, C, _ = make(a_type, b_type, M, N, K, seed=zlib.crc32(repr(("w8l", a_type, shape)).encode()))
+    d_type = "s32" if a_type == "s8" else "f32"
+    compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, "auto", expect_kernel="tiled256w8l")
+
+
+def test_long_k_tiles_need_whole_128_byte_tiles(monkeypatch):
+    """K bytes not a multiple of 128: the tuning override is ignored."""
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", "tiled256w8l")
+    assert G.gemm_plan(G.make_desc(512, 512, 256, "bf16", "bf16", "f32")).name.startswith("tiled256w8l")
+    assert not G.gemm_plan(G.make_desc(512, 512, 96, "bf16", "bf16", "f32")).name.startswith("tiled256w8l")
+
+
+@pytest.mark.parametrize("a_type,b_type", PAIRS)
 @pytest.mark.parametrize("shape", [(16, 1024, 2048), (1, 300, 512), (7, 96, 1024), (16, 33, 256),
                                    (12, 8192, 768)])
 def test_skinny_parity(orc, a_type, b_type, shape):
@@ -138,7 +158,7 @@ def test_epilogue_variants(orc, a_type, b_type, d_type, algo, epi):
             alpha=epi.get("alpha", 1.0), relu=epi.get("relu", False))
 
 
-@pytest.mark.parametrize("algo", ["tiled256", "tiled128", "generic", "tiled256dma5"])
+@pytest.mark.parametrize("algo", ["tiled256", "tiled128", "generic", "tiled256dma5", "tiled256w8l"])
 @pytest.mark.parametrize("a_type,b_type,d_type", [("bf16", "bf16", "bf16"), ("f16", "f16", "f16"),
                                                   ("e4m3", "e5m2", "f16"),
                                                   ("e4m3", "e5m2", "bf16")])
@@ -146,7 +166,7 @@ def test_epilogue_bit_exact(orc, monkeypatch, algo, a_type, b_type, d_type):
     """The fused epilogue equals the oracle's fp32 epilogue applied to the
     same kernel's fp32 accumulator output, bit for bit (same plan family, so
     the same summation order)."""
-    if algo.startswith("tiled256dma"):
+    if algo.startswith("tiled256") and algo != "tiled256":
         monkeypatch.setenv("STGEMM_FORCE_KERNEL", algo)
         algo = "tiled256"
     M, N, K = 384, 320, 256
