@@ -771,8 +771,9 @@ __global__ __launch_bounds__(512, 1) void k_pingpong(GemmArgs g, int tiles_m, in
 // ---------------------------------------------------------------- skinny
 
 // Small-M GEMM (M <= 16), bound by streaming B once from HBM.  One workgroup
-// owns 32 output columns (two 16x16 MFMA fragments); its 4 waves split K
-// (chunk c of 256 K bytes goes to wave c % 4), feed 16x16 MFMAs directly from
+// owns 32 output columns (two 16x16 MFMA fragments); its 8 waves split K
+// (chunk c of 256 K bytes goes to wave c % 8; 8 waves keep twice the bytes in
+// flight of 4 and measured 3-22 % faster), feed 16x16 MFMAs directly from
 // global memory and reduce their partial sums through LDS before the
 // epilogue.  Within a chunk, lane l (group g = l / 16) loads 64 contiguous
 // bytes of its row at byte 64 g, and MFMA step j uses bytes 16 j.. of every
@@ -780,14 +781,15 @@ __global__ __launch_bounds__(512, 1) void k_pingpong(GemmArgs g, int tiles_m, in
 // each product pairs equal K.  Each row's 256 bytes are fetched by 4 lanes as
 // whole cache lines; two chunks are kept in flight per wave.
 template <class OP>
-__global__ __launch_bounds__(256, 1) void k_skinny(GemmArgs g)
+__global__ __launch_bounds__(512, 1) void k_skinny(GemmArgs g)
 {
+    constexpr int WAVES = 8;
     constexpr int CB = 256;                      // K bytes per chunk
     constexpr int LB = 64;                       // bytes per lane per chunk
     constexpr int NLD = LB / 16;                 // 16-byte loads per row-fragment per chunk
     constexpr int STEPS = LB / OP::LANE_BYTES;   // MFMAs per fragment per chunk
     constexpr int FW = OP::LANE_BYTES / 4;
-    __shared__ __attribute__((aligned(16))) uint32_t red[4][2][64][4];
+    __shared__ __attribute__((aligned(16))) uint32_t red[WAVES][2][64][4];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -828,18 +830,18 @@ __global__ __launch_bounds__(256, 1) void k_skinny(GemmArgs g)
     int c = wave;
     if (c < NC)
         load(I0{}, c);
-    for (; c < NC; c += 8) {
-        if (c + 4 < NC)
-            load(I1{}, c + 4);
+    for (; c < NC; c += 2 * WAVES) {
+        if (c + WAVES < NC)
+            load(I1{}, c + WAVES);
         compute(I0{});
-        if (c + 4 >= NC)
+        if (c + WAVES >= NC)
             break;
-        if (c + 8 < NC)
-            load(I0{}, c + 8);
+        if (c + 2 * WAVES < NC)
+            load(I0{}, c + 2 * WAVES);
         compute(I1{});
     }
 
-    // reduce the four waves' partial sums, then one wave stores 16 x 32
+    // reduce the waves' partial sums, then one wave stores 16 x 32
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
@@ -853,7 +855,7 @@ __global__ __launch_bounds__(256, 1) void k_skinny(GemmArgs g)
         for (int f = 0; f < 2; ++f) {
             typename OP::acc_t t = acc[f];
 #pragma unroll
-            for (int w = 1; w < 4; ++w)
+            for (int w = 1; w < WAVES; ++w)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t u = red[w][f][lane][i];
@@ -986,7 +988,7 @@ template <class OP>
 static hipError_t launch_skinny_t(const GemmArgs &g, hipStream_t s)
 {
     const unsigned blocks = (unsigned)((g.e.N + 31) / 32);
-    hipLaunchKernelGGL(k_skinny<OP>, dim3(blocks), dim3(256), 0, s, g);
+    hipLaunchKernelGGL(k_skinny<OP>, dim3(blocks), dim3(512), 0, s, g);
     return hipGetLastError();
 }
 
