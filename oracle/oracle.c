@@ -368,27 +368,69 @@ int oracle_epilogue_f32(int64_t M, int64_t N, const float *T, float alpha, const
 
 /* ------------------------------------------------------------------ 2:4 */
 
-static int f16_is_zero(uint16_t h) { return (h & 0x7FFF) == 0; }
+/* Storage bytes of an element of a 2:4-compressible type, 0 for the others. */
+static int sp_bytes(int type)
+{
+    switch (type) {
+    case OR_F16:
+    case OR_BF16: return 2;
+    case OR_E4M3:
+    case OR_E5M2:
+    case OR_S8: return 1;
+    default: return 0;
+    }
+}
+
+/* A zero of the format: +0 or -0 for the float formats (all bits but the
+ * sign clear), 0 for s8 (whose 0x80 is -128, not a zero).  Every other code,
+ * NaN and infinity included, is a non-zero. */
+static int sp_is_zero(int type, uint32_t bits)
+{
+    switch (type) {
+    case OR_F16:
+    case OR_BF16: return (bits & 0x7FFFu) == 0;
+    case OR_E4M3:
+    case OR_E5M2: return (bits & 0x7Fu) == 0;
+    default: return bits == 0;
+    }
+}
+
+static uint32_t sp_get(const void *p, int eb, int64_t i)
+{
+    return eb == 2 ? ((const uint16_t *)p)[i] : ((const uint8_t *)p)[i];
+}
+
+static void sp_put(void *p, int eb, int64_t i, uint32_t v)
+{
+    if (eb == 2)
+        ((uint16_t *)p)[i] = (uint16_t)v;
+    else
+        ((uint8_t *)p)[i] = (uint8_t)v;
+}
 
 /* "NVIDIA MMA", section "Dense and 2:4 structured sparse multiplication":
  * every 4 consecutive K positions of A keep 2 values and the positions they
  * came from (logical [a0,0,0,a3] -> values [a0,a3], positions [0,3]); the
  * "ordered metadata" form (section "Ampere: FP16/BF16 and integer MMA
- * baseline") lists the positions in ascending order. */
-int64_t oracle_sparse24_compress(int64_t M, int64_t K, const uint16_t *A, uint16_t *values,
+ * baseline") lists the positions in ascending order.  The format does not
+ * depend on the element type: only what counts as a zero does. */
+int64_t oracle_sparse24_compress(int type, int64_t M, int64_t K, const void *A, void *values,
                                  uint32_t *meta)
 {
-    if (M < 0 || K < 0 || (K % 4) != 0)
+    const int eb = sp_bytes(type);
+    if (eb == 0 || M < 0 || K < 0 || (K % 4) != 0)
         return -1;
     const int64_t G = K / 4, W = (K + 31) / 32;
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t w = 0; w < W; ++w)
             meta[m * W + w] = 0u;
         for (int64_t g = 0; g < G; ++g) {
-            const uint16_t *grp = A + m * K + 4 * g;
+            uint32_t grp[4];
+            for (int i = 0; i < 4; ++i)
+                grp[i] = sp_get(A, eb, m * K + 4 * g + i);
             int kept[4], nk = 0;
             for (int i = 0; i < 4; ++i)
-                if (!f16_is_zero(grp[i]))
+                if (!sp_is_zero(type, grp[i]))
                     kept[nk++] = i;
             if (nk > 2)
                 return m + 1;
@@ -405,8 +447,8 @@ int64_t oracle_sparse24_compress(int64_t M, int64_t K, const uint16_t *A, uint16
                 kept[0] = kept[1];
                 kept[1] = t;
             }
-            values[m * (K / 2) + 2 * g] = grp[kept[0]];
-            values[m * (K / 2) + 2 * g + 1] = grp[kept[1]];
+            sp_put(values, eb, m * (K / 2) + 2 * g, grp[kept[0]]);
+            sp_put(values, eb, m * (K / 2) + 2 * g + 1, grp[kept[1]]);
             uint32_t nib = (uint32_t)kept[0] | ((uint32_t)kept[1] << 2);
             meta[m * W + g / 8] |= nib << (4 * (g % 8));
         }
@@ -414,22 +456,23 @@ int64_t oracle_sparse24_compress(int64_t M, int64_t K, const uint16_t *A, uint16
     return 0;
 }
 
-int oracle_sparse24_decompress(int64_t M, int64_t K, const uint16_t *values, const uint32_t *meta,
-                               uint16_t *A)
+int oracle_sparse24_decompress(int type, int64_t M, int64_t K, const void *values,
+                               const uint32_t *meta, void *A)
 {
-    if (M < 0 || K < 0 || (K % 4) != 0)
+    const int eb = sp_bytes(type);
+    if (eb == 0 || M < 0 || K < 0 || (K % 4) != 0)
         return -1;
     const int64_t G = K / 4, W = (K + 31) / 32;
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t k = 0; k < K; ++k)
-            A[m * K + k] = 0;
+            sp_put(A, eb, m * K + k, 0u);
         for (int64_t g = 0; g < G; ++g) {
             uint32_t nib = (meta[m * W + g / 8] >> (4 * (g % 8))) & 0xFu;
             int i0 = (int)(nib & 3u), i1 = (int)(nib >> 2);
             if (i0 >= i1)
                 return -1;
-            A[m * K + 4 * g + i0] = values[m * (K / 2) + 2 * g];
-            A[m * K + 4 * g + i1] = values[m * (K / 2) + 2 * g + 1];
+            sp_put(A, eb, m * K + 4 * g + i0, sp_get(values, eb, m * (K / 2) + 2 * g));
+            sp_put(A, eb, m * K + 4 * g + i1, sp_get(values, eb, m * (K / 2) + 2 * g + 1));
         }
     }
     return 0;

@@ -22,7 +22,12 @@
  *     2:4 format keeps 2 of every 4 consecutive K positions of A, with their
  *     positions as metadata; ascending positions per the "ordered metadata"
  *     remark in the Ampere section.  Metadata bit packing is not on the pages;
- *     the packing used here is stated at oracle_sparse24_compress.
+ *     the packing used here is stated at oracle_sparse24_compress.  The
+ *     sparse rows of the instruction tables in the sections "Ampere:
+ *     FP16/BF16 and integer MMA baseline" (FP16, BF16, INT8) and "Ada:
+ *     mma.sync adds FP8" (E4M3/E5M2, A and B formats may differ) give the
+ *     element types the format applies to; the format itself is the same
+ *     for all of them.
  *   - bit formats: IEEE binary16; bfloat16 = the upper 16 bits of binary32;
  *     OCP FP8 E4M3 (bias 7, no infinity, 0x7F/0xFF NaN, max 448) and E5M2
  *     (bias 15, IEEE-like infinities, max 57344), the bare FP8 formats named
@@ -95,24 +100,28 @@ int oracle_gemm_entries(const oracle_gemm_t *g, const void *A, const void *B, co
 int oracle_epilogue_f32(int64_t M, int64_t N, const float *T, float alpha, const float *bias,
                         int relu, int d_type, void *D);
 
-/* 2:4 compression of a row-major fp16 [M,K] matrix, K % 4 == 0.
+/* 2:4 compression of a row-major [M,K] matrix of type `type` (OR_F16,
+ * OR_BF16, OR_E4M3, OR_E5M2 or OR_S8; elements of 2 or 1 bytes), K % 4 == 0.
  * Group g of row m is K positions 4g..4g+3.  Its kept positions i0 < i1 give
  *   values[m*(K/2) + 2g]   = A[m, 4g+i0]
- *   values[m*(K/2) + 2g+1] = A[m, 4g+i1]
+ *   values[m*(K/2) + 2g+1] = A[m, 4g+i1]   (elements of the same type)
  *   nibble (i0 | i1 << 2) at bits 4*(g%8) .. 4*(g%8)+3 of meta[m*W + g/8],
  * with W = ceil(K/32) words per row and unused high nibbles 0.
- * Zeros (+0 and -0) are the dropped positions; a group with fewer than two
- * non-zeros keeps its non-zero positions and fills up with the lowest unused
- * positions; NaN counts as non-zero.
- * Returns 0, or the 1-based row index of the first row holding a group with
- * more than two non-zeros (then the outputs are unspecified). */
-int64_t oracle_sparse24_compress(int64_t M, int64_t K, const uint16_t *A, uint16_t *values,
+ * The dropped positions are zeros: +0 and -0 of the float formats, 0 of s8
+ * (0x80 is -128 there).  A group with fewer than two non-zeros keeps its
+ * non-zero positions and fills up with the lowest unused positions; NaN and
+ * infinity count as non-zero.
+ * Returns 0, -1 for a bad type or shape, or the 1-based row index of the
+ * first row holding a group with more than two non-zeros (then the outputs
+ * are unspecified). */
+int64_t oracle_sparse24_compress(int type, int64_t M, int64_t K, const void *A, void *values,
                                  uint32_t *meta);
 
-/* Inverse: logical fp16 [M,K] with +0 at the dropped positions.  Returns 0, or
- * -1 if some nibble is not ascending (i0 >= i1). */
-int oracle_sparse24_decompress(int64_t M, int64_t K, const uint16_t *values, const uint32_t *meta,
-                               uint16_t *A);
+/* Inverse: logical [M,K] of `type` with all-zero bits at the dropped
+ * positions.  Returns 0, or -1 for a bad type or shape or if some nibble is
+ * not ascending (i0 >= i1). */
+int oracle_sparse24_decompress(int type, int64_t M, int64_t K, const void *values,
+                               const uint32_t *meta, void *A);
 
 /* Threads the OpenMP loops use. */
 int oracle_num_threads(void);

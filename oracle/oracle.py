@@ -59,9 +59,9 @@ def lib():
         L.oracle_epilogue_f32.argtypes = [i64, i64, vp, ctypes.c_float, vp, ctypes.c_int,
                                           ctypes.c_int, vp]
         L.oracle_sparse24_compress.restype = ctypes.c_int64
-        L.oracle_sparse24_compress.argtypes = [i64, i64, vp, vp, vp]
+        L.oracle_sparse24_compress.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp]
         L.oracle_sparse24_decompress.restype = ctypes.c_int
-        L.oracle_sparse24_decompress.argtypes = [i64, i64, vp, vp, vp]
+        L.oracle_sparse24_decompress.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -176,15 +176,21 @@ class NotSparse24(ValueError):
     pass
 
 
-def sparse24_compress(A):
-    """fp16 [M,K] bits -> (values [M,K/2] uint16, meta [M,ceil(K/32)] uint32)."""
-    A = np.ascontiguousarray(A, dtype=np.uint16)
+SPARSE24_TYPES = ("f16", "bf16", "e4m3", "e5m2", "s8")
+
+
+def sparse24_compress(A, type_name="f16"):
+    """[M,K] raw bits of type_name -> (values [M,K/2] same storage,
+    meta [M,ceil(K/32)] uint32)."""
+    if type_name not in SPARSE24_TYPES:
+        raise ValueError("no 2:4 form for %s" % type_name)
+    A = np.ascontiguousarray(A, dtype=STORAGE[type_name])
     M, K = A.shape
     if K % 4:
         raise ValueError("K must be a multiple of 4")
-    values = np.zeros((M, K // 2), dtype=np.uint16)
+    values = np.zeros((M, K // 2), dtype=A.dtype)
     meta = np.zeros((M, (K + 31) // 32), dtype=np.uint32)
-    rc = lib().oracle_sparse24_compress(M, K, _ptr(A), _ptr(values), _ptr(meta))
+    rc = lib().oracle_sparse24_compress(TYPES[type_name], M, K, _ptr(A), _ptr(values), _ptr(meta))
     if rc > 0:
         raise NotSparse24("row %d has a group with more than two non-zeros" % (rc - 1))
     if rc < 0:
@@ -192,11 +198,14 @@ def sparse24_compress(A):
     return values, meta
 
 
-def sparse24_decompress(values, meta, M, K):
-    values = np.ascontiguousarray(values, dtype=np.uint16)
+def sparse24_decompress(values, meta, M, K, type_name="f16"):
+    if type_name not in SPARSE24_TYPES:
+        raise ValueError("no 2:4 form for %s" % type_name)
+    values = np.ascontiguousarray(values, dtype=STORAGE[type_name])
     meta = np.ascontiguousarray(meta, dtype=np.uint32)
-    A = np.zeros((M, K), dtype=np.uint16)
-    rc = lib().oracle_sparse24_decompress(M, K, _ptr(values), _ptr(meta), _ptr(A))
+    A = np.zeros((M, K), dtype=values.dtype)
+    rc = lib().oracle_sparse24_decompress(TYPES[type_name], M, K, _ptr(values), _ptr(meta),
+                                          _ptr(A))
     if rc != 0:
         raise ValueError("metadata not ascending or bad shape")
     return A

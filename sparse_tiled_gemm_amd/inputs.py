@@ -12,6 +12,7 @@ Operand layouts: A is [M,K] row-major, B is stored [N,K] (column-major K x N),
 C and D are [M,N] row-major, bias is [N] fp32.
 
 Seeds are 1000*workload + tensor (A=1, B=2, C=3, bias=4, sparsity pattern=5).
+For the 2:4 workloads the A seed draws the kept values.
 """
 import numpy as np
 import torch
@@ -102,33 +103,111 @@ def dense_fp8(M=8192, N=8192, K=8192, workload=4):
                    bias=bias, alpha=alpha, relu=True)
 
 
+_PAIRS = np.array([(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)], dtype=np.int64)
+# bits that must be non-zero for an element to count as a non-zero
+_NZ_MASK = {"f16": 0x7FFF, "bf16": 0x7FFF, "e4m3": 0x7F, "e5m2": 0x7F, "s8": 0xFF}
+
+
+def _scatter_24(M, K, workload, draw_kept, a_type):
+    """Logical [M,K] A with exactly two non-zeros in every 4 consecutive K
+    positions (one of the 6 position pairs, uniformly; seed tensor 5).
+    draw_kept(rng, n) returns n raw-bit values of a_type; exact zeros are
+    redrawn, so the non-zero positions are exactly the drawn pattern."""
+    if K % 4:
+        raise ValueError("K must be a multiple of 4")
+    G = K // 4
+    choice = _rng(workload, 5).integers(0, 6, size=(M, G))
+    pos = _PAIRS[choice]  # [M, G, 2], ascending
+    vr = _rng(workload, 1)
+    vals = draw_kept(vr, M * G * 2).reshape(M, G, 2)
+    mask = _NZ_MASK[a_type]
+    zero = (vals.view(np.uint16 if vals.itemsize == 2 else np.uint8) & mask) == 0
+    while zero.any():
+        vals[zero] = draw_kept(vr, int(zero.sum()))
+        zero = (vals.view(np.uint16 if vals.itemsize == 2 else np.uint8) & mask) == 0
+    A = np.zeros((M, G, 4), dtype=vals.dtype)
+    rows = np.arange(M)[:, None]
+    grps = np.arange(G)[None, :]
+    A[rows, grps, pos[..., 0]] = vals[..., 0]
+    A[rows, grps, pos[..., 1]] = vals[..., 1]
+    return A.reshape(M, K)
+
+
 def sparse24_f16(M=8192, N=8192, K=8192, workload=5):
     """Logical fp16 A with exactly two non-zeros in every 4 consecutive K
     positions (one of the 6 position pairs, uniformly), non-zero values
     uniform[-1,1] with exact zeros redrawn; B fp16 uniform[-1,1]; C fp32
     uniform[-1,1]; fp32 out.  A_logical is what the compressor receives."""
-    if K % 4:
-        raise ValueError("K must be a multiple of 4")
-    G = K // 4
-    pairs = np.array([(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)], dtype=np.int64)
-    choice = _rng(workload, 5).integers(0, 6, size=(M, G))
-    pos = pairs[choice]  # [M, G, 2], ascending
-    vr = _rng(workload, 1)
-    vals = to_f16(vr.uniform(-1.0, 1.0, size=(M, G, 2)))
-    zero = (vals & 0x7FFF) == 0
-    while zero.any():
-        vals[zero] = to_f16(vr.uniform(-1.0, 1.0, size=int(zero.sum())))
-        zero = (vals & 0x7FFF) == 0
-    A = np.zeros((M, G, 4), dtype=np.uint16)
-    rows = np.arange(M)[:, None]
-    grps = np.arange(G)[None, :]
-    A[rows, grps, pos[..., 0]] = vals[..., 0]
-    A[rows, grps, pos[..., 1]] = vals[..., 1]
-    A = A.reshape(M, K)
+    A = _scatter_24(M, K, workload, lambda r, n: to_f16(r.uniform(-1.0, 1.0, size=n)), "f16")
     B = to_f16(_rng(workload, 2).uniform(-1.0, 1.0, size=(N, K)))
     C = _rng(workload, 3).uniform(-1.0, 1.0, size=(M, N)).astype(np.float32)
     return Problem(M=M, N=N, K=K, a_type="f16", b_type="f16", d_type="f32", A=None, B=B, C=C,
                    bias=None, alpha=1.0, relu=False, A_logical=A)
+
+
+def sparse24_bf16(M=8192, N=8192, K=8192, workload=6, d_type="bf16"):
+    """The bf16 workload with A pruned 2:4: kept values normal(0,1)*sqrt(2/K)
+    (the same row variance as a dense normal(0,1)/sqrt(K) row), B
+    normal(0,1)/sqrt(K), C fp32 uniform[-1,1]; bf16 out."""
+    s = np.sqrt(2.0 / K) if K else 1.0
+    A = _scatter_24(M, K, workload,
+                    lambda r, n: to_bf16(r.standard_normal(size=n, dtype=np.float32) * s), "bf16")
+    B = to_bf16(_rng(workload, 2).standard_normal(size=(N, K), dtype=np.float32) /
+                np.sqrt(max(K, 1)))
+    C = _rng(workload, 3).uniform(-1.0, 1.0, size=(M, N)).astype(np.float32)
+    return Problem(M=M, N=N, K=K, a_type="bf16", b_type="bf16", d_type=d_type, A=None, B=B, C=C,
+                   bias=None, alpha=1.0, relu=False, A_logical=A)
+
+
+def sparse24_s8(M=8192, N=8192, K=8192, workload=7):
+    """s8 A pruned 2:4 with kept values uniform in [-128,127] minus 0, B
+    uniform in [-128,127]; C s32 uniform in [-2^20, 2^20]; s32 out."""
+    A = _scatter_24(M, K, workload, lambda r, n: r.integers(-128, 128, size=n, dtype=np.int8), "s8")
+    B = _rng(workload, 2).integers(-128, 128, size=(N, K), dtype=np.int8)
+    C = _rng(workload, 3).integers(-(1 << 20), (1 << 20) + 1, size=(M, N), dtype=np.int32)
+    return Problem(M=M, N=N, K=K, a_type="s8", b_type="s8", d_type="s32", A=None, B=B, C=C,
+                   bias=None, alpha=1.0, relu=False, A_logical=A)
+
+
+def sparse24_fp8(M=8192, N=8192, K=8192, workload=8, a_type="e4m3", b_type="e5m2"):
+    """The fp8 workload with A pruned 2:4: kept values normal(0,1) scaled by
+    sA = max/amax and rounded to a_type, B normal(0,1) scaled likewise to
+    b_type; no C; alpha = fp32(1/(sA*sB)); bias fp32 normal(0,1) [N];
+    out = relu(alpha*acc + bias[n]) as fp16."""
+    mx = {"e4m3": E4M3_MAX, "e5m2": E5M2_MAX}
+    enc = {"e4m3": to_e4m3, "e5m2": to_e5m2}
+    st = {}
+
+    def draw(r, n):
+        # sA is fixed by the first draw (all kept values); redraws of exact
+        # zeros reuse it
+        x = r.standard_normal(size=n, dtype=np.float32).astype(np.float64)
+        if "sA" not in st:
+            st["sA"] = mx[a_type] / max(np.abs(x).max(), 1e-30) if x.size else 1.0
+        return enc[a_type](np.clip(x * st["sA"], -mx[a_type], mx[a_type]))
+
+    A = _scatter_24(M, K, workload, draw, a_type)
+    sA = st.get("sA", 1.0)
+    b = _rng(workload, 2).standard_normal(size=(N, K), dtype=np.float32).astype(np.float64)
+    sB = mx[b_type] / max(np.abs(b).max(), 1e-30) if b.size else 1.0
+    B = enc[b_type](np.clip(b * sB, -mx[b_type], mx[b_type]))
+    bias = _rng(workload, 4).standard_normal(size=(N,)).astype(np.float32)
+    alpha = float(np.float32(1.0 / (sA * sB)))
+    return Problem(M=M, N=N, K=K, a_type=a_type, b_type=b_type, d_type="f16", A=None, B=B,
+                   C=None, bias=bias, alpha=alpha, relu=True, A_logical=A)
+
+
+def sparse24(a_type, M, N, K, **kw):
+    """The 2:4 problem of the given A type (f16, bf16, s8, e4m3, e5m2)."""
+    if a_type == "f16":
+        return sparse24_f16(M, N, K, **kw)
+    if a_type == "bf16":
+        return sparse24_bf16(M, N, K, **kw)
+    if a_type == "s8":
+        return sparse24_s8(M, N, K, **kw)
+    if a_type in ("e4m3", "e5m2"):
+        return sparse24_fp8(M, N, K, a_type=a_type, **kw)
+    raise ValueError(a_type)
 
 
 WORKLOADS = {
@@ -138,4 +217,7 @@ WORKLOADS = {
     "s8_8192": lambda: dense_s8(8192, 8192, 8192),
     "fp8_8192": lambda: dense_fp8(8192, 8192, 8192),
     "sparse24_f16_8192": lambda: sparse24_f16(8192, 8192, 8192),
+    "sparse24_bf16_8192": lambda: sparse24_bf16(8192, 8192, 8192),
+    "sparse24_s8_8192": lambda: sparse24_s8(8192, 8192, 8192),
+    "sparse24_fp8_8192": lambda: sparse24_fp8(8192, 8192, 8192),
 }
