@@ -95,8 +95,9 @@ typedef enum {
  *   differ): c_type F32, d_type F32 / F16 / BF16, any epilogue.
  *   a = b = S8: c_type S32, d_type S32, alpha == 1, no bias, no activation;
  *   the int32 sum wraps modulo 2^32 (no saturation).
- *   sparse_a = 1: a = b = F16, A row-major, K % 4 == 0; used with
- *   gemm_sparse24_run (A is then given in compressed form).
+ *   sparse_a = 1: any of the pairs above, A row-major and packed,
+ *   K % 4 == 0; used with gemm_sparse24_run (A is then given in compressed
+ *   form).
  * Epilogue, in fp32 for float outputs:  t = acc (+ C[m,n] if has_c);
  *   y = has_bias ? fmaf(alpha, t, bias[n]) : alpha * t;
  *   z = (act == RELU) ? (y > 0 ? y : +0) : y;  D = round-to-nearest-even(z).
@@ -143,30 +144,42 @@ gemm_status_t gemm_plan_describe(const gemm_plan_t *plan, char *buf, size_t len)
 gemm_status_t gemm_run(const gemm_plan_t *plan, const void *A, const void *B, const void *C,
                        const void *bias, void *D, gemm_stream_t stream);
 
-/* Bytes of the compressed form of an M x K fp16 A (K % 4 == 0):
- * values are M x K/2 fp16; metadata is M x ceil(K/32) uint32. */
+/* Bytes of the compressed form of an M x K A of type a_type (f16, bf16,
+ * fp8 E4M3/E5M2 or s8; K % 4 == 0): values are M x K/2 elements of a_type;
+ * metadata is M x ceil(K/32) uint32 whatever the type.  The sparse rows of
+ * the instruction tables on "NVIDIA MMA" (sections "Ampere: FP16/BF16 and
+ * integer MMA baseline" and "Ada: mma.sync adds FP8") give these types a
+ * 2:4 form. */
 gemm_status_t gemm_sparse24_sizes(int64_t M, int64_t K, int32_t a_type, size_t *values_bytes,
                                   size_t *meta_bytes);
 
-/* Compress a dense row-major M x K fp16 A (device) into the 2:4 form:
+/* Compress a dense row-major M x K A of type a_type (device) into the 2:4
+ * form:
  *   group g of row m covers K positions 4g .. 4g+3; its kept positions
  *   i0 < i1 (the non-zeros, filled up with the lowest free positions when a
  *   group has fewer than two) give
  *     values[m*(K/2) + 2g] = A[m, 4g+i0],  values[m*(K/2) + 2g+1] = A[m, 4g+i1]
  *   and the nibble (i0 | i1 << 2) at bits 4(g%8)..4(g%8)+3 of
  *   meta[m*ceil(K/32) + g/8]; unused high nibbles are 0.
- * +0 and -0 count as zero, NaN as non-zero.  Positions ascend, as the
+ * The zeros are +0 and -0 of the float types and 0 of s8 (whose 0x80 is
+ * -128); NaN and infinity count as non-zero.  Positions ascend, as the
  * ordered-metadata form on "NVIDIA MMA" (section "Ampere: FP16/BF16 and
  * integer MMA baseline") requires; the bit packing is this library's own.
  * Synchronises `stream` (a one-time weight preprocessing step) and returns
  * GEMM_ERR_NOT_SPARSE24 when some group holds more than two non-zeros
- * (values/meta are then unspecified).  A must be 8-byte aligned, values and
- * meta 4-byte aligned. */
+ * (values/meta are then unspecified).  A must be aligned to 4 elements,
+ * values to 2 elements and meta to 4 bytes (GEMM_ERR_MISALIGNED). */
 gemm_status_t gemm_sparse24_compress(int64_t M, int64_t K, int32_t a_type, const void *A,
                                      void *values, uint32_t *meta, gemm_stream_t stream);
 
 /* Enqueue D = epilogue(A*B + C) with A given as (values, meta) from
- * gemm_sparse24_compress.  The plan must have sparse_a == 1. */
+ * gemm_sparse24_compress.  The plan must have sparse_a == 1; its A/B types,
+ * accumulator and epilogue follow the dense rules (f16 x f16, bf16 x bf16,
+ * any fp8 pair -> fp32 accumulation; s8 x s8 -> s32).  The SMFMAC kernels
+ * need B column-major with 16-byte rows, K a multiple of 64 (16-bit types)
+ * or 128 (8-bit types), and 16-byte aligned values, meta and B; otherwise
+ * (also when only the alignment is missing at run time) the generic kernel
+ * runs. */
 gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, const uint32_t *meta,
                                 const void *B, const void *C, const void *bias, void *D,
                                 gemm_stream_t stream);

@@ -170,6 +170,38 @@ struct Op16S8 {
     }
 };
 
+// LE consecutive K elements (k0 ..) of one row or column of an operand read
+// element by element (any stride), zero past K or for a row outside the
+// matrix, packed into 32-bit words.
+template <int ELEM, int LE>
+__device__ STG_AI inline void load_frag_strided(uint32_t *out, const void *base, bool row_ok,
+                                         int64_t row_off, int64_t kstride, int64_t k0, int64_t K)
+{
+    if constexpr (ELEM == 2) {
+        const uint16_t *p = (const uint16_t *)base;
+#pragma unroll
+        for (int j = 0; j < LE; j += 2) {
+            uint32_t lo = 0, hi = 0;
+            if (row_ok && k0 + j < K)
+                lo = p[row_off + (k0 + j) * kstride];
+            if (row_ok && k0 + j + 1 < K)
+                hi = p[row_off + (k0 + j + 1) * kstride];
+            out[j / 2] = lo | (hi << 16);
+        }
+    } else {
+        const uint8_t *p = (const uint8_t *)base;
+#pragma unroll
+        for (int j = 0; j < LE; j += 4) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (row_ok && k0 + j + q < K)
+                    w |= (uint32_t)p[row_off + (k0 + j + q) * kstride] << (8 * q);
+            out[j / 4] = w;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- epilogue
 
 __device__ STG_AI inline uint16_t f32_to_f16_bits(float x)

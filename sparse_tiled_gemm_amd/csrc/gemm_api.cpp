@@ -257,8 +257,9 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
             return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16 or bf16");
     }
     if (d.sparse_a) {
-        if (d.a_type != GEMM_F16 || d.b_type != GEMM_F16)
-            return fail(GEMM_ERR_UNSUPPORTED, "2:4 sparse A supports f16 x f16 only");
+        // every supported pair has a 2:4 form (the A/B pairs above)
+        if (op_kind(d.a_type, d.b_type) < 0)
+            return fail(GEMM_ERR_UNSUPPORTED, "2:4 sparse A: unsupported A/B type pair");
         if (d.a_layout != GEMM_ROW_MAJOR)
             return fail(GEMM_ERR_UNSUPPORTED, "2:4 sparse A must be row-major");
         if (d.K % 4 != 0)
@@ -294,13 +295,16 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     p->fallback = KF_GENERIC;
 
     if (d.sparse_a) {
-        // 64-logical-K tiles; 32-bit buffer offsets cover 256 rows of values
-        // (K bytes each) and of B
-        const int64_t lim = (int64_t)1 << 30;
-        const bool fast = d.b_layout == GEMM_COL_MAJOR && d.K % 64 == 0 && d.ldb % 8 == 0 &&
-                          d.K * 256 < lim && d.ldb * 2 * 256 < lim;
+        // K tiles of two SMFMAC steps (64 logical K of a 16-bit type, 128 of
+        // an 8-bit type: 64 value bytes and 128 B bytes per row); 32-bit
+        // buffer offsets cover 256 rows of values and of B; 16-byte B rows
+        const int64_t eb = elem_bytes(d.a_type), lim = (int64_t)1 << 30;
+        const int64_t ktile = 128 / eb;
+        const bool fast = d.b_layout == GEMM_COL_MAJOR && d.K % ktile == 0 &&
+                          (d.ldb * eb) % 16 == 0 && d.K * eb / 2 * 256 < lim &&
+                          d.ldb * eb * 256 < lim;
         // the 8-wave kernel with direct copies measured fastest (2:4 f16,
-        // 8192^3); it takes K in whole groups of four 64-wide K tiles
+        // 8192^3); it takes K in whole metadata groups of 256 logical K
         const bool dma8 = fast && d.K % 256 == 0;
         const int tiled_fam = dma8 ? KF_SPARSE_DMA8 : KF_SPARSE_TILED;
         int fam = -1;
@@ -323,7 +327,7 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
         }
         p->family = fam;
         p->fallback = KF_SPARSE_GENERIC;
-        snprintf(p->name, sizeof p->name, "%s_f16", family_name(fam));
+        snprintf(p->name, sizeof p->name, "%s_%s", family_name(fam), op_name(p->op));
         *out = p;
         return ok();
     }
@@ -479,11 +483,11 @@ gemm_status_t gemm_sparse24_sizes(int64_t M, int64_t K, int32_t a_type, size_t *
         return fail(GEMM_ERR_NULL_POINTER, "output pointer is NULL");
     if (M < 0 || K < 0)
         return fail(GEMM_ERR_INVALID_VALUE, "negative size");
-    if (a_type != GEMM_F16)
-        return fail(GEMM_ERR_UNSUPPORTED, "2:4 compression supports f16 only");
+    if (a_type != GEMM_F16 && a_type != GEMM_BF16 && a_type != GEMM_S8 && !is_fp8(a_type))
+        return fail(GEMM_ERR_UNSUPPORTED, "2:4 compression takes f16, bf16, fp8 or s8");
     if (K % 4)
         return fail(GEMM_ERR_UNSUPPORTED, "K must be a multiple of 4");
-    *values_bytes = (size_t)M * (size_t)(K / 2) * 2;
+    *values_bytes = (size_t)M * (size_t)(K / 2) * (size_t)elem_bytes(a_type);
     *meta_bytes = (size_t)M * (size_t)((K + 31) / 32) * 4;
     return ok();
 }
@@ -499,8 +503,11 @@ gemm_status_t gemm_sparse24_compress(int64_t M, int64_t K, int32_t a_type, const
         return ok();
     if (!A || !values || !meta)
         return fail(GEMM_ERR_NULL_POINTER, "A, values or meta is NULL");
-    if (!aligned(A, 8) || !aligned(values, 4) || !aligned(meta, 4))
-        return fail(GEMM_ERR_MISALIGNED, "A must be 8-byte, values and meta 4-byte aligned");
+    // one load per group of four elements, one store per pair of values
+    const int eb = elem_bytes(a_type);
+    if (!aligned(A, 4 * eb) || !aligned(values, 2 * eb) || !aligned(meta, 4))
+        return fail(GEMM_ERR_MISALIGNED,
+                    "A must be aligned to 4 elements, values to 2 elements, meta to 4 bytes");
     int dev = 0;
     st = check_device(&dev, nullptr);
     if (st != GEMM_OK)
@@ -513,7 +520,8 @@ gemm_status_t gemm_sparse24_compress(int64_t M, int64_t K, int32_t a_type, const
     int host_flag = 0;
     e = hipMemsetAsync(flag, 0, sizeof(int), s);
     if (e == hipSuccess)
-        e = launch_sparse24_compress(M, K, (const uint16_t *)A, (uint16_t *)values, meta, flag, s);
+        e = launch_sparse24_compress(eb, eb == 2 ? 0x7FFFu : (a_type == GEMM_S8 ? 0xFFu : 0x7Fu),
+                                     M, K, A, values, meta, flag, s);
     if (e == hipSuccess)
         e = hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess)
@@ -546,10 +554,11 @@ gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, con
     gemm_status_t st = check_epilogue_ptrs(d, C, bias, D);
     if (st != GEMM_OK)
         return st;
-    if (d.K > 0 && (!aligned(values, 2) || !aligned(meta, 4) || !aligned(B, 2)))
+    const int eb = elem_bytes(d.a_type);
+    if (d.K > 0 && (!aligned(values, eb) || !aligned(meta, 4) || !aligned(B, eb)))
         return fail(GEMM_ERR_MISALIGNED, "values, meta or B not aligned to its element size");
     SparseArgs a;
-    a.values = (const uint16_t *)values;
+    a.values = values;
     a.meta = meta;
     a.B = B;
     a.K = d.K;
@@ -564,7 +573,7 @@ gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, con
     int fam = plan->family;
     if (fam != KF_SPARSE_GENERIC && (!aligned(values, 16) || !aligned(B, 16) || !aligned(meta, 16)))
         fam = plan->fallback;
-    hipError_t e = launch_sparse(fam, a, (hipStream_t)stream);
+    hipError_t e = launch_sparse(fam, plan->op, a, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "kernel launch");
     return ok();

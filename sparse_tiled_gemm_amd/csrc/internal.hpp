@@ -40,12 +40,14 @@ enum KernelFamily {
 };
 
 hipError_t launch_dense(int family, int op, const GemmArgs &g, hipStream_t s);
-hipError_t launch_sparse(int family, const SparseArgs &a, hipStream_t s);
-// Compressor: writes values/meta; *flag (device int, zeroed by the caller)
-// becomes 0x7fffffff - r for the lowest row r holding a group with more than
-// two non-zeros, and stays 0 otherwise.
-hipError_t launch_sparse24_compress(int64_t M, int64_t K, const uint16_t *A, uint16_t *values,
-                                    uint32_t *meta, int *flag, hipStream_t s);
+hipError_t launch_sparse(int family, int op, const SparseArgs &a, hipStream_t s);
+// Compressor for elements of elem_bytes (2 or 1) bytes, an element being a
+// zero when (bits & zero_mask) == 0: writes values/meta; *flag (device int,
+// zeroed by the caller) becomes 0x7fffffff - r for the lowest row r holding a
+// group with more than two non-zeros, and stays 0 otherwise.
+hipError_t launch_sparse24_compress(int elem_bytes, uint32_t zero_mask, int64_t M, int64_t K,
+                                    const void *A, void *values, uint32_t *meta, int *flag,
+                                    hipStream_t s);
 
 } // namespace stg
 

@@ -36,7 +36,7 @@ struct GemmArgs {
 
 // 2:4-compressed A: values [M, K/2] fp16, meta [M, ceil(K/32)] u32.
 struct SparseArgs {
-    const uint16_t *values;
+    const void *values; // kept A values (elements of A's type)
     const uint32_t *meta;
     const void *B; // element (k,n) at B[k*b_rs + n*b_cs]
     int64_t K;

@@ -52,20 +52,20 @@ def gpu_gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, *, alpha=1.0, relu=
     return h[: M * ld].reshape(M, ld)[:, :N].copy(), plan.name
 
 
-def gpu_compress(A_logical):
+def gpu_compress(A_logical, a_type="f16"):
     M, K = A_logical.shape
-    vb, mb = G.gemm_sparse24_sizes(M, K)
+    vb, mb = G.gemm_sparse24_sizes(M, K, a_type)
     tA = to_dev(A_logical)
     vals = torch.empty(max(vb, 16), dtype=torch.uint8, device="cuda")
     meta = torch.empty(max(mb, 16), dtype=torch.uint8, device="cuda")
-    G.gemm_sparse24_compress(M, K, "f16", tA, vals, meta)
+    G.gemm_sparse24_compress(M, K, a_type, tA, vals, meta)
     torch.cuda.synchronize()
     return vals, meta, vb, mb
 
 
 def gpu_sparse_gemm(vals, meta, B, C, M, N, K, d_type="f32", *, algo="auto", bias=None,
-                    alpha=1.0, relu=False, b_col=True):
-    desc = G.make_desc(M, N, K, "f16", "f16", d_type, has_c=C is not None,
+                    alpha=1.0, relu=False, b_col=True, a_type="f16", b_type=None):
+    desc = G.make_desc(M, N, K, a_type, b_type or a_type, d_type, has_c=C is not None,
                        has_bias=bias is not None, alpha=alpha, act="relu" if relu else "none",
                        b_layout="col" if b_col else "row", sparse_a=True, algo=algo)
     plan = G.gemm_plan(desc)

@@ -60,7 +60,12 @@ def _ok(**kw):
     (dict(d_type="s32"), G.GEMM_ERR_UNSUPPORTED),
     (dict(d_type="e4m3"), G.GEMM_ERR_UNSUPPORTED),
     (dict(c_type="bf16"), G.GEMM_ERR_UNSUPPORTED),
-    (dict(sparse_a=True), G.GEMM_ERR_UNSUPPORTED),     # sparse is f16 only
+    (dict(sparse_a=True), G.GEMM_OK),                  # 2:4 bf16
+    (dict(sparse_a=True, a_type="s8", b_type="s8", d_type="s32"), G.GEMM_OK),
+    (dict(sparse_a=True, a_type="e4m3", b_type="e5m2", d_type="f16"), G.GEMM_OK),
+    (dict(sparse_a=True, a_type="e5m2", b_type="e5m2", d_type="f32"), G.GEMM_OK),
+    (dict(sparse_a=True, a_type="f16", b_type="bf16", d_type="f32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(sparse_a=True, a_type="s8", b_type="s8", d_type="f32"), G.GEMM_ERR_UNSUPPORTED),
     (dict(sparse_a=True, a_type="f16", b_type="f16", K=66), G.GEMM_ERR_UNSUPPORTED),
     (dict(sparse_a=True, a_type="f16", b_type="f16", a_layout="col"), G.GEMM_ERR_UNSUPPORTED),
     (dict(sparse_a=True, a_type="f16", b_type="f16", d_type="f32"), G.GEMM_OK),
@@ -91,8 +96,13 @@ def test_sparse24_sizes():
     with pytest.raises(G.GemmError) as e:
         G.gemm_sparse24_sizes(4, 6)
     assert e.value.status == G.GEMM_ERR_UNSUPPORTED
-    with pytest.raises(G.GemmError):
-        G.gemm_sparse24_sizes(4, 8, "bf16")
+    # values are elements of A's type; the metadata does not depend on it
+    assert G.gemm_sparse24_sizes(4, 8, "bf16") == (4 * 4 * 2, 4 * 4)
+    for t in ("s8", "e4m3", "e5m2"):
+        assert G.gemm_sparse24_sizes(4, 40, t) == (4 * 20, 4 * 2 * 4)
+    with pytest.raises(G.GemmError) as e:
+        G.gemm_sparse24_sizes(4, 8, "f32")
+    assert e.value.status == G.GEMM_ERR_UNSUPPORTED
 
 
 def test_run_rejects_null_plan_without_gpu():
