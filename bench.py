@@ -25,7 +25,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # MI355X datasheet dense peaks (TFLOP/s or TOP/s) and HBM bandwidth (GB/s).
-PEAK = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "s8": 5033.2, "sparse_f16": 5033.2}
+# The 2:4 kinds are priced against twice the dense peak of their type (the
+# effective rate of a 2:4 product counts the dropped half of A's products).
+PEAK = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "s8": 5033.2, "sparse_f16": 5033.2,
+        "sparse_bf16": 5033.2, "sparse_fp8": 10066.4, "sparse_s8": 10066.4}
 HBM_GBS = 8000.0
 
 HEADLINE = "bf16_8192"
@@ -40,6 +43,9 @@ def _workloads():
         "s8_8192": (lambda: inputs.dense_s8(8192, 8192, 8192), "s8"),
         "fp8_8192": (lambda: inputs.dense_fp8(8192, 8192, 8192), "fp8"),
         "sparse24_f16_8192": (lambda: inputs.sparse24_f16(8192, 8192, 8192), "sparse_f16"),
+        "sparse24_bf16_8192": (lambda: inputs.sparse24_bf16(8192, 8192, 8192), "sparse_bf16"),
+        "sparse24_s8_8192": (lambda: inputs.sparse24_s8(8192, 8192, 8192), "sparse_s8"),
+        "sparse24_fp8_8192": (lambda: inputs.sparse24_fp8(8192, 8192, 8192), "sparse_fp8"),
     }
 
 
@@ -57,7 +63,7 @@ def algorithmic_bytes(p, sparse=False):
     M, N, K = p["M"], p["N"], p["K"]
     eb = G.ELEM_BYTES
     if sparse:
-        a = M * (K // 2) * 2 + M * ((K + 31) // 32) * 4
+        a = M * (K // 2) * eb[p["a_type"]] + M * ((K + 31) // 32) * 4
     else:
         a = M * K * eb[p["a_type"]]
     b = N * K * eb[p["b_type"]]
@@ -84,11 +90,11 @@ def run_workload(name, steps, warmup, rotate_b=1):
     tbias = _dev(p["bias"]) if p["bias"] is not None else None
     D = torch.empty(M * N * G.ELEM_BYTES[p["d_type"]], dtype=torch.uint8, device="cuda")
     if sparse:
-        vb, mb = G.gemm_sparse24_sizes(M, K)
+        vb, mb = G.gemm_sparse24_sizes(M, K, p["a_type"])
         tAl = _dev(p["A_logical"])
         vals = torch.empty(vb, dtype=torch.uint8, device="cuda")
         meta = torch.empty(mb, dtype=torch.uint8, device="cuda")
-        G.gemm_sparse24_compress(M, K, "f16", tAl, vals, meta)
+        G.gemm_sparse24_compress(M, K, p["a_type"], tAl, vals, meta)
         del tAl
 
         def call(i):
@@ -121,6 +127,7 @@ def run_workload(name, steps, warmup, rotate_b=1):
     out["algorithmic_bytes"] = byts
     out["GBps"] = byts / (ms * 1e-3) / 1e9
     if sparse:
+        # TOPS for s8 (the key names keep the float spelling)
         out["effective_TFLOPS"] = flops / (ms * 1e-3) / 1e12
         out["algorithmic_TFLOPS"] = flops / 2 / (ms * 1e-3) / 1e12
         out["frac_sparse_peak"] = out["effective_TFLOPS"] / PEAK[kind]
@@ -212,12 +219,12 @@ def main():
 
     head, p = run_workload(args.workload, args.steps, args.warmup)
     kind = _workloads()[args.workload][1]
-    unit = "TOPS" if kind == "s8" else "TFLOPS"
-    sparse = kind == "sparse_f16"
+    unit = "TOPS" if kind in ("s8", "sparse_s8") else "TFLOPS"
+    sparse = kind.startswith("sparse_")
     value = head["effective_TFLOPS"] if sparse else head[unit]
     achieved = value
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK[kind],
-                "unit": "TOP/s" if kind == "s8" else "TFLOP/s", "frac": achieved / PEAK[kind],
+                "unit": "TOP/s" if unit == "TOPS" else "TFLOP/s", "frac": achieved / PEAK[kind],
                 "traffic": measured_traffic(args.workload), "kernel": head["kernel"],
                 "algorithmic_flops_per_launch": 2.0 * p["M"] * p["N"] * p["K"]}
     result = {
@@ -232,7 +239,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "f16": "f16", "fp8": "fp8_e4m3xe5m2", "s8": "s8",
-                  "sparse_f16": "f16"}[kind],
+                  "sparse_f16": "f16", "sparse_bf16": "bf16", "sparse_fp8": "fp8_e4m3xe5m2",
+                  "sparse_s8": "s8"}[kind],
         "data": "synthetic",
         "config": {"workload": args.workload, "M": p["M"], "N": p["N"], "K": p["K"],
                    "a_type": p["a_type"], "b_type": p["b_type"], "d_type": p["d_type"],

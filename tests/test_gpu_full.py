@@ -164,3 +164,42 @@ def test_full_sparse24_8192(orc):
     pd["A"] = p["A_logical"]
     _check_samples(orc, pd, D, a_logical=p["A_logical"], seed=5)
     _float_colsum_check(pd, D, a_logical=p["A_logical"])
+
+
+@pytest.mark.parametrize("t", ["bf16", "s8", "e4m3"])
+def test_full_sparse24_types_8192(orc, t):
+    """2:4 A of the other types at 8192^3 through the plan the 8-wave SMFMAC
+    kernel serves: bf16 -> bf16 with C, s8 -> s32 with C, e4m3 x e5m2 ->
+    relu(alpha acc + bias) as fp16."""
+    say("workload 2:4", t, "8192^3")
+    p = inputs.sparse24(t, 8192, 8192, 8192)
+    M, K = 8192, 8192
+    vb, mb = G.gemm_sparse24_sizes(M, K, t)
+    vals = torch.empty(vb, dtype=torch.uint8, device="cuda")
+    meta = torch.empty(mb, dtype=torch.uint8, device="cuda")
+    G.gemm_sparse24_compress(M, K, t, to_dev(p["A_logical"]), vals, meta)
+    rv, rm = orc.sparse24_compress(p["A_logical"], t)
+    assert np.array_equal(vals.cpu().numpy().view(rv.dtype).reshape(rv.shape), rv)
+    assert np.array_equal(meta.cpu().numpy().view(np.uint32).reshape(rm.shape), rm)
+    say("  compressor bytes identical to the oracle's")
+    D, name = _run(p, sparse_dev=(vals, meta))
+    assert name.startswith("sparse24_dma8")
+    pd = dict(p)
+    pd["A"] = p["A_logical"]
+    _check_samples(orc, pd, D, a_logical=p["A_logical"], seed=6)
+    if t == "s8":
+        colA = p["A_logical"].astype(np.int64).sum(axis=0)
+        ref = p["B"].astype(np.int64) @ colA + p["C"].astype(np.int64).sum(axis=0)
+        got = D.astype(np.int64).sum(axis=0)
+        assert np.array_equal(np.mod(got, 2 ** 32), np.mod(ref, 2 ** 32))
+        say("  column sums exact")
+    elif t == "bf16":
+        _float_colsum_check(pd, D, a_logical=p["A_logical"])
+    else:
+        T, name32 = _run(p, d_type="f32", alpha=1.0, bias=False, relu=False,
+                         sparse_dev=(vals, meta))
+        assert name32.startswith("sparse24_dma8")
+        ref = orc.epilogue_f32(T, p["alpha"], p["bias"], True, "f16")
+        mism = int((D != ref).sum())
+        say("  fused epilogue mismatches:", mism)
+        assert mism == 0
