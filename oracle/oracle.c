@@ -69,9 +69,39 @@ static double dec_e5m2(uint8_t v)
     return s * ldexp((double)(4 + f), e - 17);
 }
 
+/* OCP MX element formats: sign, e exponent bits, f fraction bits, bias;
+ * exponent field 0 is subnormal (f/2^f_bits * 2^(1-bias)); no inf or NaN. */
+static double dec_mx(uint32_t v, int ebits, int fbits, int bias)
+{
+    double s = (v >> (ebits + fbits)) & 1u ? -1.0 : 1.0;
+    int e = (int)((v >> fbits) & ((1u << ebits) - 1u));
+    int f = (int)(v & ((1u << fbits) - 1u));
+    if (e == 0)
+        return s * ldexp((double)f, 1 - bias - fbits);
+    return s * ldexp((double)((1 << fbits) + f), e - bias - fbits);
+}
+
+/* element idx of a packed 6-bit row: bits 6 idx .. 6 idx + 5, little-endian */
+static uint32_t get6(const void *base, int64_t idx)
+{
+    const uint8_t *p = (const uint8_t *)base;
+    const int64_t bit = 6 * idx;
+    uint32_t w = p[bit / 8];
+    if ((bit % 8) > 2)
+        w |= (uint32_t)p[bit / 8 + 1] << 8;
+    return (w >> (bit % 8)) & 0x3Fu;
+}
+
 double oracle_decode(int type, const void *base, int64_t idx)
 {
     switch (type) {
+    case OR_E2M3: return dec_mx(get6(base, idx), 2, 3, 1);
+    case OR_E3M2: return dec_mx(get6(base, idx), 3, 2, 3);
+    case OR_E2M1: return dec_mx((((const uint8_t *)base)[idx / 2] >> (4 * (idx % 2))) & 0xFu, 2, 1, 1);
+    case OR_E8M0: {
+        uint8_t e = ((const uint8_t *)base)[idx];
+        return e == 0xFF ? NAN : ldexp(1.0, (int)e - 127);
+    }
     case OR_F16: return dec_f16(((const uint16_t *)base)[idx]);
     case OR_BF16: return dec_bf16(((const uint16_t *)base)[idx]);
     case OR_E4M3: return dec_e4m3(((const uint8_t *)base)[idx]);
@@ -346,6 +376,90 @@ int oracle_gemm_entries(const oracle_gemm_t *g, const void *A, const void *B, co
             }
         }
         finish(g, m, n, acc, sabs, C, bias, D_out, i, Y ? Y + i : NULL, S ? S + i : NULL);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ MX */
+
+static int is_mx_elem(int t)
+{
+    return t == OR_E4M3 || t == OR_E5M2 || t == OR_E2M3 || t == OR_E3M2 || t == OR_E2M1;
+}
+
+static int check_mx_desc(const oracle_gemm_t *g)
+{
+    if (g->M < 0 || g->N < 0 || g->K < 0 || g->K % 32)
+        return -1;
+    if (!is_mx_elem(g->a_type) || !is_mx_elem(g->b_type) || g->a_col_major || !g->b_col_major)
+        return -1;
+    if (g->c_type != OR_F32)
+        return -1;
+    if (g->d_type != OR_F32 && g->d_type != OR_F16 && g->d_type != OR_BF16)
+        return -1;
+    return 0;
+}
+
+/* One output of the block-scaled sum ("NVIDIA MMA", section "Blackwell:
+ * FP4/FP6 and block-scaled MMA"): for each K block g of 32, the block's sum
+ * of products, times 2^(SA-127) 2^(SB-127), added to the accumulator. */
+static void mx_dot(const oracle_gemm_t *g, const void *A, const uint8_t *SA, const void *B,
+                   const uint8_t *SB, int64_t m, int64_t n, double *acc_out, double *sabs_out)
+{
+    const int64_t KB = g->K / 32;
+    double acc = 0.0, sabs = 0.0;
+    for (int64_t blk = 0; blk < KB; ++blk) {
+        const double sa = oracle_decode(OR_E8M0, SA, m * KB + blk);
+        const double sb = oracle_decode(OR_E8M0, SB, n * KB + blk);
+        double part = 0.0, pabs = 0.0;
+        for (int64_t k = 32 * blk; k < 32 * blk + 32; ++k) {
+            const double p = oracle_decode(g->a_type, A, m * g->lda + k) *
+                             oracle_decode(g->b_type, B, n * g->ldb + k);
+            part += p;
+            pabs += fabs(p);
+        }
+        acc += sa * sb * part;
+        sabs += sa * sb * pabs;
+    }
+    *acc_out = acc;
+    *sabs_out = sabs;
+}
+
+int oracle_mx_gemm(const oracle_gemm_t *g, const void *A, const uint8_t *SA, const void *B,
+                   const uint8_t *SB, const void *C, const float *bias, void *D, double *Y,
+                   double *S)
+{
+    if (check_mx_desc(g))
+        return -1;
+    const int64_t M = g->M, N = g->N;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc, sabs;
+            mx_dot(g, A, SA, B, SB, m, n, &acc, &sabs);
+            const int64_t o = m * N + n;
+            finish(g, m, n, acc, sabs, C, bias, D, m * g->ldd + n, Y ? Y + o : NULL,
+                   S ? S + o : NULL);
+        }
+    return 0;
+}
+
+int oracle_mx_gemm_entries(const oracle_gemm_t *g, const void *A, const uint8_t *SA,
+                           const void *B, const uint8_t *SB, const void *C, const float *bias,
+                           int64_t n_entries, const int64_t *rows, const int64_t *cols,
+                           void *D_out, double *Y, double *S)
+{
+    if (check_mx_desc(g))
+        return -1;
+    for (int64_t i = 0; i < n_entries; ++i)
+        if (rows[i] < 0 || rows[i] >= g->M || cols[i] < 0 || cols[i] >= g->N)
+            return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < n_entries; ++i) {
+        double acc, sabs;
+        mx_dot(g, A, SA, B, SB, rows[i], cols[i], &acc, &sabs);
+        finish(g, rows[i], cols[i], acc, sabs, C, bias, D_out, i, Y ? Y + i : NULL,
+               S ? S + i : NULL);
     }
     return 0;
 }

@@ -31,7 +31,11 @@
  *   - bit formats: IEEE binary16; bfloat16 = the upper 16 bits of binary32;
  *     OCP FP8 E4M3 (bias 7, no infinity, 0x7F/0xFF NaN, max 448) and E5M2
  *     (bias 15, IEEE-like infinities, max 57344), the bare FP8 formats named
- *     in the precision tables of "NVIDIA MMA".
+ *     in the precision tables of "NVIDIA MMA"; for the block-scaled path the
+ *     OCP MX element formats E2M3 (bias 1, max 7.5), E3M2 (bias 3, max 28)
+ *     and E2M1 (bias 1, max 6), all without infinity or NaN, and the UE8M0
+ *     scale (2^(e-127), 0xFF NaN) - the formats the pages name, defined by
+ *     the OCP Microscaling specification.
  */
 #ifndef ORACLE_H
 #define ORACLE_H
@@ -50,7 +54,15 @@ enum {
     OR_E5M2 = 3,
     OR_S8 = 4,
     OR_F32 = 5,
-    OR_S32 = 6
+    OR_S32 = 6,
+    /* the narrow formats of the MX block-scaled path; stored packed along a
+     * row: E2M1 two to a byte (element i in bits 4(i%2) .. of byte i/2, the
+     * even element in the low nibble), E2M3 / E3M2 as a little-endian bit
+     * string (element i in bits 6i .. 6i+5, four elements in three bytes) */
+    OR_E2M3 = 7,
+    OR_E3M2 = 8,
+    OR_E2M1 = 9,
+    OR_E8M0 = 10 /* block scale: 2^(e - 127), 0xFF = NaN; one byte each */
 };
 
 typedef struct {
@@ -122,6 +134,28 @@ int64_t oracle_sparse24_compress(int type, int64_t M, int64_t K, const void *A, 
  * not ascending (i0 >= i1). */
 int oracle_sparse24_decompress(int type, int64_t M, int64_t K, const void *values,
                                const uint32_t *meta, void *A);
+
+/* MX block-scaled GEMM ("NVIDIA MMA", section "Blackwell: FP4/FP6 and
+ * block-scaled MMA": D = C + sum_g (A_g S_A,g)(B_g S_B,g), every scale applied
+ * to its K block's partial sum before that sum joins the accumulation; the
+ * "MXFP4 and NVFP4" table: UE8M0 scales, one per 32 K elements).  a_type and
+ * b_type are any of OR_E4M3, OR_E5M2, OR_E2M3, OR_E3M2, OR_E2M1 (they may
+ * differ); A row-major (element (m,k) at index m*lda + k of its packed
+ * storage), B column-major (element (k,n) at n*ldb + k); K % 32 == 0.
+ * SA[m*(K/32) + g] scales A's row m over K block g (K 32g .. 32g+31),
+ * SB[n*(K/32) + g] B's column n.  Block sums in fp64 (exact products),
+ * scaled by the exact powers of two, summed in block order; then C and the
+ * epilogue as in oracle_gemm.  Y/S as there, S = sum over k of the scaled
+ * |a b| plus |c|.  Returns 0, or -1 for an unsupported description. */
+int oracle_mx_gemm(const oracle_gemm_t *g, const void *A, const uint8_t *SA, const void *B,
+                   const uint8_t *SB, const void *C, const float *bias, void *D, double *Y,
+                   double *S);
+
+/* The same definition at chosen entries (rows[i], cols[i]) only. */
+int oracle_mx_gemm_entries(const oracle_gemm_t *g, const void *A, const uint8_t *SA,
+                           const void *B, const uint8_t *SB, const void *C, const float *bias,
+                           int64_t n_entries, const int64_t *rows, const int64_t *cols,
+                           void *D_out, double *Y, double *S);
 
 /* Threads the OpenMP loops use. */
 int oracle_num_threads(void);

@@ -12,7 +12,10 @@ import numpy as np
 
 from . import build as _build
 
-TYPES = {"f16": 0, "bf16": 1, "e4m3": 2, "e5m2": 3, "s8": 4, "f32": 5, "s32": 6}
+TYPES = {"f16": 0, "bf16": 1, "e4m3": 2, "e5m2": 3, "s8": 4, "f32": 5, "s32": 6,
+         "e2m3": 7, "e3m2": 8, "e2m1": 9, "e8m0": 10}
+# bits per element of the MX element formats (6- and 4-bit ones are stored packed)
+MX_BITS = {"e4m3": 8, "e5m2": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}
 STORAGE = {
     "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8, "e5m2": np.uint8,
     "s8": np.int8, "f32": np.float32, "s32": np.int32,
@@ -62,6 +65,11 @@ def lib():
         L.oracle_sparse24_compress.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp]
         L.oracle_sparse24_decompress.restype = ctypes.c_int
         L.oracle_sparse24_decompress.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp]
+        L.oracle_mx_gemm.restype = ctypes.c_int
+        L.oracle_mx_gemm.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, vp, dp, dp]
+        L.oracle_mx_gemm_entries.restype = ctypes.c_int
+        L.oracle_mx_gemm_entries.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, i64,
+                                             vp, vp, vp, dp, dp]
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -209,3 +217,70 @@ def sparse24_decompress(values, meta, M, K, type_name="f16"):
     if rc != 0:
         raise ValueError("metadata not ascending or bad shape")
     return A
+
+
+# ---------------------------------------------------------------- MX
+
+def decode_packed(type_name, packed, n):
+    """First n elements of a packed row-major byte array of an MX element
+    format (or e8m0 scales), decoded to float64."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1)
+    need = (n * MX_BITS.get(type_name, 8) + 7) // 8
+    if packed.size < need:
+        raise ValueError("packed array too short")
+    out = np.empty(n, dtype=np.float64)
+    lib().oracle_decode_array(TYPES[type_name], _ptr(packed), n, _ptr(out))
+    return out
+
+
+def _mx_args(A, SA, B, SB, C, bias, M, N, K, a_type, b_type, d_type, alpha, relu):
+    g = _desc(M, N, K, a_type, b_type, "f32", d_type, False, True, K, K, N, N, alpha,
+              C is not None, bias is not None, relu)
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    SA = np.ascontiguousarray(SA, dtype=np.uint8)
+    SB = np.ascontiguousarray(SB, dtype=np.uint8)
+    if A.size * 8 < M * K * MX_BITS[a_type] or B.size * 8 < N * K * MX_BITS[b_type]:
+        raise ValueError("A or B shorter than M*K / N*K packed elements")
+    if SA.size < M * (K // 32) or SB.size < N * (K // 32):
+        raise ValueError("scales shorter than M*K/32 / N*K/32")
+    if C is not None:
+        C = np.ascontiguousarray(C, dtype=np.float32)
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+    return g, A, SA, B, SB, C, bias
+
+
+def mx_gemm(A, SA, B, SB, C, bias, M, N, K, a_type, b_type, d_type, *, alpha=1.0, relu=False,
+            want_y=True, want_s=True):
+    """Block-scaled GEMM on packed operands: A [M, K] row-major and B stored
+    [N, K] (column-major K x N), each as bytes of packed elements; SA [M, K/32],
+    SB [N, K/32] E8M0 codes.  Returns (D_bits, Y, S) as gemm() does."""
+    g, A, SA, B, SB, C, bias = _mx_args(A, SA, B, SB, C, bias, M, N, K, a_type, b_type, d_type,
+                                        alpha, relu)
+    D = np.zeros((M, N), dtype=STORAGE[d_type])
+    Y = np.empty((M, N), dtype=np.float64) if want_y else None
+    S = np.empty((M, N), dtype=np.float64) if want_s else None
+    rc = lib().oracle_mx_gemm(ctypes.byref(g), _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(C),
+                              _ptr(bias), _ptr(D), _ptr(Y), _ptr(S))
+    if rc != 0:
+        raise ValueError("oracle_mx_gemm rejected the problem")
+    return D, Y, S
+
+
+def mx_gemm_entries(A, SA, B, SB, C, bias, M, N, K, a_type, b_type, d_type, rows, cols, *,
+                    alpha=1.0, relu=False):
+    g, A, SA, B, SB, C, bias = _mx_args(A, SA, B, SB, C, bias, M, N, K, a_type, b_type, d_type,
+                                        alpha, relu)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    n = rows.size
+    D = np.zeros(n, dtype=STORAGE[d_type])
+    Y = np.empty(n, dtype=np.float64)
+    S = np.empty(n, dtype=np.float64)
+    rc = lib().oracle_mx_gemm_entries(ctypes.byref(g), _ptr(A), _ptr(SA), _ptr(B), _ptr(SB),
+                                      _ptr(C), _ptr(bias), n, _ptr(rows), _ptr(cols), _ptr(D),
+                                      _ptr(Y), _ptr(S))
+    if rc != 0:
+        raise ValueError("oracle_mx_gemm_entries rejected the problem")
+    return D, Y, S

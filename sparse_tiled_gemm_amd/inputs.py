@@ -210,6 +210,96 @@ def sparse24(a_type, M, N, K, **kw):
     raise ValueError(a_type)
 
 
+# ---------------------------------------------------------------- MX block-scaled
+
+# OCP MX element formats: exponent bits, fraction bits, bias, and the exponent
+# of the largest normal value (the emax of the MX quantisation recipe)
+_MX_FMT = {"e4m3": (4, 3, 7, 8), "e5m2": (5, 2, 15, 15), "e2m3": (2, 3, 1, 2),
+           "e3m2": (3, 2, 3, 4), "e2m1": (2, 1, 1, 2)}
+MX_BITS = {"e4m3": 8, "e5m2": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}
+
+
+def _mx_grid(fmt):
+    """Non-negative finite values of an MX element format and their codes,
+    ascending (E4M3 without its NaN code, E5M2 without inf/NaN)."""
+    eb, fb, bias, _ = _MX_FMT[fmt]
+    vals, codes = [], []
+    for c in range(1 << (eb + fb)):
+        e, f = c >> fb, c & ((1 << fb) - 1)
+        if fmt == "e4m3" and c == 0x7F:
+            continue
+        if fmt == "e5m2" and e == 31:
+            continue
+        v = f * 2.0 ** (1 - bias - fb) if e == 0 else (1 + f / 2.0 ** fb) * 2.0 ** (e - bias)
+        vals.append(v)
+        codes.append(c)
+    order = np.argsort(vals)
+    return np.array(vals)[order], np.array(codes)[order]
+
+
+def mx_encode(x, fmt):
+    """Round to nearest (ties to the even code), saturating at the largest
+    finite value; returns codes (sign in the top bit of the format)."""
+    v, c = _mx_grid(fmt)
+    a = np.minimum(np.abs(np.asarray(x, dtype=np.float64)), v[-1])
+    i = np.clip(np.searchsorted(v, a), 1, len(v) - 1)
+    lo, hi = v[i - 1], v[i]
+    pick_hi = (a - lo > hi - a) | ((a - lo == hi - a) & (c[i] % 2 == 0))
+    code = np.where(pick_hi, c[i], c[i - 1])
+    sign = (np.signbit(x) & (code != 0)).astype(np.int64) << (MX_BITS[fmt] - 1)
+    return (code | sign).astype(np.uint8)
+
+
+def mx_quantize(x, fmt):
+    """The MX recipe along the last axis: per block of 32, shared exponent
+    floor(log2(amax)) - emax (E8M0 code = that + 127, clamped to 0..254),
+    elements = x / 2^shared rounded to the format.  Returns (codes, scales)."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, K = x.shape
+    xb = x.reshape(rows, K // 32, 32)
+    amax = np.abs(xb).max(-1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))), -127.0)
+    shared = np.clip(e - _MX_FMT[fmt][3], -127, 127)
+    codes = mx_encode(xb / np.ldexp(1.0, shared.astype(np.int64))[..., None], fmt)
+    return codes.reshape(rows, K), (shared + 127).astype(np.uint8)
+
+
+def mx_pack(codes, fmt):
+    """Pack [rows, K] codes along each row: 8-bit one per byte, E2M1 two per
+    byte (even element in the low nibble), 6-bit as a little-endian bit
+    string (element i in bits 6i .. 6i+5)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, K = codes.shape
+    b = MX_BITS[fmt]
+    if b == 8:
+        return codes.copy()
+    if b == 4:
+        c = codes.reshape(rows, K // 2, 2).astype(np.uint8)
+        return (c[..., 0] | (c[..., 1] << 4)).astype(np.uint8)
+    c = codes.reshape(rows, K // 4, 4).astype(np.uint32)
+    w = c[..., 0] | (c[..., 1] << 6) | (c[..., 2] << 12) | (c[..., 3] << 18)  # 24 bits
+    out = np.stack([w & 0xFF, (w >> 8) & 0xFF, (w >> 16) & 0xFF], axis=-1)
+    return out.reshape(rows, K // 4 * 3).astype(np.uint8)
+
+
+def mx_problem(M=8192, N=8192, K=8192, a_type="e4m3", b_type="e4m3", workload=9,
+               d_type="bf16"):
+    """A and B normal(0,1), each MX-quantised to its format per block of 32 K
+    (B along K of each column, i.e. rows of its stored [N, K] form); no C,
+    alpha 1, no bias, d_type out.  A, B are packed bytes; SA [M, K/32] and SB
+    [N, K/32] E8M0 codes."""
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    a = _rng(workload, 1).standard_normal(size=(M, K), dtype=np.float32)
+    b = _rng(workload, 2).standard_normal(size=(N, K), dtype=np.float32)
+    ca, SA = mx_quantize(a, a_type)
+    cb, SB = mx_quantize(b, b_type)
+    return Problem(M=M, N=N, K=K, a_type=a_type, b_type=b_type, d_type=d_type,
+                   A=mx_pack(ca, a_type), B=mx_pack(cb, b_type), SA=SA, SB=SB, C=None,
+                   bias=None, alpha=1.0, relu=False, mx=True)
+
+
 WORKLOADS = {
     "f16_128": lambda: dense_f16(128, 128, 128),
     "bf16_8192": lambda: dense_bf16(8192, 8192, 8192),
@@ -220,4 +310,7 @@ WORKLOADS = {
     "sparse24_bf16_8192": lambda: sparse24_bf16(8192, 8192, 8192),
     "sparse24_s8_8192": lambda: sparse24_s8(8192, 8192, 8192),
     "sparse24_fp8_8192": lambda: sparse24_fp8(8192, 8192, 8192),
+    "mxfp8_8192": lambda: mx_problem(8192, 8192, 8192, "e4m3", "e4m3", 9),
+    "mxfp6_8192": lambda: mx_problem(8192, 8192, 8192, "e2m3", "e2m3", 10),
+    "mxfp4_8192": lambda: mx_problem(8192, 8192, 8192, "e2m1", "e2m1", 11),
 }
