@@ -69,7 +69,12 @@ typedef enum {
     GEMM_F8_E5M2 = 4, /* OCP FP8 E5M2 (max 57344) */
     GEMM_S8 = 5,      /* int8, two's complement */
     GEMM_F32 = 6,     /* IEEE binary32 */
-    GEMM_S32 = 7      /* int32, two's complement */
+    GEMM_S32 = 7,     /* int32, two's complement */
+    /* OCP MX element formats, block-scaled GEMM only (block_scale = 32),
+     * stored packed along K: */
+    GEMM_F6_E2M3 = 8, /* bias 1, max 7.5, no inf/NaN; 4 elements in 3 bytes */
+    GEMM_F6_E3M2 = 9, /* bias 3, max 28, no inf/NaN; 4 elements in 3 bytes */
+    GEMM_F4_E2M1 = 10 /* bias 1, max 6, no inf/NaN; 2 elements per byte */
 } gemm_dtype_t;
 
 typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout_t;
@@ -98,6 +103,11 @@ typedef enum {
  *   sparse_a = 1: any of the pairs above, A row-major and packed,
  *   K % 4 == 0; used with gemm_sparse24_run (A is then given in compressed
  *   form).
+ *   block_scale = 32 (MX): a, b any of F8_E4M3, F8_E5M2, F6_E2M3, F6_E3M2,
+ *   F4_E2M1 (they may differ), A row-major, B column-major, K % 32 == 0,
+ *   rows of whole bytes (lda, ldb in elements); c_type F32, d_type F32 /
+ *   F16 / BF16, any epilogue; used with gemm_mx_run.  The 6- and 4-bit
+ *   formats exist only here.
  * Epilogue, in fp32 for float outputs:  t = acc (+ C[m,n] if has_c);
  *   y = has_bias ? fmaf(alpha, t, bias[n]) : alpha * t;
  *   z = (act == RELU) ? (y > 0 ? y : +0) : y;  D = round-to-nearest-even(z).
@@ -113,6 +123,7 @@ typedef struct {
     int32_t act;                            /* gemm_act_t */
     int32_t sparse_a;                       /* 1: 2:4-compressed A */
     int32_t algo;                           /* gemm_algo_t, normally AUTO */
+    int32_t block_scale;                    /* 0, or 32: MX block-scaled (gemm_mx_run) */
 } gemm_desc_t;
 
 typedef struct gemm_plan gemm_plan_t;
@@ -183,6 +194,27 @@ gemm_status_t gemm_sparse24_compress(int64_t M, int64_t K, int32_t a_type, const
 gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, const uint32_t *meta,
                                 const void *B, const void *C, const void *bias, void *D,
                                 gemm_stream_t stream);
+
+/* Enqueue the MX block-scaled product ("NVIDIA MMA", section "Blackwell:
+ * FP4/FP6 and block-scaled MMA"; UE8M0 scales per 32 K from the table in
+ * "MXFP4 and NVFP4"):
+ *     acc[m,n] = sum_g 2^(sa[m,g]-127) 2^(sb[n,g]-127) sum_{k in block g} A[m,k] B[k,n]
+ * over K blocks g = k / 32, each block's partial sum scaled before it joins
+ * the fp32 accumulation, then D = epilogue(acc + C) as for gemm_run.  The
+ * plan must have block_scale == 32.
+ *   A: row m at byte m*lda*bits/8, K elements packed from bit 0 up (8-bit:
+ *      one per byte; E2M1: two per byte, the even element in the low
+ *      nibble; 6-bit: element k in bits 6k .. 6k+5 of the row read as a
+ *      little-endian bit string).
+ *   B: stored N x K (column-major K x N), column n packed the same way.
+ *   scale_a: M x K/32 E8M0 bytes (row-major), 2^(e-127); scale_b: N x K/32.
+ *   A scale of 0xFF (NaN) gives an unspecified result.
+ * Device pointers; the fast kernel (pairs of one width: both 8-bit or both
+ * E2M1, K % 128 == 0, rows of whole 16 bytes) needs A and B 16-byte and
+ * the scales 4-byte aligned, else the generic kernel runs. */
+gemm_status_t gemm_mx_run(const gemm_plan_t *plan, const void *A, const uint8_t *scale_a,
+                          const void *B, const uint8_t *scale_b, const void *C, const void *bias,
+                          void *D, gemm_stream_t stream);
 
 /* Static text for a status code. */
 const char *gemm_status_string(gemm_status_t status);

@@ -73,8 +73,8 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 // mma(a, b, acc) on LANE_BYTES/4 packed 32-bit words per operand.
 
 struct OpF16 {
-    static constexpr int ELEM = 2, LANE_BYTES = 16, KB = 32;
-    static constexpr bool INT = false;
+    static constexpr int ELEM = 2, LANE_BYTES = 16, KB = 32, BITS = 16;
+    static constexpr bool INT = false, MX = false, SPLIT = false;
     typedef f16_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {
@@ -85,8 +85,8 @@ struct OpF16 {
 };
 
 struct OpBF16 {
-    static constexpr int ELEM = 2, LANE_BYTES = 16, KB = 32;
-    static constexpr bool INT = false;
+    static constexpr int ELEM = 2, LANE_BYTES = 16, KB = 32, BITS = 16;
+    static constexpr bool INT = false, MX = false, SPLIT = false;
     typedef f16_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {
@@ -100,8 +100,8 @@ struct OpBF16 {
 // 1 = E5M2, and both block scales are E8M0 127 (= 2^0), i.e. no scaling.
 template <int AFMT, int BFMT>
 struct OpF8 {
-    static constexpr int ELEM = 1, LANE_BYTES = 32, KB = 64;
-    static constexpr bool INT = false;
+    static constexpr int ELEM = 1, LANE_BYTES = 32, KB = 64, BITS = 8;
+    static constexpr bool INT = false, MX = false, SPLIT = false;
     typedef f16_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {
@@ -113,14 +113,62 @@ struct OpF8 {
 };
 
 struct OpS8 {
-    static constexpr int ELEM = 1, LANE_BYTES = 16, KB = 32;
-    static constexpr bool INT = true;
+    static constexpr int ELEM = 1, LANE_BYTES = 16, KB = 32, BITS = 8;
+    static constexpr bool INT = true, MX = false, SPLIT = false;
     typedef i16_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {
         i4_t va = *(const i4_t *)a;
         i4_t vb = *(const i4_t *)b;
         return __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb, c, 0, 0, 0);
+    }
+};
+
+// x >> s as an instruction the compiler neither moves nor folds (a volatile
+// asm stays after the barriers and memory operations before it)
+__device__ STG_AI inline uint32_t shr_opaque(uint32_t x, int s)
+{
+    uint32_t r;
+    asm volatile("v_lshrrev_b32 %0, %1, %2" : "=v"(r) : "v"(s), "v"(x));
+    return r;
+}
+
+// MX block-scaled product of OCP MX element formats (AF / BF: 0 = E4M3, 1 =
+// E5M2, 2 = E2M3, 3 = E3M2, 4 = E2M1, the selectors of the gfx950
+// v_mfma_scale_f32_32x32x64_f8f6f4) with one E8M0 scale per 32 K of every A
+// row and B column.  The tiled kernel takes pairs of one width: both 8-bit or
+// both 4-bit (BITS).  Lane layouts (measured with single-instruction probes):
+//  - 8-bit operands: lane l (h = l / 32) gives bytes 0..15 = K 16h .. 16h+15
+//    and bytes 16..31 = K 32+16h .. 32+16h+15 of row / column l % 32 (so
+//    K block b of the instruction is bytes 16b .. 16b+15 of both lane
+//    halves; in LDS: 16-byte chunks h and h+2 of the step's 64 bytes);
+//  - 6- and 4-bit operands: lane half h gives K 32h .. 32h+31, packed from
+//    bit 0 up (4-bit: the even element in the low nibble);
+//  - the scale VGPR of lane half b holds (in the byte the instruction's
+//    op_sel picks) the scale of the lane's row / column over K block b.
+template <int AF, int BF>
+struct OpMX {
+    static constexpr int BITS = AF <= 1 ? 8 : (AF == 4 ? 4 : 6);
+    static_assert((BF <= 1 ? 8 : (BF == 4 ? 4 : 6)) == BITS, "one width for A and B");
+    static constexpr int ELEM = 1; // (unused: MX addressing is by BITS)
+    static constexpr int LANE_BYTES = 32 * BITS / 8; // one 32-K block per lane
+    static constexpr int KB = 2 * LANE_BYTES;        // row bytes per instruction (64 K)
+    static constexpr bool INT = false, MX = true;
+    static constexpr bool SPLIT = BITS == 8; // chunk h and h+2 instead of 2h, 2h+1
+    typedef f16_t acc_t;
+    // SEL: byte of sa / sb holding this instruction's scales
+    template <int SEL>
+    __device__ static STG_AI acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c, uint32_t sa,
+                                      uint32_t sb)
+    {
+        i8_t va = {}, vb = {};
+#pragma unroll
+        for (int i = 0; i < LANE_BYTES / 4; ++i) {
+            va[i] = (int)a[i];
+            vb[i] = (int)b[i];
+        }
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, c, AF, BF, SEL, (int)sa, SEL,
+                                                               (int)sb);
     }
 };
 

@@ -39,6 +39,24 @@ gemm_status_t hip_fail(hipError_t e, const char *what)
 }
 
 bool is_fp8(int t) { return t == GEMM_F8_E4M3 || t == GEMM_F8_E5M2; }
+// MX element formats: their bits and the scaled MFMA's format selector
+bool is_mx_elem(int t) { return is_fp8(t) || t == GEMM_F6_E2M3 || t == GEMM_F6_E3M2 || t == GEMM_F4_E2M1; }
+int mx_bits(int t) { return is_fp8(t) ? 8 : (t == GEMM_F4_E2M1 ? 4 : 6); }
+int mx_sel(int t)
+{
+    switch (t) {
+    case GEMM_F8_E4M3: return 0;
+    case GEMM_F8_E5M2: return 1;
+    case GEMM_F6_E2M3: return 2;
+    case GEMM_F6_E3M2: return 3;
+    default: return 4;
+    }
+}
+const char *mx_name(int sel)
+{
+    static const char *n[] = {"e4m3", "e5m2", "e2m3", "e3m2", "e2m1"};
+    return sel >= 0 && sel < 5 ? n[sel] : "?";
+}
 bool is_float_in(int t) { return t == GEMM_F16 || t == GEMM_BF16 || is_fp8(t); }
 int elem_bytes(int t)
 {
@@ -167,6 +185,8 @@ const char *family_name(int f)
     case KF_TILED_256W8T: return "tiled256w8t";
     case KF_PINGPONG4: return "pingpong4";
     case KF_PINGPONG5: return "pingpong5";
+    case KF_MX_GENERIC: return "mx_generic";
+    case KF_MX_TILED: return "mx_tiled";
     default: return "?";
     }
 }
@@ -217,7 +237,7 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
     if (d.M < 0 || d.N < 0 || d.K < 0)
         return fail(GEMM_ERR_INVALID_VALUE, "negative size M=%lld N=%lld K=%lld",
                     (long long)d.M, (long long)d.N, (long long)d.K);
-    auto dtype_ok = [](int t) { return t >= GEMM_F16 && t <= GEMM_S32; };
+    auto dtype_ok = [](int t) { return t >= GEMM_F16 && t <= GEMM_F4_E2M1; };
     if (!dtype_ok(d.a_type) || !dtype_ok(d.b_type) || !dtype_ok(d.d_type) ||
         !(d.c_type == 0 || dtype_ok(d.c_type)))
         return fail(GEMM_ERR_INVALID_VALUE, "unknown dtype code");
@@ -235,6 +255,34 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
         return fail(GEMM_ERR_INVALID_VALUE, "negative leading dimension");
     if (!normalise(d))
         return fail(GEMM_ERR_INVALID_VALUE, "leading dimension smaller than the matrix extent");
+    if (d.block_scale != 0 && d.block_scale != 32)
+        return fail(GEMM_ERR_INVALID_VALUE, "block_scale must be 0 or 32");
+
+    if (d.block_scale == 32) {
+        // MX block-scaled ("NVIDIA MMA", section "Blackwell: FP4/FP6 and
+        // block-scaled MMA"): any two MX element formats, fp32 accumulation
+        if (!is_mx_elem(d.a_type) || !is_mx_elem(d.b_type))
+            return fail(GEMM_ERR_UNSUPPORTED,
+                        "block-scaled A/B must be e4m3, e5m2, e2m3, e3m2 or e2m1");
+        if (d.sparse_a)
+            return fail(GEMM_ERR_UNSUPPORTED, "block-scaled A cannot be 2:4 sparse");
+        if (d.a_layout != GEMM_ROW_MAJOR || d.b_layout != GEMM_COL_MAJOR)
+            return fail(GEMM_ERR_UNSUPPORTED,
+                        "block-scaled operands are K-contiguous: A row-major, B column-major");
+        if (d.K % 32)
+            return fail(GEMM_ERR_UNSUPPORTED, "block-scaled K must be a multiple of 32");
+        if ((d.lda * mx_bits(d.a_type)) % 8 || (d.ldb * mx_bits(d.b_type)) % 8)
+            return fail(GEMM_ERR_UNSUPPORTED, "packed rows must be whole bytes");
+        if (!(d.c_type == GEMM_F32 || (d.c_type == 0 && !d.has_c)))
+            return fail(GEMM_ERR_UNSUPPORTED, "float inputs take an f32 C");
+        if (d.d_type != GEMM_F32 && d.d_type != GEMM_F16 && d.d_type != GEMM_BF16)
+            return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16 or bf16");
+        return ok();
+    }
+    if (d.a_type > GEMM_S32 || d.b_type > GEMM_S32)
+        return fail(GEMM_ERR_UNSUPPORTED, "6- and 4-bit formats need block_scale = 32");
+    if (d.d_type > GEMM_S32 || d.c_type > GEMM_S32)
+        return fail(GEMM_ERR_UNSUPPORTED, "unsupported C or D type");
 
     if (d.a_type == GEMM_S8 || d.b_type == GEMM_S8) {
         if (d.a_type != GEMM_S8 || d.b_type != GEMM_S8)
@@ -293,6 +341,41 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     p->device = dev;
     p->op = op_kind(d.a_type, d.b_type);
     p->fallback = KF_GENERIC;
+
+    if (d.block_scale) {
+        const int ab = mx_bits(d.a_type), bb = mx_bits(d.b_type);
+        const int64_t lim = (int64_t)1 << 30, rowa = d.lda * ab / 8, rowb = d.ldb * bb / 8;
+        // the 4-wave 256 x 256 kernel: one width (8 or 4 bits), whole words of
+        // four scales (K % 128), 16-byte rows, 32-bit offsets over 256 rows
+        const bool fast = ab == bb && ab != 6 && d.K % 128 == 0 && rowa % 16 == 0 &&
+                          rowb % 16 == 0 && rowa * 256 < lim && rowb * 256 < lim &&
+                          (d.K / 32) * 256 < lim;
+        int fam = -1;
+        switch (d.algo) {
+        case GEMM_ALGO_AUTO: fam = fast ? KF_MX_TILED : KF_MX_GENERIC; break;
+        case GEMM_ALGO_TILED:
+        case GEMM_ALGO_TILED_256: fam = fast ? KF_MX_TILED : -1; break;
+        case GEMM_ALGO_GENERIC: fam = KF_MX_GENERIC; break;
+        default: fam = -1;
+        }
+        if (fam < 0) {
+            delete p;
+            return fail(GEMM_ERR_UNSUPPORTED, "requested algorithm cannot serve this MX problem");
+        }
+        if (const char *force = getenv("STGEMM_FORCE_KERNEL")) { // tuning override
+            if (strcmp(force, family_name(KF_MX_GENERIC)) == 0)
+                fam = KF_MX_GENERIC;
+            if (strcmp(force, family_name(KF_MX_TILED)) == 0 && fast)
+                fam = KF_MX_TILED;
+        }
+        p->op = mx_sel(d.a_type) * 8 + mx_sel(d.b_type);
+        p->family = fam;
+        p->fallback = KF_MX_GENERIC;
+        snprintf(p->name, sizeof p->name, "%s_%sx%s", family_name(fam), mx_name(mx_sel(d.a_type)),
+                 mx_name(mx_sel(d.b_type)));
+        *out = p;
+        return ok();
+    }
 
     if (d.sparse_a) {
         // K tiles of two SMFMAC steps (64 logical K of a 16-bit type, 128 of
@@ -436,6 +519,8 @@ gemm_status_t gemm_run(const gemm_plan_t *plan, const void *A, const void *B, co
     const gemm_desc_t &d = plan->d;
     if (d.sparse_a)
         return fail(GEMM_ERR_UNSUPPORTED, "plan is for 2:4 sparse A: use gemm_sparse24_run");
+    if (d.block_scale)
+        return fail(GEMM_ERR_UNSUPPORTED, "plan is block-scaled: use gemm_mx_run");
     if (d.M == 0 || d.N == 0)
         return ok();
     if (d.K > 0 && (!A || !B))
@@ -466,6 +551,7 @@ gemm_status_t gemm_run(const gemm_plan_t *plan, const void *A, const void *B, co
         g.b_cs = 1;
     }
     g.e = make_epi(d, C, bias, D);
+    g.sa = g.sb = nullptr;
 
     int fam = plan->family;
     if (fam != KF_GENERIC && (!aligned(A, 16) || !aligned(B, 16)))
@@ -574,6 +660,43 @@ gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, con
     if (fam != KF_SPARSE_GENERIC && (!aligned(values, 16) || !aligned(B, 16) || !aligned(meta, 16)))
         fam = plan->fallback;
     hipError_t e = launch_sparse(fam, plan->op, a, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "kernel launch");
+    return ok();
+}
+
+gemm_status_t gemm_mx_run(const gemm_plan_t *plan, const void *A, const uint8_t *scale_a,
+                          const void *B, const uint8_t *scale_b, const void *C, const void *bias,
+                          void *D, gemm_stream_t stream)
+{
+    if (!plan)
+        return fail(GEMM_ERR_NULL_POINTER, "plan is NULL");
+    const gemm_desc_t &d = plan->d;
+    if (!d.block_scale)
+        return fail(GEMM_ERR_UNSUPPORTED, "plan is not block-scaled: use gemm_run");
+    if (d.M == 0 || d.N == 0)
+        return ok();
+    if (d.K > 0 && (!A || !B || !scale_a || !scale_b))
+        return fail(GEMM_ERR_NULL_POINTER, "A, B or a scale array is NULL");
+    gemm_status_t st = check_epilogue_ptrs(d, C, bias, D);
+    if (st != GEMM_OK)
+        return st;
+    GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.K = d.K;
+    g.a_rs = d.lda;
+    g.a_cs = 1;
+    g.b_rs = 1;
+    g.b_cs = d.ldb;
+    g.e = make_epi(d, C, bias, D);
+    g.sa = scale_a;
+    g.sb = scale_b;
+    int fam = plan->family;
+    if (fam == KF_MX_TILED &&
+        (!aligned(A, 16) || !aligned(B, 16) || !aligned(scale_a, 4) || !aligned(scale_b, 4)))
+        fam = plan->fallback;
+    hipError_t e = launch_mx(fam, plan->op / 8, plan->op % 8, g, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "kernel launch");
     return ok();

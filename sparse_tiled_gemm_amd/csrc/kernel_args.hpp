@@ -32,6 +32,9 @@ struct GemmArgs {
     int64_t a_rs, a_cs;
     int64_t b_rs, b_cs;
     EpiArgs e;
+    // MX block scales (E8M0, one per 32 K): sa[m*(K/32) + g] for row m of A,
+    // sb[n*(K/32) + g] for column n of B; nullptr outside the MX path
+    const uint8_t *sa, *sb;
 };
 
 // 2:4-compressed A: values [M, K/2] fp16, meta [M, ceil(K/32)] u32.

@@ -93,8 +93,8 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int64_t m_blk = (int64_t)tm * BM, n_blk = (int64_t)tn * BN;
-    const int64_t lda_b = g.a_rs * OP::ELEM, ldb_b = g.b_cs * OP::ELEM;
-    const int64_t kbytes = g.K * OP::ELEM;
+    const int64_t lda_b = g.a_rs * OP::BITS / 8, ldb_b = g.b_cs * OP::BITS / 8;
+    const int64_t kbytes = g.K * OP::BITS / 8;
     const int KT = (int)(kbytes / BKB);
     // bounded by the last byte of the last row: loads past it return zero
     const __amdgpu_buffer_rsrc_t ra = tile_rsrc((const uint8_t *)g.A + m_blk * lda_b,
@@ -143,10 +143,15 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         constexpr int S = decltype(set)::value;
         const uint8_t *lsa = stage_base + a_off;
         const uint8_t *lsb = stage_base + b_off;
+        // 16-byte chunks of the step's slice: consecutive ones per lane half,
+        // or chunks h and h+2 for the 8-bit MX layout (whose K blocks are the
+        // two 16-byte halves of both lanes' operands)
         const int c0 = (s * OP::KB + half * OP::LANE_BYTES) >> 4;
+        constexpr bool split = OP::MX && OP::SPLIT;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const int oa = ((c0 + v) ^ sa) << 4, ob = ((c0 + v) ^ sb) << 4;
+            const int c = split ? (s * OP::KB >> 4) + half + 2 * v : c0 + v;
+            const int oa = (c ^ sa) << 4, ob = (c ^ sb) << 4;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
                 *(u4_t *)&fa[S][i][4 * v] = *(const u4_t *)(lsa + i * 32 * BKB + oa);
@@ -156,25 +161,79 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         }
     };
 
+    // MX block scales: per fragment row / column one 32-bit word of four
+    // consecutive K blocks (128 K), loaded for tile t+1 while tile t runs and
+    // shifted by 8h so that byte 2c of lane half h is block 2c + h
+    constexpr int KPT = BKB * 8 / OP::BITS;   // K per tile
+    constexpr int NSW = OP::MX ? FM + FN : 0; // scale words per lane
+    uint32_t scl[2][NSW > 0 ? NSW : 1];
+    const int64_t kblk = g.K / 32; // scale bytes per row
+    // (not used outside MX, where the compiler drops them)
+    const __amdgpu_buffer_rsrc_t rsa = tile_rsrc(g.sa + m_blk * kblk, (g.e.M - m_blk) * kblk);
+    const __amdgpu_buffer_rsrc_t rsb = tile_rsrc(g.sb + n_blk * kblk, (g.e.N - n_blk) * kblk);
+    auto sload = [&](auto set, int kt) STG_AI {
+        if constexpr (OP::MX) {
+            constexpr int S = decltype(set)::value;
+            const int q = kt * KPT / 128; // the word holding tile kt's blocks
+            const int arow0 = (wave / GN) * (BM / GM) + (tid & 31);
+            const int brow0 = (wave % GN) * (BN / GN) + (tid & 31);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                scl[S][i] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rsa, (arow0 + 32 * i) * (int)kblk + 4 * q, 0, 0);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                scl[S][FM + j] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rsb, (brow0 + 32 * j) * (int)kblk + 4 * q, 0, 0);
+        }
+    };
+
     typename OP::acc_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             acc[i][j] = typename OP::acc_t{};
-    auto mma = [&](auto set) STG_AI {
+    // the current tile's scale words shifted by 8h, computed at the start of
+    // the tile that uses them: an opaque shift, so the compiler cannot hoist
+    // it up to the load (which would make it wait for every load in flight)
+    uint32_t ssh[NSW > 0 ? NSW : 1];
+    auto sshift = [&](auto set) STG_AI {
+        if constexpr (OP::MX) {
+            constexpr int S = decltype(set)::value;
+            const int hs = 8 * (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < NSW; ++i)
+                ssh[i] = shr_opaque(scl[S][i], hs);
+        }
+    };
+    // fragment set F; for MX also the tile's parity P and step S
+    auto mma = [&](auto set, auto pset, auto step) STG_AI {
         constexpr int S = decltype(set)::value;
+        if constexpr (OP::MX) {
+            constexpr int P = decltype(pset)::value, ST = decltype(step)::value;
+            // byte of the shifted word: block (t KPT + 64 ST) / 32 mod 4, minus h
+            constexpr int SEL = (KPT == 64 ? 2 * P : 2 * ST) & 3;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = OP::mma(fa[S][i], fb[S][j], acc[i][j]);
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = OP::template mma<SEL>(fa[S][i], fb[S][j], acc[i][j], ssh[i],
+                                                      ssh[FM + j]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = OP::mma(fa[S][i], fb[S][j], acc[i][j]);
+        }
     };
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
 
     // prologue: tiles 0 and 1 in LDS stages 0 and 1, tile 2 in registers set 0
+    sload(I0{}, 0);
     gload(I0{}, 0);
     gload(I1{}, 1);
     lstore(I0{}, lds);
@@ -193,7 +252,7 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     // every VM_EVERY MFMAs, a store half-way between), so neither the vector
     // memory pipe (64 B/clk per CU) nor the LDS write path (about half the
     // LDS read rate) backs up and stalls MFMA issue.
-    constexpr int NM = FM * FN, NR = (FM + FN) * NV, NL = A_LD + B_LD;
+    constexpr int NM = FM * FN, NR = (FM + FN) * NV, NL = A_LD + B_LD + NSW;
     constexpr int NMT = KS * NM;
     auto schedule = [&]() STG_AI {
         [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
@@ -224,6 +283,10 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         // `wr`; restrict lets the scheduler interleave the stores with reads
         auto body = [&](const uint8_t *__restrict__ cur, const uint8_t *__restrict__ nxt,
                         uint8_t *__restrict__ wr) STG_AI {
+            // this tile's scales, then the next tile's scales before the tile
+            // loads: waiting for them must not wait for the loads after them
+            sshift(std::integral_constant<int, P>{});
+            sload(std::integral_constant<int, P ^ 1>{}, t + 1);
             gload(std::integral_constant<int, P ^ 1>{}, t + 3);
             [&]<int... S>(std::integer_sequence<int, S...>) STG_AI {
                 (
@@ -233,7 +296,8 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
                             lread(std::integral_constant<int, F ^ 1>{}, cur, S + 1);
                         else
                             lread(std::integral_constant<int, F ^ 1>{}, nxt, 0);
-                        mma(std::integral_constant<int, F>{});
+                        mma(std::integral_constant<int, F>{}, std::integral_constant<int, P>{},
+                            std::integral_constant<int, S>{});
                     }(),
                     ...);
             }(std::make_integer_sequence<int, KS>{});
@@ -998,6 +1062,29 @@ static dense_launch_fn dma_table_t(int op)
     case OPK_F8_E5E5: return launch_dma_t<OpF8<1, 1>, BM, BN, NS>;
     case OPK_S8: return launch_dma_t<OpS8, BM, BN, NS>;
     default: return nullptr;
+    }
+}
+
+// MX block-scaled pairs of one width on the 4-wave 256x256 tile (the fp8
+// choice); afmt / bfmt are the OpMX selectors.
+template <class OP>
+static hipError_t launch_mx_tiled_t(const GemmArgs &g, hipStream_t s)
+{
+    const int tiles_m = (int)((g.e.M + 255) / 256), tiles_n = (int)((g.e.N + 255) / 256);
+    hipLaunchKernelGGL((k_tiled<OP, 256, 256>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
+                       s, g, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_tiled(int afmt, int bfmt, const GemmArgs &g, hipStream_t s)
+{
+    switch (afmt * 8 + bfmt) {
+    case 0 * 8 + 0: return launch_mx_tiled_t<OpMX<0, 0>>(g, s);
+    case 0 * 8 + 1: return launch_mx_tiled_t<OpMX<0, 1>>(g, s);
+    case 1 * 8 + 0: return launch_mx_tiled_t<OpMX<1, 0>>(g, s);
+    case 1 * 8 + 1: return launch_mx_tiled_t<OpMX<1, 1>>(g, s);
+    case 4 * 8 + 4: return launch_mx_tiled_t<OpMX<4, 4>>(g, s);
+    default: return hipErrorInvalidValue;
     }
 }
 

@@ -5,7 +5,7 @@ addresses; PyTorch provides memory and streams only.
 
 The functions carry the C names: gemm_validate_desc, gemm_plan,
 gemm_plan_destroy, gemm_plan_describe, gemm_run, gemm_sparse24_sizes,
-gemm_sparse24_compress, gemm_sparse24_run, gemm_status_string,
+gemm_sparse24_compress, gemm_sparse24_run, gemm_mx_run, gemm_status_string,
 gemm_last_error.  Non-OK statuses raise GemmError (except
 gemm_validate_desc, which returns the status).
 """
@@ -26,7 +26,8 @@ GEMM_ERR_DEVICE = 6
 GEMM_ERR_HIP = 7
 
 # gemm_dtype_t
-DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "e5m2": 4, "s8": 5, "f32": 6, "s32": 7}
+DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "e5m2": 4, "s8": 5, "f32": 6, "s32": 7,
+          "e2m3": 8, "e3m2": 9, "e2m1": 10}
 ROW_MAJOR, COL_MAJOR = 0, 1
 ACT_NONE, ACT_RELU = 0, 1
 # gemm_algo_t
@@ -52,6 +53,7 @@ class gemm_desc_t(ctypes.Structure):
         ("alpha", ctypes.c_float),
         ("has_c", ctypes.c_int32), ("has_bias", ctypes.c_int32), ("act", ctypes.c_int32),
         ("sparse_a", ctypes.c_int32), ("algo", ctypes.c_int32),
+        ("block_scale", ctypes.c_int32),
     ]
 
 
@@ -76,6 +78,7 @@ def load():
         "gemm_plan_destroy": (st, [vp]),
         "gemm_plan_describe": (st, [vp, ctypes.c_char_p, ctypes.c_size_t]),
         "gemm_run": (st, [vp, vp, vp, vp, vp, vp, vp]),
+        "gemm_mx_run": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "gemm_sparse24_sizes": (st, [i64, i64, i32, ctypes.POINTER(ctypes.c_size_t),
                                      ctypes.POINTER(ctypes.c_size_t)]),
         "gemm_sparse24_compress": (st, [i64, i64, i32, vp, vp, vp, vp]),
@@ -130,7 +133,7 @@ def _stream(stream):
 
 def make_desc(M, N, K, a_type, b_type, d_type, *, c_type=None, has_c=True, has_bias=False,
               alpha=1.0, act="none", a_layout="row", b_layout="col", lda=0, ldb=0, ldc=0,
-              ldd=0, sparse_a=False, algo="auto"):
+              ldd=0, sparse_a=False, algo="auto", block_scale=0):
     """Build a gemm_desc_t from readable arguments (type names as in DTYPES)."""
     integer = a_type == "s8"
     if c_type is None:
@@ -147,6 +150,7 @@ def make_desc(M, N, K, a_type, b_type, d_type, *, c_type=None, has_c=True, has_b
     d.act = ACT_RELU if act == "relu" else ACT_NONE
     d.sparse_a = int(bool(sparse_a))
     d.algo = ALGO[algo] if isinstance(algo, str) else int(algo)
+    d.block_scale = int(block_scale)
     return d
 
 
@@ -214,3 +218,8 @@ def gemm_sparse24_compress(M, K, a_type, A, values, meta, stream=None):
 def gemm_sparse24_run(plan, values, meta, B, C, bias, D, stream=None):
     _check(load().gemm_sparse24_run(plan.handle, _ptr(values), _ptr(meta), _ptr(B), _ptr(C),
                                     _ptr(bias), _ptr(D), _stream(stream)))
+
+
+def gemm_mx_run(plan, A, scale_a, B, scale_b, C, bias, D, stream=None):
+    _check(load().gemm_mx_run(plan.handle, _ptr(A), _ptr(scale_a), _ptr(B), _ptr(scale_b),
+                              _ptr(C), _ptr(bias), _ptr(D), _stream(stream)))

@@ -8,13 +8,14 @@
   (distance of the ordered bit patterns), or, where fp32 accumulation error
   alone can exceed one output ulp (results near 0),
   |D - Y| <= ulp_out(Y) + tol * |alpha| * S.
-tol = 1e-5 for fp16/bf16 inputs and 1e-4 for fp8 inputs.
+tol = 1e-5 for fp16/bf16 inputs and 1e-4 for fp8 inputs (and the MX formats).
 """
 import numpy as np
 
 from exact import lib_decode
 
-TOL = {"f16": 1e-5, "bf16": 1e-5, "e4m3": 1e-4, "e5m2": 1e-4}
+TOL = {"f16": 1e-5, "bf16": 1e-5, "e4m3": 1e-4, "e5m2": 1e-4, "e2m3": 1e-4, "e3m2": 1e-4,
+       "e2m1": 1e-4}
 
 
 def ordered16(bits):

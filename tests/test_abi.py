@@ -69,6 +69,21 @@ def _ok(**kw):
     (dict(sparse_a=True, a_type="f16", b_type="f16", K=66), G.GEMM_ERR_UNSUPPORTED),
     (dict(sparse_a=True, a_type="f16", b_type="f16", a_layout="col"), G.GEMM_ERR_UNSUPPORTED),
     (dict(sparse_a=True, a_type="f16", b_type="f16", d_type="f32"), G.GEMM_OK),
+    # MX block-scaled
+    (dict(a_type="e4m3", b_type="e4m3", block_scale=32), G.GEMM_OK),
+    (dict(a_type="e2m1", b_type="e5m2", d_type="f16", block_scale=32, has_bias=True,
+          act="relu"), G.GEMM_OK),
+    (dict(a_type="e2m3", b_type="e3m2", d_type="f32", block_scale=32), G.GEMM_OK),
+    (dict(a_type="e2m1", b_type="e2m1", block_scale=16), G.GEMM_ERR_INVALID_VALUE),
+    (dict(a_type="e2m1", b_type="e2m1"), G.GEMM_ERR_UNSUPPORTED),      # fp4 needs scales
+    (dict(a_type="bf16", b_type="bf16", block_scale=32), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="e4m3", b_type="e4m3", block_scale=32, K=48), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="e4m3", b_type="e4m3", block_scale=32, a_layout="col"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="e4m3", b_type="e4m3", block_scale=32, sparse_a=True), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="e4m3", b_type="e4m3", block_scale=32, d_type="s32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="e2m1", b_type="e2m1", block_scale=32, lda=65), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="e2m3", b_type="e2m3", block_scale=32, lda=66), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="e2m3", b_type="e2m3", block_scale=32, lda=68), G.GEMM_OK),
 ])
 def test_validate_desc(desc, status):
     assert G.gemm_validate_desc(_ok(**desc)) == status, G.gemm_last_error()

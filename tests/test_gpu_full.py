@@ -203,3 +203,44 @@ def test_full_sparse24_types_8192(orc, t):
         mism = int((D != ref).sum())
         say("  fused epilogue mismatches:", mism)
         assert mism == 0
+
+
+@pytest.mark.parametrize("name,a,seed", [("mxfp8", "e4m3", 9), ("mxfp4", "e2m1", 11),
+                                         ("mxfp6", "e2m3", 10)])
+def test_full_mx_8192(orc, name, a, seed):
+    """MX block-scaled GEMM at 8192^3 -> bf16 through the plan bench.py times
+    (the tiled kernel for MXFP8 and MXFP4, the generic one for MXFP6):
+    sampled entries against the oracle, and column sums over every output."""
+    say("workload", name, "8192^3 -> bf16")
+    M = N = K = 8192
+    p = inputs.mx_problem(M, N, K, a, a, seed)
+    desc = G.make_desc(M, N, K, a, a, "bf16", has_c=False, block_scale=32)
+    plan = G.gemm_plan(desc)
+    D = torch.empty(M * N * 2, dtype=torch.uint8, device="cuda")
+    G.gemm_mx_run(plan, to_dev(p["A"]), to_dev(p["SA"]), to_dev(p["B"]), to_dev(p["SB"]), None,
+                  None, D)
+    torch.cuda.synchronize()
+    D = D.cpu().numpy().view(np.uint16).reshape(M, N)
+    say("  ran", plan.name)
+    assert plan.name.startswith("mx_generic" if a == "e2m3" else "mx_tiled")
+    rows, cols = _samples(M, N, seed)
+    Dr, Y, S = orc.mx_gemm_entries(p["A"], p["SA"], p["B"], p["SB"], None, None, M, N, K, a, a,
+                                   "bf16", rows, cols)
+    r = check(D[rows, cols], "bf16", Dr, Y, S, a)
+    say("  sampled", r)
+    assert r.ok, r
+    # column sums: sum_m D[m,n] = sum_k b'[k,n] sum_m a'[m,k], a', b' the scaled values
+    sa = np.repeat(orc.decode_packed("e8m0", p["SA"], M * K // 32).reshape(M, K // 32), 32, 1)
+    A = orc.decode_packed(a, p["A"], M * K).reshape(M, K) * sa
+    del sa
+    sb = np.repeat(orc.decode_packed("e8m0", p["SB"], N * K // 32).reshape(N, K // 32), 32, 1)
+    B = orc.decode_packed(a, p["B"], N * K).reshape(N, K) * sb
+    del sb
+    ref = B @ A.sum(axis=0)
+    sabs = np.abs(B) @ np.abs(A).sum(axis=0)
+    del A, B
+    d = lib_decode("bf16", D)
+    got = d.sum(axis=0)
+    bound = TOL[a] * sabs + ulp16(d, "bf16").sum(axis=0) * 2
+    say("  column sums: max |diff|/bound = %.3g" % float((np.abs(got - ref) / bound).max()))
+    assert (np.abs(got - ref) <= bound).all()
