@@ -210,8 +210,8 @@ gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, con
  *   scale_a: M x K/32 E8M0 bytes (row-major), 2^(e-127); scale_b: N x K/32.
  *   A scale of 0xFF (NaN) gives an unspecified result.
  * Device pointers; the fast kernel (pairs of one width: both 8-bit or both
- * E2M1, K % 128 == 0, rows of whole 16 bytes) needs A and B 16-byte and
- * the scales 4-byte aligned, else the generic kernel runs. */
+ * E2M1, K % 512 == 0, rows of whole 16 bytes) needs A, B and the scales
+ * 16-byte aligned, else the generic kernel runs. */
 gemm_status_t gemm_mx_run(const gemm_plan_t *plan, const void *A, const uint8_t *scale_a,
                           const void *B, const uint8_t *scale_b, const void *C, const void *bias,
                           void *D, gemm_stream_t stream);

@@ -141,7 +141,8 @@ __device__ STG_AI inline uint32_t shr_opaque(uint32_t x, int s)
 //  - 8-bit operands: lane l (h = l / 32) gives bytes 0..15 = K 16h .. 16h+15
 //    and bytes 16..31 = K 32+16h .. 32+16h+15 of row / column l % 32 (so
 //    K block b of the instruction is bytes 16b .. 16b+15 of both lane
-//    halves; in LDS: 16-byte chunks h and h+2 of the step's 64 bytes);
+//    halves; the tiled kernel swaps chunks 1 and 2 of each 64-byte K tile
+//    on its way into LDS, so a lane half reads two consecutive chunks);
 //  - 6- and 4-bit operands: lane half h gives K 32h .. 32h+31, packed from
 //    bit 0 up (4-bit: the even element in the low nibble);
 //  - the scale VGPR of lane half b holds (in the byte the instruction's
@@ -154,7 +155,7 @@ struct OpMX {
     static constexpr int LANE_BYTES = 32 * BITS / 8; // one 32-K block per lane
     static constexpr int KB = 2 * LANE_BYTES;        // row bytes per instruction (64 K)
     static constexpr bool INT = false, MX = true;
-    static constexpr bool SPLIT = BITS == 8; // chunk h and h+2 instead of 2h, 2h+1
+    static constexpr bool SPLIT = BITS == 8; // the 8-bit K order (chunks 1 and 2 swapped)
     typedef f16_t acc_t;
     // SEL: byte of sa / sb holding this instruction's scales
     template <int SEL>

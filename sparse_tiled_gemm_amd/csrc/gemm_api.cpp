@@ -345,9 +345,10 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     if (d.block_scale) {
         const int ab = mx_bits(d.a_type), bb = mx_bits(d.b_type);
         const int64_t lim = (int64_t)1 << 30, rowa = d.lda * ab / 8, rowb = d.ldb * bb / 8;
-        // the 4-wave 256 x 256 kernel: one width (8 or 4 bits), whole words of
-        // four scales (K % 128), 16-byte rows, 32-bit offsets over 256 rows
-        const bool fast = ab == bb && ab != 6 && d.K % 128 == 0 && rowa % 16 == 0 &&
+        // the 4-wave 256 x 256 kernel: one width (8 or 4 bits), K in whole
+        // groups of 16 scales (K % 512: 16-byte scale copies), 16-byte rows,
+        // 32-bit offsets over 256 rows
+        const bool fast = ab == bb && ab != 6 && d.K % 512 == 0 && rowa % 16 == 0 &&
                           rowb % 16 == 0 && rowa * 256 < lim && rowb * 256 < lim &&
                           (d.K / 32) * 256 < lim;
         int fam = -1;
@@ -694,7 +695,7 @@ gemm_status_t gemm_mx_run(const gemm_plan_t *plan, const void *A, const uint8_t 
     g.sb = scale_b;
     int fam = plan->family;
     if (fam == KF_MX_TILED &&
-        (!aligned(A, 16) || !aligned(B, 16) || !aligned(scale_a, 4) || !aligned(scale_b, 4)))
+        (!aligned(A, 16) || !aligned(B, 16) || !aligned(scale_a, 16) || !aligned(scale_b, 16)))
         fam = plan->fallback;
     hipError_t e = launch_mx(fam, plan->op / 8, plan->op % 8, g, (hipStream_t)stream);
     if (e != hipSuccess)

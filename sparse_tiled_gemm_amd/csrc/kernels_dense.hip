@@ -85,7 +85,15 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     // LDS holds the stages during the K loop and the epilogue's per-wave
     // 32-row staging slabs afterwards
     constexpr int EPI = GM * GN * 32 * (WN + 4) * 4;
-    constexpr int LDS_BYTES = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
+    // MX: the block scales of the tile's 256 A rows and 256 B columns pass
+    // through LDS in groups of QG 32-bit words per row (16 K blocks, 512 K),
+    // two group slots after the stages
+    constexpr int QG = 4;
+    constexpr int SC_OFF = NSTAGE * STAGE;
+    constexpr int SC_BYTES = OP::MX ? 2 * 2 * QG * 256 * 4 : 0;
+    static_assert(!OP::MX || (BM == 256 && BN == 256 && NT == 256), "one scale row per thread");
+    constexpr int KLOOP = NSTAGE * STAGE + SC_BYTES;
+    constexpr int LDS_BYTES = KLOOP > EPI ? KLOOP : EPI;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
@@ -106,7 +114,13 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     const int ch = tid % CH, r0 = tid / CH;
     const int va0 = r0 * (int)lda_b + ch * 16, vb0 = r0 * (int)ldb_b + ch * 16;
     const int va_step = RPP * (int)lda_b, vb_step = RPP * (int)ldb_b;
-    const int l0 = r0 * BKB + ((ch ^ swz64(r0)) << 4); // + i*RPP*BKB (swz64 is RPP-periodic)
+    // 8-bit MX operands: chunks 1 and 2 of every 64-byte K tile trade places in
+    // LDS, so that a lane half's two consecutive chunks hold K 16h .. and
+    // 32+16h .. (the instruction's K blocks are the two 16-byte halves of
+    // both lane halves' operands)
+    constexpr bool perm = OP::MX && OP::SPLIT;
+    const int lch = perm ? (((ch & 1) << 1) | (ch >> 1)) : ch;
+    const int l0 = r0 * BKB + ((lch ^ swz64(r0)) << 4); // + i*RPP*BKB (swz64 is RPP-periodic)
 
     // register staging of global tiles, two sets (prefetch distance 2 tiles)
     u4_t ga[2][A_LD], gb[2][B_LD];
@@ -143,15 +157,10 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         constexpr int S = decltype(set)::value;
         const uint8_t *lsa = stage_base + a_off;
         const uint8_t *lsb = stage_base + b_off;
-        // 16-byte chunks of the step's slice: consecutive ones per lane half,
-        // or chunks h and h+2 for the 8-bit MX layout (whose K blocks are the
-        // two 16-byte halves of both lanes' operands)
         const int c0 = (s * OP::KB + half * OP::LANE_BYTES) >> 4;
-        constexpr bool split = OP::MX && OP::SPLIT;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const int c = split ? (s * OP::KB >> 4) + half + 2 * v : c0 + v;
-            const int oa = (c ^ sa) << 4, ob = (c ^ sb) << 4;
+            const int oa = ((c0 + v) ^ sa) << 4, ob = ((c0 + v) ^ sb) << 4;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
                 *(u4_t *)&fa[S][i][4 * v] = *(const u4_t *)(lsa + i * 32 * BKB + oa);
@@ -161,30 +170,51 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         }
     };
 
-    // MX block scales: per fragment row / column one 32-bit word of four
-    // consecutive K blocks (128 K), loaded for tile t+1 while tile t runs and
-    // shifted by 8h so that byte 2c of lane half h is block 2c + h
+    // MX block scales.  Each K tile needs, per fragment row / column, one
+    // 32-bit word of four consecutive K blocks (128 K: two tiles of 8-bit
+    // operands, one of 4-bit ones); in HBM those words of 32 consecutive rows
+    // lie K/32 bytes apart, so reading them straight from memory costs a
+    // cache line per lane.  Instead, at the first tile of a group of TG
+    // tiles, each thread copies the next group's QG words (16 contiguous
+    // bytes) of its own A row and B column straight into LDS; the copies are
+    // waited for before the barrier two tiles before that group starts, and
+    // the fragments read their words from LDS one tile ahead.  Slot s,
+    // operand o (0 A, 1 B): 256 rows of 16 bytes at SC_OFF + (2 s + o) 4 KB.
     constexpr int KPT = BKB * 8 / OP::BITS;   // K per tile
-    constexpr int NSW = OP::MX ? FM + FN : 0; // scale words per lane
+    constexpr int TG = QG * 128 / KPT;        // tiles per scale group: 8 or 4
+    constexpr int NSW = OP::MX ? FM + FN : 0; // scale words per lane per tile
+    static_assert(!OP::MX || TG >= 2, "a group spans at least two tiles");
     uint32_t scl[2][NSW > 0 ? NSW : 1];
-    const int64_t kblk = g.K / 32; // scale bytes per row
+    const int64_t kblk = g.K / 32; // scale bytes per row (a multiple of 16)
     // (not used outside MX, where the compiler drops them)
     const __amdgpu_buffer_rsrc_t rsa = tile_rsrc(g.sa + m_blk * kblk, (g.e.M - m_blk) * kblk);
     const __amdgpu_buffer_rsrc_t rsb = tile_rsrc(g.sb + n_blk * kblk, (g.e.N - n_blk) * kblk);
-    auto sload = [&](auto set, int kt) STG_AI {
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto sc_at = [&](int slot, int o, int w, int r) STG_AI {
+        return *(const uint32_t *)(lds + SC_OFF + (2 * slot + o) * 4096 + 16 * r + 4 * w);
+    };
+    // group grp's words of this thread's A row and B column into slot grp & 1
+    // (wave w's copy instruction covers rows 64 w .. 64 w + 63)
+    auto sg_copy = [&](int grp) STG_AI {
+        if constexpr (OP::MX) {
+            uint8_t *base = lds + SC_OFF + 2 * (grp & 1) * 4096 + wave_u * 1024;
+            dma16(rsa, base, tid * (int)kblk, 16 * grp);
+            dma16(rsb, base + 4096, tid * (int)kblk, 16 * grp);
+        }
+    };
+    // this lane's words for tile u into register set S
+    auto sload = [&](auto set, int u) STG_AI {
         if constexpr (OP::MX) {
             constexpr int S = decltype(set)::value;
-            const int q = kt * KPT / 128; // the word holding tile kt's blocks
+            const int slot = (u / TG) & 1, w = (u * KPT / 128) % QG;
             const int arow0 = (wave / GN) * (BM / GM) + (tid & 31);
             const int brow0 = (wave % GN) * (BN / GN) + (tid & 31);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                scl[S][i] = __builtin_amdgcn_raw_buffer_load_b32(
-                    rsa, (arow0 + 32 * i) * (int)kblk + 4 * q, 0, 0);
+                scl[S][i] = sc_at(slot, 0, w, arow0 + 32 * i);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                scl[S][FM + j] = __builtin_amdgcn_raw_buffer_load_b32(
-                    rsb, (brow0 + 32 * j) * (int)kblk + 4 * q, 0, 0);
+                scl[S][FM + j] = sc_at(slot, 1, w, brow0 + 32 * j);
         }
     };
 
@@ -233,13 +263,18 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     using I1 = std::integral_constant<int, 1>;
 
     // prologue: tiles 0 and 1 in LDS stages 0 and 1, tile 2 in registers set 0
-    sload(I0{}, 0);
+    // (MX: scale group 0 into its LDS slot; tile 0's words read after the
+    // barrier)
+    sg_copy(0);
     gload(I0{}, 0);
     gload(I1{}, 1);
     lstore(I0{}, lds);
     lstore(I1{}, lds + STAGE);
     gload(I0{}, 2);
+    if constexpr (OP::MX)
+        STG_WAIT_VMCNT(0); // the direct copies of scale group 0
     __syncthreads();
+    sload(I0{}, 0);
     lread(I0{}, lds, 0);
 
     // one K tile: `P` is the parity of the tile index (register sets and the
@@ -252,7 +287,7 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     // every VM_EVERY MFMAs, a store half-way between), so neither the vector
     // memory pipe (64 B/clk per CU) nor the LDS write path (about half the
     // LDS read rate) backs up and stalls MFMA issue.
-    constexpr int NM = FM * FN, NR = (FM + FN) * NV, NL = A_LD + B_LD + NSW;
+    constexpr int NM = FM * FN, NR = (FM + FN) * NV, NL = A_LD + B_LD;
     constexpr int NMT = KS * NM;
     auto schedule = [&]() STG_AI {
         [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
@@ -283,9 +318,12 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         // `wr`; restrict lets the scheduler interleave the stores with reads
         auto body = [&](const uint8_t *__restrict__ cur, const uint8_t *__restrict__ nxt,
                         uint8_t *__restrict__ wr) STG_AI {
-            // this tile's scales, then the next tile's scales before the tile
-            // loads: waiting for them must not wait for the loads after them
+            // MX: this tile's scale words, the next scale group at the
+            // first tile of a group, and the next tile's words
             sshift(std::integral_constant<int, P>{});
+            if constexpr (OP::MX)
+                if (t % TG == 0)
+                    sg_copy(t / TG + 1);
             sload(std::integral_constant<int, P ^ 1>{}, t + 1);
             gload(std::integral_constant<int, P ^ 1>{}, t + 3);
             [&]<int... S>(std::integer_sequence<int, S...>) STG_AI {
@@ -303,6 +341,12 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
             }(std::make_integer_sequence<int, KS>{});
             lstore(std::integral_constant<int, P>{}, wr);
             schedule();
+            // the next group's words (copied into the slot the previous
+            // group used): complete before this tile's barrier, one tile
+            // before their first read
+            if constexpr (OP::MX)
+                if (t % TG == TG - 2)
+                    STG_WAIT_VMCNT(0);
         };
         body(lds + st * STAGE, lds + st1 * STAGE, lds + st2 * STAGE);
         __syncthreads();
@@ -314,8 +358,10 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         iter(I0{}, t);
         iter(I1{}, t + 1);
     }
-    if (t < KT)
-        iter(I0{}, t);
+    // (MX takes K in whole scale groups, so its tile count is even)
+    if constexpr (!OP::MX)
+        if (t < KT)
+            iter(I0{}, t);
 
     __syncthreads(); // every wave is done with the LDS stages
     epilogue_grid_lds<OP, FM, FN>(g.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,

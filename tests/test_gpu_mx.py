@@ -72,7 +72,7 @@ def test_mx_generic_every_pair(orc, a):
 
 @pytest.mark.parametrize("pair", TILED_PAIRS, ids=["x".join(q) for q in TILED_PAIRS])
 def test_mx_tiled(orc, pair):
-    for (M, N, K) in [(600, 520, 384), (256, 256, 128), (130, 300, 1024), (17, 700, 256)]:
+    for (M, N, K) in [(600, 520, 512), (256, 256, 1024), (130, 300, 1536), (17, 700, 512)]:
         p = _problem(pair[0], pair[1], M, N, K, seed=41)
         C, _ = _extras(M, N, 2)
         say("mx tiled", pair, (M, N, K))
@@ -89,7 +89,7 @@ def test_mx_tiled(orc, pair):
 def test_mx_epilogue(orc, pair, d_type):
     """The fused epilogue bit for bit against the oracle's fp32 epilogue on
     the same kernel's fp32 output, and the cast result against the oracle."""
-    M, N, K = 384, 320, 512
+    M, N, K = 384, 320, 1024
     p = _problem(pair[0], pair[1], M, N, K, seed=42)
     C, bias = _extras(M, N, 3)
     T, n1 = gpu_mx(p, "f32", C=C)
@@ -108,7 +108,7 @@ def _pad_rows(packed, extra_bytes):
 
 @pytest.mark.parametrize("fmt,pad_elems", [("e2m1", 32), ("e4m3", 16), ("e2m3", 4)])
 def test_mx_padded_rows(orc, fmt, pad_elems):
-    M, N, K = 200, 150, 256
+    M, N, K = 200, 150, 512
     p = _problem(fmt, fmt, M, N, K, seed=43)
     bits = inputs.MX_BITS[fmt]
     A = _pad_rows(p["A"], pad_elems * bits // 8)
@@ -122,7 +122,7 @@ def test_mx_padded_rows(orc, fmt, pad_elems):
 
 
 def test_mx_misaligned_a_falls_back(orc):
-    M, N, K = 160, 96, 256
+    M, N, K = 160, 96, 512
     p = _problem("e4m3", "e5m2", M, N, K, seed=44)
     buf = torch.zeros(p["A"].size + 64, dtype=torch.uint8, device="cuda")
     buf[8:8 + p["A"].size] = to_dev(p["A"]).view(-1)
@@ -136,11 +136,12 @@ def test_mx_plan_choice():
     def name(a, b, K):
         return G.gemm_plan(G.make_desc(512, 512, K, a, b, "f32", has_c=False,
                                        block_scale=32)).name
-    assert name("e4m3", "e5m2", 256).startswith("mx_tiled")
-    assert name("e2m1", "e2m1", 128).startswith("mx_tiled")
-    assert name("e4m3", "e4m3", 96).startswith("mx_generic")    # K % 128
-    assert name("e2m1", "e4m3", 256).startswith("mx_generic")   # two widths
-    assert name("e2m3", "e2m3", 256).startswith("mx_generic")   # 6-bit
+    assert name("e4m3", "e5m2", 512).startswith("mx_tiled")
+    assert name("e2m1", "e2m1", 1024).startswith("mx_tiled")
+    assert name("e4m3", "e4m3", 96).startswith("mx_generic")    # K % 512
+    assert name("e2m1", "e2m1", 256).startswith("mx_generic")
+    assert name("e2m1", "e4m3", 512).startswith("mx_generic")   # two widths
+    assert name("e2m3", "e2m3", 512).startswith("mx_generic")   # 6-bit
     with pytest.raises(G.GemmError):
         G.gemm_plan(G.make_desc(512, 512, 96, "e4m3", "e4m3", "f32", has_c=False,
                                 block_scale=32, algo="tiled"))
