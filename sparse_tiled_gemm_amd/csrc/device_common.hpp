@@ -124,15 +124,6 @@ struct OpS8 {
     }
 };
 
-// x >> s as an instruction the compiler neither moves nor folds (a volatile
-// asm stays after the barriers and memory operations before it)
-__device__ STG_AI inline uint32_t shr_opaque(uint32_t x, int s)
-{
-    uint32_t r;
-    asm volatile("v_lshrrev_b32 %0, %1, %2" : "=v"(r) : "v"(s), "v"(x));
-    return r;
-}
-
 // MX block-scaled product of OCP MX element formats (AF / BF: 0 = E4M3, 1 =
 // E5M2, 2 = E2M3, 3 = E3M2, 4 = E2M1, the selectors of the gfx950
 // v_mfma_scale_f32_32x32x64_f8f6f4) with one E8M0 scale per 32 K of every A

@@ -170,19 +170,19 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         }
     };
 
-    // MX block scales.  Each K tile needs, per fragment row / column, one
-    // 32-bit word of four consecutive K blocks (128 K: two tiles of 8-bit
-    // operands, one of 4-bit ones); in HBM those words of 32 consecutive rows
-    // lie K/32 bytes apart, so reading them straight from memory costs a
-    // cache line per lane.  Instead, at the first tile of a group of TG
-    // tiles, each thread copies the next group's QG words (16 contiguous
-    // bytes) of its own A row and B column straight into LDS; the copies are
-    // waited for before the barrier two tiles before that group starts, and
-    // the fragments read their words from LDS one tile ahead.  Slot s,
+    // MX block scales.  Each MFMA needs, per fragment row / column, the
+    // scale byte of the lane half's K block; in HBM the bytes of 32
+    // consecutive rows lie K/32 bytes apart, so reading them straight from
+    // memory costs a cache line per lane.  Instead, at the first tile of a
+    // group of TG tiles (512 K, 16 blocks), each thread copies the next
+    // group's 16 scale bytes of its own A row and B column straight into
+    // LDS; the copies are waited for before the barrier two tiles before
+    // that group starts, and the fragments read their bytes (ds_read_u8,
+    // already in the byte the instruction takes) one tile ahead.  Slot s,
     // operand o (0 A, 1 B): 256 rows of 16 bytes at SC_OFF + (2 s + o) 4 KB.
-    constexpr int KPT = BKB * 8 / OP::BITS;   // K per tile
-    constexpr int TG = QG * 128 / KPT;        // tiles per scale group: 8 or 4
-    constexpr int NSW = OP::MX ? FM + FN : 0; // scale words per lane per tile
+    constexpr int KPT = BKB * 8 / OP::BITS;          // K per tile
+    constexpr int TG = QG * 128 / KPT;               // tiles per scale group: 8 or 4
+    constexpr int NSW = OP::MX ? (FM + FN) * KS : 0; // scale bytes per lane per tile
     static_assert(!OP::MX || TG >= 2, "a group spans at least two tiles");
     uint32_t scl[2][NSW > 0 ? NSW : 1];
     const int64_t kblk = g.K / 32; // scale bytes per row (a multiple of 16)
@@ -190,8 +190,8 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     const __amdgpu_buffer_rsrc_t rsa = tile_rsrc(g.sa + m_blk * kblk, (g.e.M - m_blk) * kblk);
     const __amdgpu_buffer_rsrc_t rsb = tile_rsrc(g.sb + n_blk * kblk, (g.e.N - n_blk) * kblk);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    auto sc_at = [&](int slot, int o, int w, int r) STG_AI {
-        return *(const uint32_t *)(lds + SC_OFF + (2 * slot + o) * 4096 + 16 * r + 4 * w);
+    auto sc_at = [&](int slot, int o, int b, int r) STG_AI {
+        return (uint32_t) * (const uint8_t *)(lds + SC_OFF + (2 * slot + o) * 4096 + 16 * r + b);
     };
     // group grp's words of this thread's A row and B column into slot grp & 1
     // (wave w's copy instruction covers rows 64 w .. 64 w + 63)
@@ -202,19 +202,24 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
             dma16(rsb, base + 4096, tid * (int)kblk, 16 * grp);
         }
     };
-    // this lane's words for tile u into register set S
+    // this lane's scale bytes for tile u into register set S: step st, lane
+    // half h takes K block u KPT / 32 + 2 st + h
     auto sload = [&](auto set, int u) STG_AI {
         if constexpr (OP::MX) {
             constexpr int S = decltype(set)::value;
-            const int slot = (u / TG) & 1, w = (u * KPT / 128) % QG;
+            const int slot = (u / TG) & 1;
             const int arow0 = (wave / GN) * (BM / GM) + (tid & 31);
             const int brow0 = (wave % GN) * (BN / GN) + (tid & 31);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                scl[S][i] = sc_at(slot, 0, w, arow0 + 32 * i);
+            for (int st = 0; st < KS; ++st) {
+                const int b = (u * KPT / 32 + 2 * st + ((tid >> 5) & 1)) % 16;
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                scl[S][FM + j] = sc_at(slot, 1, w, brow0 + 32 * j);
+                for (int i = 0; i < FM; ++i)
+                    scl[S][st * (FM + FN) + i] = sc_at(slot, 0, b, arow0 + 32 * i);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    scl[S][st * (FM + FN) + FM + j] = sc_at(slot, 1, b, brow0 + 32 * j);
+            }
         }
     };
 
@@ -224,32 +229,18 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             acc[i][j] = typename OP::acc_t{};
-    // the current tile's scale words shifted by 8h, computed at the start of
-    // the tile that uses them: an opaque shift, so the compiler cannot hoist
-    // it up to the load (which would make it wait for every load in flight)
-    uint32_t ssh[NSW > 0 ? NSW : 1];
-    auto sshift = [&](auto set) STG_AI {
-        if constexpr (OP::MX) {
-            constexpr int S = decltype(set)::value;
-            const int hs = 8 * (lane >> 5);
-#pragma unroll
-            for (int i = 0; i < NSW; ++i)
-                ssh[i] = shr_opaque(scl[S][i], hs);
-        }
-    };
     // fragment set F; for MX also the tile's parity P and step S
     auto mma = [&](auto set, auto pset, auto step) STG_AI {
         constexpr int S = decltype(set)::value;
         if constexpr (OP::MX) {
             constexpr int P = decltype(pset)::value, ST = decltype(step)::value;
-            // byte of the shifted word: block (t KPT + 64 ST) / 32 mod 4, minus h
-            constexpr int SEL = (KPT == 64 ? 2 * P : 2 * ST) & 3;
+            constexpr int o = ST * (FM + FN);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = OP::template mma<SEL>(fa[S][i], fb[S][j], acc[i][j], ssh[i],
-                                                      ssh[FM + j]);
+                    acc[i][j] = OP::template mma<0>(fa[S][i], fb[S][j], acc[i][j], scl[P][o + i],
+                                                    scl[P][o + FM + j]);
         } else {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
@@ -318,9 +309,8 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         // `wr`; restrict lets the scheduler interleave the stores with reads
         auto body = [&](const uint8_t *__restrict__ cur, const uint8_t *__restrict__ nxt,
                         uint8_t *__restrict__ wr) STG_AI {
-            // MX: this tile's scale words, the next scale group at the
-            // first tile of a group, and the next tile's words
-            sshift(std::integral_constant<int, P>{});
+            // MX: the next scale group at the first tile of a group, and
+            // the next tile's scale bytes
             if constexpr (OP::MX)
                 if (t % TG == 0)
                     sg_copy(t / TG + 1);
@@ -341,12 +331,14 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
             }(std::make_integer_sequence<int, KS>{});
             lstore(std::integral_constant<int, P>{}, wr);
             schedule();
-            // the next group's words (copied into the slot the previous
+            // the next group's bytes (copied into the slot the previous
             // group used): complete before this tile's barrier, one tile
-            // before their first read
+            // before their first read.  Loads retire in order and the
+            // copies are older than this tile's A_LD + B_LD prefetch loads,
+            // which may stay in flight.
             if constexpr (OP::MX)
                 if (t % TG == TG - 2)
-                    STG_WAIT_VMCNT(0);
+                    STG_WAIT_VMCNT(A_LD + B_LD);
         };
         body(lds + st * STAGE, lds + st1 * STAGE, lds + st2 * STAGE);
         __syncthreads();
