@@ -464,6 +464,26 @@ int oracle_mx_gemm_entries(const oracle_gemm_t *g, const void *A, const uint8_t 
     return 0;
 }
 
+/* ------------------------------------------------------------------ W4A16 */
+
+int oracle_w4a16_dequant(int w_type, int64_t N, int64_t K, int64_t gs, const uint8_t *Bq,
+                         int64_t ldq, const void *scales, const uint8_t *zeros, void *W)
+{
+    if ((w_type != OR_F16 && w_type != OR_BF16) || N < 0 || K < 0 || gs <= 0 || K % gs ||
+        ldq * 2 < K)
+        return -1;
+    const int64_t G = K / gs;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const int q = (Bq[n * ldq + k / 2] >> (4 * (k % 2))) & 0xF;
+            const int64_t g = k / gs;
+            const int z = zeros ? zeros[n * G + g] : 8;
+            const double sc = oracle_decode(w_type, scales, n * G + g);
+            oracle_encode(w_type, (double)(q - z) * sc, W, n * K + k);
+        }
+    return 0;
+}
+
 int oracle_epilogue_f32(int64_t M, int64_t N, const float *T, float alpha, const float *bias,
                         int relu, int d_type, void *D)
 {

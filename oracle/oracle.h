@@ -157,6 +157,22 @@ int oracle_mx_gemm_entries(const oracle_gemm_t *g, const void *A, const uint8_t 
                            int64_t n_entries, const int64_t *rows, const int64_t *cols,
                            void *D_out, double *Y, double *S);
 
+/* W4A16 weight dequantisation ("NVIDIA MMA", section "How quantisation
+ * configurations map to MMA": W4A16 INT4 weight-only runs an FP16 x FP16 or
+ * BF16 x BF16 MMA on a weight tile dequantised first; section "Ampere:
+ * FP16/BF16 and integer MMA baseline": a W4A16 kernel converts the weight
+ * tile to FP16/BF16 before the float MMA).  Bq is the N x K weight matrix
+ * (B stored column-major, one row per output column n) of unsigned 4-bit
+ * codes, two per byte along K (element k of row n in bits 4(k%2) .. of byte
+ * n*ldq + k/2, ldq in bytes); group g of row n is K positions gs*g ..
+ * gs*g+gs-1 (K % gs == 0).  Output W (N x K, type w_type = OR_F16 or
+ * OR_BF16): W[n,k] = RNE_w_type((q - z[n,g]) * s[n,g]), s = scales[n*(K/gs)
+ * + g] of type w_type, z = zeros[n*(K/gs) + g] (0..15), or 8 for every group
+ * when zeros is NULL.  The product is exact in fp64 (and in fp32), so the
+ * one rounding is the cast.  Returns 0 or -1 for a bad argument. */
+int oracle_w4a16_dequant(int w_type, int64_t N, int64_t K, int64_t gs, const uint8_t *Bq,
+                         int64_t ldq, const void *scales, const uint8_t *zeros, void *W);
+
 /* Threads the OpenMP loops use. */
 int oracle_num_threads(void);
 

@@ -70,6 +70,8 @@ def lib():
         L.oracle_mx_gemm_entries.restype = ctypes.c_int
         L.oracle_mx_gemm_entries.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp, vp, vp, i64,
                                              vp, vp, vp, dp, dp]
+        L.oracle_w4a16_dequant.restype = ctypes.c_int
+        L.oracle_w4a16_dequant.argtypes = [ctypes.c_int, i64, i64, i64, vp, i64, vp, vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -284,3 +286,20 @@ def mx_gemm_entries(A, SA, B, SB, C, bias, M, N, K, a_type, b_type, d_type, rows
     if rc != 0:
         raise ValueError("oracle_mx_gemm_entries rejected the problem")
     return D, Y, S
+
+
+# ---------------------------------------------------------------- W4A16
+
+def w4a16_dequant(Bq, scales, zeros, N, K, gs, w_type):
+    """[N, K/2] packed u4 codes + [N, K/gs] scales (w_type bits) + [N, K/gs]
+    u8 zero points (or None: 8) -> [N, K] w_type bits (see oracle.h)."""
+    Bq = np.ascontiguousarray(Bq, dtype=np.uint8).reshape(N, -1)
+    scales = np.ascontiguousarray(scales, dtype=STORAGE[w_type])
+    if zeros is not None:
+        zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+    W = np.zeros((N, K), dtype=STORAGE[w_type])
+    rc = lib().oracle_w4a16_dequant(TYPES[w_type], N, K, gs, _ptr(Bq), Bq.shape[1],
+                                    _ptr(scales), _ptr(zeros), _ptr(W))
+    if rc != 0:
+        raise ValueError("oracle_w4a16_dequant rejected the arguments")
+    return W

@@ -300,6 +300,44 @@ def mx_problem(M=8192, N=8192, K=8192, a_type="e4m3", b_type="e4m3", workload=9,
                    bias=None, alpha=1.0, relu=False, mx=True)
 
 
+# ---------------------------------------------------------------- W4A16
+
+def w4_pack(q):
+    """[N, K] codes 0..15 -> [N, K/2] bytes, element k in bits 4(k%2) .. of byte k/2."""
+    q = np.asarray(q, dtype=np.uint8)
+    return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+
+
+def w4a16_problem(M=8192, N=8192, K=8192, a_type="bf16", gs=128, workload=12, zeros=True):
+    """Activations A normal(0,1) in a_type; weights normal(0, 1/K) quantised
+    asymmetrically per group of gs K: s = (max - min) / 15 rounded to a_type,
+    z = round(-min / s) in 0..15 (or 8 when zeros is False), q = clamp(round(w
+    / s) + z, 0, 15); B = packed codes [N, K/2]; no C, no bias, a_type out."""
+    enc = to_f16 if a_type == "f16" else to_bf16
+    dec = (lambda b: np.asarray(b, np.uint16).view(np.float16).astype(np.float64)) \
+        if a_type == "f16" else \
+        (lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    A = enc(_rng(workload, 1).standard_normal(size=(M, K), dtype=np.float32))
+    w = _rng(workload, 2).standard_normal(size=(N, K), dtype=np.float32).astype(np.float64)
+    w /= np.sqrt(K)
+    wg = w.reshape(N, K // gs, gs)
+    lo = np.minimum(wg.min(-1), 0.0)
+    hi = np.maximum(wg.max(-1), 0.0)
+    if zeros:
+        S = enc(np.maximum(hi - lo, 1e-8) / 15.0)
+        s = dec(S)
+        Z = np.clip(np.round(-lo / s), 0, 15).astype(np.uint8)
+    else:
+        S = enc(np.maximum(np.maximum(hi, -lo), 1e-8) / 7.0)
+        s = dec(S)
+        Z = None
+    z = Z.astype(np.float64) if zeros else 8.0
+    q = np.clip(np.round(wg / s[..., None]) + (z[..., None] if zeros else z), 0, 15)
+    B = w4_pack(q.reshape(N, K).astype(np.uint8))
+    return Problem(M=M, N=N, K=K, a_type=a_type, b_type="u4", d_type=a_type, A=A, B=B,
+                   scales=S, zeros=Z, gs=gs, C=None, bias=None, alpha=1.0, relu=False, w4=True)
+
+
 WORKLOADS = {
     "f16_128": lambda: dense_f16(128, 128, 128),
     "bf16_8192": lambda: dense_bf16(8192, 8192, 8192),
@@ -312,5 +350,6 @@ WORKLOADS = {
     "sparse24_fp8_8192": lambda: sparse24_fp8(8192, 8192, 8192),
     "mxfp8_8192": lambda: mx_problem(8192, 8192, 8192, "e4m3", "e4m3", 9),
     "mxfp6_8192": lambda: mx_problem(8192, 8192, 8192, "e2m3", "e2m3", 10),
+    "w4a16_bf16_8192": lambda: w4a16_problem(8192, 8192, 8192, "bf16", 128, 12),
     "mxfp4_8192": lambda: mx_problem(8192, 8192, 8192, "e2m1", "e2m1", 11),
 }
