@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 # effective rate of a 2:4 product counts the dropped half of A's products).
 PEAK = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "s8": 5033.2, "sparse_f16": 5033.2,
         "sparse_bf16": 5033.2, "sparse_fp8": 10066.4, "sparse_s8": 10066.4,
-        "mxfp8": 5033.2, "mxfp6": 10066.4, "mxfp4": 10066.4}
+        "mxfp8": 5033.2, "mxfp6": 10066.4, "mxfp4": 10066.4, "w4a16_bf16": 2516.6}
 HBM_GBS = 8000.0
 
 HEADLINE = "bf16_8192"
@@ -50,6 +50,8 @@ def _workloads():
         "mxfp8_8192": (lambda: inputs.mx_problem(8192, 8192, 8192, "e4m3", "e4m3", 9), "mxfp8"),
         "mxfp4_8192": (lambda: inputs.mx_problem(8192, 8192, 8192, "e2m1", "e2m1", 11), "mxfp4"),
         "mxfp6_8192": (lambda: inputs.mx_problem(8192, 8192, 8192, "e2m3", "e2m3", 10), "mxfp6"),
+        "w4a16_bf16_8192": (lambda: inputs.w4a16_problem(8192, 8192, 8192, "bf16", 128, 12),
+                            "w4a16_bf16"),
     }
 
 
@@ -66,6 +68,10 @@ def algorithmic_bytes(p, sparse=False):
     from sparse_tiled_gemm_amd import gemm as G
     M, N, K = p["M"], p["N"], p["K"]
     eb = G.ELEM_BYTES
+    if p.get("w4"):  # A, the packed codes, scales and zero points, D
+        return (p["A"].nbytes + p["B"].nbytes + p["scales"].nbytes +
+                (p["zeros"].nbytes if p["zeros"] is not None else 0) +
+                (M * N * 4 if p["C"] is not None else 0) + M * N * eb[p["d_type"]])
     if p.get("mx"):  # packed elements and one scale byte per 32 K
         return (p["A"].nbytes + p["B"].nbytes + p["SA"].nbytes + p["SB"].nbytes +
                 (M * N * 4 if p["C"] is not None else 0) + M * N * eb[p["d_type"]])
@@ -88,11 +94,11 @@ def run_workload(name, steps, warmup, rotate_b=1):
     p = make()
     M, N, K = p["M"], p["N"], p["K"]
     sparse = p.get("A_logical") is not None
-    mx = bool(p.get("mx"))
+    mx, w4 = bool(p.get("mx")), bool(p.get("w4"))
     desc = G.make_desc(M, N, K, p["a_type"], p["b_type"], p["d_type"], has_c=p["C"] is not None,
                        has_bias=p["bias"] is not None, alpha=p["alpha"],
                        act="relu" if p["relu"] else "none", sparse_a=sparse,
-                       block_scale=32 if mx else 0)
+                       block_scale=32 if mx else (p["gs"] if w4 else 0))
     plan = G.gemm_plan(desc)
     Bs = [_dev(p["B"]) for _ in range(rotate_b)]
     tC = _dev(p["C"]) if p["C"] is not None else None
@@ -108,6 +114,12 @@ def run_workload(name, steps, warmup, rotate_b=1):
 
         def call(i):
             G.gemm_sparse24_run(plan, vals, meta, Bs[i % rotate_b], tC, tbias, D)
+    elif w4:
+        tA, tS = _dev(p["A"]), _dev(p["scales"])
+        tZ = _dev(p["zeros"]) if p["zeros"] is not None else None
+
+        def call(i):
+            G.gemm_w4a16_run(plan, tA, Bs[i % rotate_b], tS, tZ, tC, tbias, D)
     elif mx:
         tA, tSA, tSB = _dev(p["A"]), _dev(p["SA"]), _dev(p["SB"])
 
@@ -255,7 +267,7 @@ def main():
         "dtype": {"bf16": "bf16", "f16": "f16", "fp8": "fp8_e4m3xe5m2", "s8": "s8",
                   "sparse_f16": "f16", "sparse_bf16": "bf16", "sparse_fp8": "fp8_e4m3xe5m2",
                   "sparse_s8": "s8", "mxfp8": "mxfp8_e4m3", "mxfp6": "mxfp6_e2m3",
-                  "mxfp4": "mxfp4_e2m1"}[kind],
+                  "mxfp4": "mxfp4_e2m1", "w4a16_bf16": "bf16_u4"}[kind],
         "data": "synthetic",
         "config": {"workload": args.workload, "M": p["M"], "N": p["N"], "K": p["K"],
                    "a_type": p["a_type"], "b_type": p["b_type"], "d_type": p["d_type"],

@@ -74,7 +74,9 @@ typedef enum {
      * stored packed along K: */
     GEMM_F6_E2M3 = 8, /* bias 1, max 7.5, no inf/NaN; 4 elements in 3 bytes */
     GEMM_F6_E3M2 = 9, /* bias 3, max 28, no inf/NaN; 4 elements in 3 bytes */
-    GEMM_F4_E2M1 = 10 /* bias 1, max 6, no inf/NaN; 2 elements per byte */
+    GEMM_F4_E2M1 = 10, /* bias 1, max 6, no inf/NaN; 2 elements per byte */
+    GEMM_U4 = 11       /* W4A16 weight codes 0..15, two per byte along K (the
+                          even element in the low nibble); B only */
 } gemm_dtype_t;
 
 typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout_t;
@@ -108,6 +110,10 @@ typedef enum {
  *   rows of whole bytes (lda, ldb in elements); c_type F32, d_type F32 /
  *   F16 / BF16, any epilogue; used with gemm_mx_run.  The 6- and 4-bit
  *   formats exist only here.
+ *   b = U4 (W4A16): a F16 or BF16, A row-major, B column-major (codes along
+ *   K, ldb even), block_scale = the weight group size (a multiple of 32
+ *   dividing K); c_type F32, d_type F32 / F16 / BF16, any epilogue; used
+ *   with gemm_w4a16_run.
  * Epilogue, in fp32 for float outputs:  t = acc (+ C[m,n] if has_c);
  *   y = has_bias ? fmaf(alpha, t, bias[n]) : alpha * t;
  *   z = (act == RELU) ? (y > 0 ? y : +0) : y;  D = round-to-nearest-even(z).
@@ -123,7 +129,8 @@ typedef struct {
     int32_t act;                            /* gemm_act_t */
     int32_t sparse_a;                       /* 1: 2:4-compressed A */
     int32_t algo;                           /* gemm_algo_t, normally AUTO */
-    int32_t block_scale;                    /* 0, or 32: MX block-scaled (gemm_mx_run) */
+    int32_t block_scale;                    /* 0; 32: MX block-scaled (gemm_mx_run);
+                                               W4A16: the weight group size */
 } gemm_desc_t;
 
 typedef struct gemm_plan gemm_plan_t;
@@ -215,6 +222,22 @@ gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, con
 gemm_status_t gemm_mx_run(const gemm_plan_t *plan, const void *A, const uint8_t *scale_a,
                           const void *B, const uint8_t *scale_b, const void *C, const void *bias,
                           void *D, gemm_stream_t stream);
+
+/* Enqueue the W4A16 weight-only product ("NVIDIA MMA", section "How
+ * quantisation configurations map to MMA": INT4 weights, FP16 / BF16
+ * activations, run as an FP16 / BF16 MMA on weight tiles dequantised in the
+ * main loop).  The plan must have b_type == GEMM_U4.
+ *   B: N x K codes q (column n at byte n*ldb/2, two codes per byte along K);
+ *   scales: N x K/gs values of A's type (gs = the plan's block_scale);
+ *   zeros: N x K/gs bytes z in 0..15, or NULL for z = 8 everywhere;
+ *   w[k,n] = RNE((q - z[n,k/gs]) * scales[n,k/gs]) in A's type, then
+ *   D = epilogue(A*w + C) with fp32 accumulation, as for gemm_run.
+ * A and scales must be 2-byte aligned (GEMM_ERR_MISALIGNED); the fast kernel
+ * (16-byte rows of A and of codes) needs A and B 16-byte aligned, else the
+ * generic kernel runs. */
+gemm_status_t gemm_w4a16_run(const gemm_plan_t *plan, const void *A, const void *B,
+                             const void *scales, const uint8_t *zeros, const void *C,
+                             const void *bias, void *D, gemm_stream_t stream);
 
 /* Static text for a status code. */
 const char *gemm_status_string(gemm_status_t status);

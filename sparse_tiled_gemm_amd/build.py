@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libstgemm.so")
-SOURCES = ["gemm_api.cpp", "kernels_dense.hip", "kernels_sparse.hip", "kernels_mx.hip"]
+SOURCES = ["gemm_api.cpp", "kernels_dense.hip", "kernels_sparse.hip", "kernels_mx.hip",
+           "kernels_w4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -74,7 +74,7 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
 struct OpF16 {
     static constexpr int ELEM = 2, LANE_BYTES = 16, KB = 32, BITS = 16;
-    static constexpr bool INT = false, MX = false, SPLIT = false;
+    static constexpr bool INT = false, MX = false, SPLIT = false, W4 = false;
     typedef f16_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {
@@ -86,7 +86,7 @@ struct OpF16 {
 
 struct OpBF16 {
     static constexpr int ELEM = 2, LANE_BYTES = 16, KB = 32, BITS = 16;
-    static constexpr bool INT = false, MX = false, SPLIT = false;
+    static constexpr bool INT = false, MX = false, SPLIT = false, W4 = false;
     typedef f16_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {
@@ -101,7 +101,7 @@ struct OpBF16 {
 template <int AFMT, int BFMT>
 struct OpF8 {
     static constexpr int ELEM = 1, LANE_BYTES = 32, KB = 64, BITS = 8;
-    static constexpr bool INT = false, MX = false, SPLIT = false;
+    static constexpr bool INT = false, MX = false, SPLIT = false, W4 = false;
     typedef f16_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {
@@ -114,7 +114,7 @@ struct OpF8 {
 
 struct OpS8 {
     static constexpr int ELEM = 1, LANE_BYTES = 16, KB = 32, BITS = 8;
-    static constexpr bool INT = true, MX = false, SPLIT = false;
+    static constexpr bool INT = true, MX = false, SPLIT = false, W4 = false;
     typedef i16_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {
@@ -145,7 +145,7 @@ struct OpMX {
     static constexpr int ELEM = 1; // (unused: MX addressing is by BITS)
     static constexpr int LANE_BYTES = 32 * BITS / 8; // one 32-K block per lane
     static constexpr int KB = 2 * LANE_BYTES;        // row bytes per instruction (64 K)
-    static constexpr bool INT = false, MX = true;
+    static constexpr bool INT = false, MX = true, W4 = false;
     static constexpr bool SPLIT = BITS == 8; // the 8-bit K order (chunks 1 and 2 swapped)
     typedef f16_t acc_t;
     // SEL: byte of sa / sb holding this instruction's scales
@@ -162,6 +162,15 @@ struct OpMX {
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, c, AF, BF, SEL, (int)sa, SEL,
                                                                (int)sb);
     }
+};
+
+// W4A16 ("NVIDIA MMA", section "How quantisation configurations map to
+// MMA": INT4 weight-only runs as an FP16 / BF16 MMA on a weight tile
+// dequantised first): Base (OpF16 or OpBF16) multiplies A by B's unsigned
+// 4-bit codes turned into Base's type in the main loop.
+template <class Base>
+struct OpW4 : Base {
+    static constexpr bool W4 = true;
 };
 
 // 16x16 MFMA forms (skinny kernel).  Lane l holds row (or column) l % 16 and
@@ -254,6 +263,30 @@ __device__ STG_AI inline uint16_t f32_to_bf16_bits(float x)
 {
     __bf16 h = (__bf16)x; // gfx950 v_cvt_pk_bf16_f32: round to nearest even
     return __builtin_bit_cast(uint16_t, h);
+}
+
+// Eight codes of one 32-bit word (element j in bits 4j ..) dequantised to
+// RNE((q - z) s) in the 16-bit type (BF: bfloat16, else fp16), two per
+// output word, element order kept.  (q - z) s is exact in fp32 (a 5-bit
+// integer times a 16-bit significand), so the cast is the only rounding.
+template <bool BF>
+__device__ STG_AI inline void w4_dequant8(uint32_t w, int z, float s, uint32_t *out)
+{
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+        const float v0 = (float)((int)((w >> (4 * j)) & 15u) - z) * s;
+        const float v1 = (float)((int)((w >> (4 * j + 4)) & 15u) - z) * s;
+        out[j / 2] = BF ? f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16)
+                        : f32_to_f16_bits(v0) | ((uint32_t)f32_to_f16_bits(v1) << 16);
+    }
+}
+
+// A 16-bit scale's bits (fp16, or bfloat16 when BF) as fp32.
+template <bool BF>
+__device__ STG_AI inline float w4_scale(uint32_t bits)
+{
+    return BF ? __builtin_bit_cast(float, bits << 16)
+              : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
 // Epilogue of one accumulator value at (row, col), both in range, for output

@@ -187,6 +187,8 @@ const char *family_name(int f)
     case KF_PINGPONG5: return "pingpong5";
     case KF_MX_GENERIC: return "mx_generic";
     case KF_MX_TILED: return "mx_tiled";
+    case KF_W4_GENERIC: return "w4_generic";
+    case KF_W4_TILED: return "w4_tiled";
     default: return "?";
     }
 }
@@ -237,7 +239,7 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
     if (d.M < 0 || d.N < 0 || d.K < 0)
         return fail(GEMM_ERR_INVALID_VALUE, "negative size M=%lld N=%lld K=%lld",
                     (long long)d.M, (long long)d.N, (long long)d.K);
-    auto dtype_ok = [](int t) { return t >= GEMM_F16 && t <= GEMM_F4_E2M1; };
+    auto dtype_ok = [](int t) { return t >= GEMM_F16 && t <= GEMM_U4; };
     if (!dtype_ok(d.a_type) || !dtype_ok(d.b_type) || !dtype_ok(d.d_type) ||
         !(d.c_type == 0 || dtype_ok(d.c_type)))
         return fail(GEMM_ERR_INVALID_VALUE, "unknown dtype code");
@@ -255,8 +257,29 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
         return fail(GEMM_ERR_INVALID_VALUE, "negative leading dimension");
     if (!normalise(d))
         return fail(GEMM_ERR_INVALID_VALUE, "leading dimension smaller than the matrix extent");
+    if (d.b_type == GEMM_U4 || d.a_type == GEMM_U4) {
+        // W4A16 ("NVIDIA MMA", section "How quantisation configurations map
+        // to MMA"): fp16 / bf16 activations, 4-bit weight codes with a scale
+        // and zero point per group of block_scale K, fp32 accumulation
+        if (d.a_type != GEMM_F16 && d.a_type != GEMM_BF16)
+            return fail(GEMM_ERR_UNSUPPORTED, "W4A16: A must be f16 or bf16 and B u4");
+        if (d.block_scale < 32 || d.block_scale % 32 || d.K % d.block_scale)
+            return fail(GEMM_ERR_UNSUPPORTED,
+                        "W4A16: block_scale (the group size) must be a multiple of 32 dividing K");
+        if (d.sparse_a)
+            return fail(GEMM_ERR_UNSUPPORTED, "W4A16: A cannot be 2:4 sparse");
+        if (d.a_layout != GEMM_ROW_MAJOR || d.b_layout != GEMM_COL_MAJOR)
+            return fail(GEMM_ERR_UNSUPPORTED, "W4A16: A row-major, B column-major (codes along K)");
+        if (d.ldb % 2)
+            return fail(GEMM_ERR_UNSUPPORTED, "W4A16: packed weight rows must be whole bytes");
+        if (!(d.c_type == GEMM_F32 || (d.c_type == 0 && !d.has_c)))
+            return fail(GEMM_ERR_UNSUPPORTED, "float inputs take an f32 C");
+        if (d.d_type != GEMM_F32 && d.d_type != GEMM_F16 && d.d_type != GEMM_BF16)
+            return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16 or bf16");
+        return ok();
+    }
     if (d.block_scale != 0 && d.block_scale != 32)
-        return fail(GEMM_ERR_INVALID_VALUE, "block_scale must be 0 or 32");
+        return fail(GEMM_ERR_INVALID_VALUE, "block_scale must be 0 or 32 (or a W4A16 group size)");
 
     if (d.block_scale == 32) {
         // MX block-scaled ("NVIDIA MMA", section "Blackwell: FP4/FP6 and
@@ -280,7 +303,7 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
         return ok();
     }
     if (d.a_type > GEMM_S32 || d.b_type > GEMM_S32)
-        return fail(GEMM_ERR_UNSUPPORTED, "6- and 4-bit formats need block_scale = 32");
+        return fail(GEMM_ERR_UNSUPPORTED, "6- and 4-bit float formats need block_scale = 32");
     if (d.d_type > GEMM_S32 || d.c_type > GEMM_S32)
         return fail(GEMM_ERR_UNSUPPORTED, "unsupported C or D type");
 
@@ -341,6 +364,38 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     p->device = dev;
     p->op = op_kind(d.a_type, d.b_type);
     p->fallback = KF_GENERIC;
+
+    if (d.b_type == GEMM_U4) {
+        // the 4-wave 256 x 256 kernel: 16-byte rows of A and of codes, 32-bit
+        // offsets over 256 rows
+        const int64_t lim = (int64_t)1 << 30, rowa = d.lda * 2, rowb = d.ldb / 2;
+        const bool fast = d.K > 0 && rowa % 16 == 0 && rowb % 16 == 0 && rowa * 256 < lim &&
+                          rowb * 256 < lim && (d.K / d.block_scale) * 2 * 256 < lim;
+        int fam = -1;
+        switch (d.algo) {
+        case GEMM_ALGO_AUTO: fam = fast ? KF_W4_TILED : KF_W4_GENERIC; break;
+        case GEMM_ALGO_TILED:
+        case GEMM_ALGO_TILED_256: fam = fast ? KF_W4_TILED : -1; break;
+        case GEMM_ALGO_GENERIC: fam = KF_W4_GENERIC; break;
+        default: fam = -1;
+        }
+        if (fam < 0) {
+            delete p;
+            return fail(GEMM_ERR_UNSUPPORTED, "requested algorithm cannot serve this W4A16 problem");
+        }
+        if (const char *force = getenv("STGEMM_FORCE_KERNEL")) { // tuning override
+            if (strcmp(force, family_name(KF_W4_GENERIC)) == 0)
+                fam = KF_W4_GENERIC;
+            if (strcmp(force, family_name(KF_W4_TILED)) == 0 && fast)
+                fam = KF_W4_TILED;
+        }
+        p->op = d.a_type == GEMM_F16 ? OPK_F16 : OPK_BF16;
+        p->family = fam;
+        p->fallback = KF_W4_GENERIC;
+        snprintf(p->name, sizeof p->name, "%s_%s", family_name(fam), op_name(p->op));
+        *out = p;
+        return ok();
+    }
 
     if (d.block_scale) {
         const int ab = mx_bits(d.a_type), bb = mx_bits(d.b_type);
@@ -520,6 +575,8 @@ gemm_status_t gemm_run(const gemm_plan_t *plan, const void *A, const void *B, co
     const gemm_desc_t &d = plan->d;
     if (d.sparse_a)
         return fail(GEMM_ERR_UNSUPPORTED, "plan is for 2:4 sparse A: use gemm_sparse24_run");
+    if (d.b_type == GEMM_U4)
+        return fail(GEMM_ERR_UNSUPPORTED, "plan is W4A16: use gemm_w4a16_run");
     if (d.block_scale)
         return fail(GEMM_ERR_UNSUPPORTED, "plan is block-scaled: use gemm_mx_run");
     if (d.M == 0 || d.N == 0)
@@ -553,6 +610,9 @@ gemm_status_t gemm_run(const gemm_plan_t *plan, const void *A, const void *B, co
     }
     g.e = make_epi(d, C, bias, D);
     g.sa = g.sb = nullptr;
+    g.ws = nullptr;
+    g.wz = nullptr;
+    g.wgs = 0;
 
     int fam = plan->family;
     if (fam != KF_GENERIC && (!aligned(A, 16) || !aligned(B, 16)))
@@ -673,8 +733,8 @@ gemm_status_t gemm_mx_run(const gemm_plan_t *plan, const void *A, const uint8_t 
     if (!plan)
         return fail(GEMM_ERR_NULL_POINTER, "plan is NULL");
     const gemm_desc_t &d = plan->d;
-    if (!d.block_scale)
-        return fail(GEMM_ERR_UNSUPPORTED, "plan is not block-scaled: use gemm_run");
+    if (!d.block_scale || d.b_type == GEMM_U4)
+        return fail(GEMM_ERR_UNSUPPORTED, "plan is not MX block-scaled");
     if (d.M == 0 || d.N == 0)
         return ok();
     if (d.K > 0 && (!A || !B || !scale_a || !scale_b))
@@ -693,11 +753,54 @@ gemm_status_t gemm_mx_run(const gemm_plan_t *plan, const void *A, const uint8_t 
     g.e = make_epi(d, C, bias, D);
     g.sa = scale_a;
     g.sb = scale_b;
+    g.ws = nullptr;
+    g.wz = nullptr;
+    g.wgs = 0;
     int fam = plan->family;
     if (fam == KF_MX_TILED &&
         (!aligned(A, 16) || !aligned(B, 16) || !aligned(scale_a, 16) || !aligned(scale_b, 16)))
         fam = plan->fallback;
     hipError_t e = launch_mx(fam, plan->op / 8, plan->op % 8, g, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "kernel launch");
+    return ok();
+}
+
+gemm_status_t gemm_w4a16_run(const gemm_plan_t *plan, const void *A, const void *B,
+                             const void *scales, const uint8_t *zeros, const void *C,
+                             const void *bias, void *D, gemm_stream_t stream)
+{
+    if (!plan)
+        return fail(GEMM_ERR_NULL_POINTER, "plan is NULL");
+    const gemm_desc_t &d = plan->d;
+    if (d.b_type != GEMM_U4)
+        return fail(GEMM_ERR_UNSUPPORTED, "plan is not W4A16");
+    if (d.M == 0 || d.N == 0)
+        return ok();
+    if (d.K > 0 && (!A || !B || !scales))
+        return fail(GEMM_ERR_NULL_POINTER, "A, B or scales is NULL");
+    gemm_status_t st = check_epilogue_ptrs(d, C, bias, D);
+    if (st != GEMM_OK)
+        return st;
+    if (d.K > 0 && (!aligned(A, 2) || !aligned(scales, 2)))
+        return fail(GEMM_ERR_MISALIGNED, "A or scales not aligned to 2 bytes");
+    GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.K = d.K;
+    g.a_rs = d.lda;
+    g.a_cs = 1;
+    g.b_rs = 1;
+    g.b_cs = d.ldb;
+    g.e = make_epi(d, C, bias, D);
+    g.sa = g.sb = nullptr;
+    g.ws = scales;
+    g.wz = zeros;
+    g.wgs = d.block_scale;
+    int fam = plan->family;
+    if (fam == KF_W4_TILED && (!aligned(A, 16) || !aligned(B, 16)))
+        fam = plan->fallback;
+    hipError_t e = launch_w4(fam, plan->op, g, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "kernel launch");
     return ok();

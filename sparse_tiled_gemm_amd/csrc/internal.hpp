@@ -38,6 +38,8 @@ enum KernelFamily {
     KF_TILED_256W8L, // 256 x 256, 8 waves of 128 x 64, 128-byte K tiles, 2 direct-copy stages
     KF_MX_GENERIC,   // MX block-scaled, any format pair
     KF_MX_TILED,     // MX block-scaled, 256 x 256 4-wave tile, pairs of one width (8 or 4 bits)
+    KF_W4_GENERIC,   // W4A16, any shape
+    KF_W4_TILED,     // W4A16, 256 x 256 4-wave tile, B dequantised into LDS
     KF_COUNT
 };
 
@@ -46,6 +48,10 @@ hipError_t launch_dense(int family, int op, const GemmArgs &g, hipStream_t s);
 // (0 E4M3, 1 E5M2, 2 E2M3, 3 E3M2, 4 E2M1); g.sa / g.sb hold the scales.
 hipError_t launch_mx(int family, int afmt, int bfmt, const GemmArgs &g, hipStream_t s);
 hipError_t launch_mx_tiled(int afmt, int bfmt, const GemmArgs &g, hipStream_t s);
+// W4A16: op is OPK_F16 or OPK_BF16 (the activations' type); g.ws / g.wz /
+// g.wgs hold the weight groups' scales and zero points.
+hipError_t launch_w4(int family, int op, const GemmArgs &g, hipStream_t s);
+hipError_t launch_w4_tiled(int op, const GemmArgs &g, hipStream_t s);
 hipError_t launch_sparse(int family, int op, const SparseArgs &a, hipStream_t s);
 // Compressor for elements of elem_bytes (2 or 1) bytes, an element being a
 // zero when (bits & zero_mask) == 0: writes values/meta; *flag (device int,

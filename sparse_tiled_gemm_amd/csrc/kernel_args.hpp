@@ -35,6 +35,12 @@ struct GemmArgs {
     // MX block scales (E8M0, one per 32 K): sa[m*(K/32) + g] for row m of A,
     // sb[n*(K/32) + g] for column n of B; nullptr outside the MX path
     const uint8_t *sa, *sb;
+    // W4A16 weights (B holds unsigned 4-bit codes, two per byte along K,
+    // b_cs in codes): group g = k / wgs of column n has scale ws[n*(K/wgs) + g]
+    // (A's 16-bit type) and zero point wz[n*(K/wgs) + g] (8 when wz is null)
+    const void *ws;
+    const uint8_t *wz;
+    int64_t wgs;
 };
 
 // 2:4-compressed A: values [M, K/2] fp16, meta [M, ceil(K/32)] u32.

@@ -101,14 +101,27 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int64_t m_blk = (int64_t)tm * BM, n_blk = (int64_t)tn * BN;
-    const int64_t lda_b = g.a_rs * OP::BITS / 8, ldb_b = g.b_cs * OP::BITS / 8;
-    const int64_t kbytes = g.K * OP::BITS / 8;
+    // W4A16: B holds 4-bit codes (half a byte per K), dequantised into the
+    // 16-bit B tile on its way into LDS
+    constexpr bool W4 = OP::W4;
+    static_assert(!W4 || (BN == 256 && NT == 256), "one B row per thread");
+    const int64_t lda_b = g.a_rs * OP::BITS / 8;
+    const int64_t ldb_b = W4 ? g.b_cs / 2 : g.b_cs * OP::BITS / 8;
+    const int64_t kbytes = g.K * OP::BITS / 8, kbytes_b = W4 ? g.K / 2 : kbytes;
     const int KT = (int)(kbytes / BKB);
     // bounded by the last byte of the last row: loads past it return zero
     const __amdgpu_buffer_rsrc_t ra = tile_rsrc((const uint8_t *)g.A + m_blk * lda_b,
                                                 (g.e.M - m_blk - 1) * lda_b + kbytes);
     const __amdgpu_buffer_rsrc_t rb = tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b,
-                                                (g.e.N - n_blk - 1) * ldb_b + kbytes);
+                                                (g.e.N - n_blk - 1) * ldb_b + kbytes_b);
+    // W4A16 group scales and zero points of the tile's columns (zero points
+    // absent: a zero-length resource, whose loads return 0, and z = 8)
+    const int64_t wgr = W4 ? g.K / g.wgs : 0; // groups per column
+    const __amdgpu_buffer_rsrc_t rws =
+        tile_rsrc((const uint8_t *)g.ws + n_blk * wgr * 2, W4 ? (g.e.N - n_blk) * wgr * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rwz =
+        tile_rsrc(g.wz ? g.wz + n_blk * wgr : (const uint8_t *)g.B, W4 && g.wz ? (g.e.N - n_blk) * wgr : 0);
+    const bool has_wz = g.wz != nullptr;
 
     // global -> LDS copy: thread owns chunk `ch` of rows r0 + i*RPP
     const int ch = tid % CH, r0 = tid / CH;
@@ -124,15 +137,25 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
 
     // register staging of global tiles, two sets (prefetch distance 2 tiles)
     u4_t ga[2][A_LD], gb[2][B_LD];
+    uint32_t wsb[2], wzb[2]; // W4A16: the tile's group scale bits and zero point
     auto gload = [&](auto set, int kt) STG_AI {
         constexpr int S = decltype(set)::value;
         const int soff = kt * BKB;
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
             ga[S][i] = buf_load16(ra, va0 + i * va_step, soff);
+        if constexpr (W4) {
+            // thread t: the 16 code bytes (32 K) of column n_blk + t, and its
+            // group's scale and zero point
+            const int grp = (int)((int64_t)kt * (BKB / 2) / g.wgs);
+            gb[S][0] = buf_load16(rb, tid * (int)ldb_b, kt * (BKB / 4));
+            wsb[S] = __builtin_amdgcn_raw_buffer_load_b16(rws, (tid * (int)wgr + grp) * 2, 0, 0);
+            wzb[S] = __builtin_amdgcn_raw_buffer_load_b8(rwz, tid * (int)wgr + grp, 0, 0);
+        } else {
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i)
-            gb[S][i] = buf_load16(rb, vb0 + i * vb_step, soff);
+            for (int i = 0; i < B_LD; ++i)
+                gb[S][i] = buf_load16(rb, vb0 + i * vb_step, soff);
+        }
     };
     auto lstore = [&](auto set, uint8_t *__restrict__ stage_base) STG_AI {
         constexpr int S = decltype(set)::value;
@@ -140,9 +163,24 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
             *(u4_t *)(base + i * RPP * BKB) = ga[S][i];
+        if constexpr (W4) {
+            // 32 codes -> 32 16-bit values: row t of the B tile, four chunks
+            constexpr bool BF = std::is_same<OP, OpW4<OpBF16>>::value;
+            const float sc = w4_scale<BF>(wsb[S]);
+            const int z = has_wz ? (int)wzb[S] : 8;
+            uint8_t *brow = stage_base + BM * BKB + tid * BKB;
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i)
-            *(u4_t *)(base + BM * BKB + i * RPP * BKB) = gb[S][i];
+            for (int c = 0; c < 4; ++c) {
+                u4_t v;
+                w4_dequant8<BF>(gb[S][0][c], z, sc, (uint32_t *)&v);
+                // chunk c holds codes 8c .. 8c+7 = one 16-byte chunk of 8 values
+                *(u4_t *)(brow + ((c ^ swz64(tid)) << 4)) = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_LD; ++i)
+                *(u4_t *)(base + BM * BKB + i * RPP * BKB) = gb[S][i];
+        }
     };
 
     // fragment reads: lane reads rows arow + 32 i (A) and brow + 32 j (B)
@@ -278,7 +316,9 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     // every VM_EVERY MFMAs, a store half-way between), so neither the vector
     // memory pipe (64 B/clk per CU) nor the LDS write path (about half the
     // LDS read rate) backs up and stalls MFMA issue.
-    constexpr int NM = FM * FN, NR = (FM + FN) * NV, NL = A_LD + B_LD;
+    // (W4A16: three loads and four LDS writes for B)
+    constexpr int NL = A_LD + (W4 ? 3 : B_LD), NLW = A_LD + (W4 ? 4 : B_LD);
+    constexpr int NM = FM * FN, NR = (FM + FN) * NV;
     constexpr int NMT = KS * NM;
     auto schedule = [&]() STG_AI {
         [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
@@ -286,7 +326,7 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
                 [&]() STG_AI {
                     constexpr int m = Q % NM;
                     constexpr int nr = spread(m, NR, NM), nl = spread(Q, NL, NMT);
-                    constexpr int nw = spread((Q + NMT / 2) % NMT, NL, NMT);
+                    constexpr int nw = spread((Q + NMT / 2) % NMT, NLW, NMT);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
                     if constexpr (nr > 0)
                         __builtin_amdgcn_sched_group_barrier(0x100, nr, 0); // DS read
@@ -1111,6 +1151,21 @@ static hipError_t launch_mx_tiled_t(const GemmArgs &g, hipStream_t s)
     const int tiles_m = (int)((g.e.M + 255) / 256), tiles_n = (int)((g.e.N + 255) / 256);
     hipLaunchKernelGGL((k_tiled<OP, 256, 256>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
                        s, g, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+// W4A16 on the 4-wave 256x256 tile (one B column per thread).
+hipError_t launch_w4_tiled(int op, const GemmArgs &g, hipStream_t s)
+{
+    const int tiles_m = (int)((g.e.M + 255) / 256), tiles_n = (int)((g.e.N + 255) / 256);
+    if (op == OPK_F16)
+        hipLaunchKernelGGL((k_tiled<OpW4<OpF16>, 256, 256>), dim3((unsigned)(tiles_m * tiles_n)),
+                           dim3(256), 0, s, g, tiles_m, tiles_n);
+    else if (op == OPK_BF16)
+        hipLaunchKernelGGL((k_tiled<OpW4<OpBF16>, 256, 256>), dim3((unsigned)(tiles_m * tiles_n)),
+                           dim3(256), 0, s, g, tiles_m, tiles_n);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -5,7 +5,7 @@ addresses; PyTorch provides memory and streams only.
 
 The functions carry the C names: gemm_validate_desc, gemm_plan,
 gemm_plan_destroy, gemm_plan_describe, gemm_run, gemm_sparse24_sizes,
-gemm_sparse24_compress, gemm_sparse24_run, gemm_mx_run, gemm_status_string,
+gemm_sparse24_compress, gemm_sparse24_run, gemm_mx_run, gemm_w4a16_run, gemm_status_string,
 gemm_last_error.  Non-OK statuses raise GemmError (except
 gemm_validate_desc, which returns the status).
 """
@@ -27,7 +27,7 @@ GEMM_ERR_HIP = 7
 
 # gemm_dtype_t
 DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "e5m2": 4, "s8": 5, "f32": 6, "s32": 7,
-          "e2m3": 8, "e3m2": 9, "e2m1": 10}
+          "e2m3": 8, "e3m2": 9, "e2m1": 10, "u4": 11}
 ROW_MAJOR, COL_MAJOR = 0, 1
 ACT_NONE, ACT_RELU = 0, 1
 # gemm_algo_t
@@ -79,6 +79,7 @@ def load():
         "gemm_plan_describe": (st, [vp, ctypes.c_char_p, ctypes.c_size_t]),
         "gemm_run": (st, [vp, vp, vp, vp, vp, vp, vp]),
         "gemm_mx_run": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "gemm_w4a16_run": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "gemm_sparse24_sizes": (st, [i64, i64, i32, ctypes.POINTER(ctypes.c_size_t),
                                      ctypes.POINTER(ctypes.c_size_t)]),
         "gemm_sparse24_compress": (st, [i64, i64, i32, vp, vp, vp, vp]),
@@ -223,3 +224,8 @@ def gemm_sparse24_run(plan, values, meta, B, C, bias, D, stream=None):
 def gemm_mx_run(plan, A, scale_a, B, scale_b, C, bias, D, stream=None):
     _check(load().gemm_mx_run(plan.handle, _ptr(A), _ptr(scale_a), _ptr(B), _ptr(scale_b),
                               _ptr(C), _ptr(bias), _ptr(D), _stream(stream)))
+
+
+def gemm_w4a16_run(plan, A, B, scales, zeros, C, bias, D, stream=None):
+    _check(load().gemm_w4a16_run(plan.handle, _ptr(A), _ptr(B), _ptr(scales), _ptr(zeros),
+                                 _ptr(C), _ptr(bias), _ptr(D), _stream(stream)))

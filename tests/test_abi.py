@@ -84,6 +84,16 @@ def _ok(**kw):
     (dict(a_type="e2m1", b_type="e2m1", block_scale=32, lda=65), G.GEMM_ERR_UNSUPPORTED),
     (dict(a_type="e2m3", b_type="e2m3", block_scale=32, lda=66), G.GEMM_ERR_UNSUPPORTED),
     (dict(a_type="e2m3", b_type="e2m3", block_scale=32, lda=68), G.GEMM_OK),
+    # W4A16 (block_scale = the weight group size)
+    (dict(a_type="bf16", b_type="u4", block_scale=64), G.GEMM_OK),
+    (dict(a_type="f16", b_type="u4", d_type="f32", block_scale=32, has_bias=True), G.GEMM_OK),
+    (dict(a_type="bf16", b_type="u4", block_scale=0), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="bf16", b_type="u4", block_scale=48), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="bf16", b_type="u4", block_scale=128), G.GEMM_ERR_UNSUPPORTED),  # K = 64
+    (dict(a_type="e4m3", b_type="u4", block_scale=32), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="bf16", b_type="u4", block_scale=32, b_layout="row"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="bf16", b_type="u4", block_scale=32, ldb=65), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="bf16", b_type="bf16", block_scale=64), G.GEMM_ERR_INVALID_VALUE),
 ])
 def test_validate_desc(desc, status):
     assert G.gemm_validate_desc(_ok(**desc)) == status, G.gemm_last_error()

@@ -244,3 +244,26 @@ def test_full_mx_8192(orc, name, a, seed):
     bound = TOL[a] * sabs + ulp16(d, "bf16").sum(axis=0) * 2
     say("  column sums: max |diff|/bound = %.3g" % float((np.abs(got - ref) / bound).max()))
     assert (np.abs(got - ref) <= bound).all()
+
+
+def test_full_w4a16_8192(orc):
+    """W4A16 at 8192^3 (bf16 activations, groups of 128, bf16 out) through the
+    plan bench.py times: sampled entries against the oracle's dequantisation
+    plus dense GEMM, and column sums over every output."""
+    say("workload W4A16 bf16 8192^3 -> bf16")
+    M = N = K = 8192
+    p = inputs.w4a16_problem(M, N, K, "bf16", 128, 12)
+    desc = G.make_desc(M, N, K, "bf16", "u4", "bf16", has_c=False, block_scale=128)
+    plan = G.gemm_plan(desc)
+    D = torch.empty(M * N * 2, dtype=torch.uint8, device="cuda")
+    G.gemm_w4a16_run(plan, to_dev(p["A"]), to_dev(p["B"]), to_dev(p["scales"]),
+                     to_dev(p["zeros"]), None, None, D)
+    torch.cuda.synchronize()
+    D = D.cpu().numpy().view(np.uint16).reshape(M, N)
+    say("  ran", plan.name)
+    assert plan.name.startswith("w4_tiled")
+    W = orc.w4a16_dequant(p["B"], p["scales"], p["zeros"], N, K, 128, "bf16")
+    q = dict(p)
+    q["B"], q["b_type"] = W, "bf16"
+    _check_samples(orc, q, D, seed=12)
+    _float_colsum_check(q, D)
