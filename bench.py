@@ -52,6 +52,8 @@ def _workloads():
         "mxfp6_8192": (lambda: inputs.mx_problem(8192, 8192, 8192, "e2m3", "e2m3", 10), "mxfp6"),
         "w4a16_bf16_8192": (lambda: inputs.w4a16_problem(8192, 8192, 8192, "bf16", 128, 12),
                             "w4a16_bf16"),
+        "w4a16_bf16_16x8192x8192": (lambda: inputs.w4a16_problem(16, 8192, 8192, "bf16", 128, 13),
+                                    "w4a16_bf16"),
     }
 
 
@@ -285,7 +287,7 @@ def main():
         for name in _workloads():
             if name == args.workload:
                 continue
-            rot = 4 if name.startswith("bf16_skinny") else 1
+            rot = 4 if (name.startswith("bf16_skinny") or name.startswith("w4a16_bf16_16x")) else 1
             try:
                 r, _ = run_workload(name, args.steps, args.warmup, rotate_b=rot)
             except Exception as e:  # report, keep the headline line

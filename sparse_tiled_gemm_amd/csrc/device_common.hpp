@@ -166,8 +166,9 @@ struct OpMX {
 
 // W4A16 ("NVIDIA MMA", section "How quantisation configurations map to
 // MMA": INT4 weight-only runs as an FP16 / BF16 MMA on a weight tile
-// dequantised first): Base (OpF16 or OpBF16) multiplies A by B's unsigned
-// 4-bit codes turned into Base's type in the main loop.
+// dequantised first): Base (OpF16 or OpBF16, or their 16x16 forms in the
+// skinny kernel) multiplies A by B's unsigned 4-bit codes turned into
+// Base's type in the main loop.
 template <class Base>
 struct OpW4 : Base {
     static constexpr bool W4 = true;
@@ -178,7 +179,7 @@ struct OpW4 : Base {
 // column l % 16.  KB16 = K bytes one instruction consumes (4 lane groups).
 struct Op16F16 {
     static constexpr int ELEM = 2, LANE_BYTES = 16;
-    static constexpr bool INT = false;
+    static constexpr bool INT = false, W4 = false;
     typedef f4_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {
@@ -189,7 +190,7 @@ struct Op16F16 {
 };
 struct Op16BF16 {
     static constexpr int ELEM = 2, LANE_BYTES = 16;
-    static constexpr bool INT = false;
+    static constexpr bool INT = false, W4 = false;
     typedef f4_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {
@@ -201,7 +202,7 @@ struct Op16BF16 {
 template <int AFMT, int BFMT>
 struct Op16F8 {
     static constexpr int ELEM = 1, LANE_BYTES = 32;
-    static constexpr bool INT = false;
+    static constexpr bool INT = false, W4 = false;
     typedef f4_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {
@@ -211,7 +212,7 @@ struct Op16F8 {
 };
 struct Op16S8 {
     static constexpr int ELEM = 1, LANE_BYTES = 16;
-    static constexpr bool INT = true;
+    static constexpr bool INT = true, W4 = false;
     typedef i4_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {

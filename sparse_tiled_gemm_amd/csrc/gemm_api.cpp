@@ -189,6 +189,7 @@ const char *family_name(int f)
     case KF_MX_TILED: return "mx_tiled";
     case KF_W4_GENERIC: return "w4_generic";
     case KF_W4_TILED: return "w4_tiled";
+    case KF_W4_SKINNY: return "w4_skinny";
     default: return "?";
     }
 }
@@ -371,9 +372,14 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
         const int64_t lim = (int64_t)1 << 30, rowa = d.lda * 2, rowb = d.ldb / 2;
         const bool fast = d.K > 0 && rowa % 16 == 0 && rowb % 16 == 0 && rowa * 256 < lim &&
                           rowb * 256 < lim && (d.K / d.block_scale) * 2 * 256 < lim;
+        // M <= 16: the skinny kernel (whole 128-K chunks), bound by streaming
+        // the codes once
+        const bool skinny = fast && d.M <= 16 && d.K % 128 == 0 && rowa * 16 < lim &&
+                            rowb * 32 < lim;
         int fam = -1;
         switch (d.algo) {
-        case GEMM_ALGO_AUTO: fam = fast ? KF_W4_TILED : KF_W4_GENERIC; break;
+        case GEMM_ALGO_AUTO: fam = skinny ? KF_W4_SKINNY : fast ? KF_W4_TILED : KF_W4_GENERIC; break;
+        case GEMM_ALGO_SKINNY: fam = skinny ? KF_W4_SKINNY : -1; break;
         case GEMM_ALGO_TILED:
         case GEMM_ALGO_TILED_256: fam = fast ? KF_W4_TILED : -1; break;
         case GEMM_ALGO_GENERIC: fam = KF_W4_GENERIC; break;
@@ -388,6 +394,8 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
                 fam = KF_W4_GENERIC;
             if (strcmp(force, family_name(KF_W4_TILED)) == 0 && fast)
                 fam = KF_W4_TILED;
+            if (strcmp(force, family_name(KF_W4_SKINNY)) == 0 && skinny)
+                fam = KF_W4_SKINNY;
         }
         p->op = d.a_type == GEMM_F16 ? OPK_F16 : OPK_BF16;
         p->family = fam;
@@ -798,7 +806,7 @@ gemm_status_t gemm_w4a16_run(const gemm_plan_t *plan, const void *A, const void 
     g.wz = zeros;
     g.wgs = d.block_scale;
     int fam = plan->family;
-    if (fam == KF_W4_TILED && (!aligned(A, 16) || !aligned(B, 16)))
+    if ((fam == KF_W4_TILED || fam == KF_W4_SKINNY) && (!aligned(A, 16) || !aligned(B, 16)))
         fam = plan->fallback;
     hipError_t e = launch_w4(fam, plan->op, g, (hipStream_t)stream);
     if (e != hipSuccess)

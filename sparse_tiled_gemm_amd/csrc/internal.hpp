@@ -40,6 +40,7 @@ enum KernelFamily {
     KF_MX_TILED,     // MX block-scaled, 256 x 256 4-wave tile, pairs of one width (8 or 4 bits)
     KF_W4_GENERIC,   // W4A16, any shape
     KF_W4_TILED,     // W4A16, 256 x 256 4-wave tile, B dequantised into LDS
+    KF_W4_SKINNY,    // W4A16, M <= 16, B streamed and dequantised in registers
     KF_COUNT
 };
 
@@ -52,6 +53,7 @@ hipError_t launch_mx_tiled(int afmt, int bfmt, const GemmArgs &g, hipStream_t s)
 // g.wgs hold the weight groups' scales and zero points.
 hipError_t launch_w4(int family, int op, const GemmArgs &g, hipStream_t s);
 hipError_t launch_w4_tiled(int op, const GemmArgs &g, hipStream_t s);
+hipError_t launch_w4_skinny(int op, const GemmArgs &g, hipStream_t s);
 hipError_t launch_sparse(int family, int op, const SparseArgs &a, hipStream_t s);
 // Compressor for elements of elem_bytes (2 or 1) bytes, an element being a
 // zero when (bits & zero_mask) == 0: writes values/meta; *flag (device int,

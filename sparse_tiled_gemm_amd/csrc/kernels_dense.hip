@@ -907,36 +907,80 @@ __global__ __launch_bounds__(512, 1) void k_skinny(GemmArgs g)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t n_blk = (int64_t)blockIdx.x * 32;
-    const int64_t lda_b = g.a_rs * OP::ELEM, ldb_b = g.b_cs * OP::ELEM;
-    const int64_t kbytes = g.K * OP::ELEM;
+    // W4A16: B holds 4-bit codes, a lane's 64 bytes of a chunk arrive as 16
+    // code bytes (32 K) and are dequantised in registers before the MFMAs
+    constexpr bool W4 = OP::W4;
+    constexpr bool BF = std::is_base_of<Op16BF16, OP>::value;
+    const int64_t lda_b = g.a_rs * OP::ELEM;
+    const int64_t ldb_b = W4 ? g.b_cs / 2 : g.b_cs * OP::ELEM;
+    const int64_t kbytes = g.K * OP::ELEM, kbytes_b = W4 ? g.K / 2 : kbytes;
     const int NC = (int)(kbytes / CB);
     const __amdgpu_buffer_rsrc_t ra = tile_rsrc(g.A, (g.e.M - 1) * lda_b + kbytes);
     const __amdgpu_buffer_rsrc_t rb =
-        tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b, (g.e.N - n_blk - 1) * ldb_b + kbytes);
+        tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b, (g.e.N - n_blk - 1) * ldb_b + kbytes_b);
     const int row = lane & 15, grp = lane >> 4;
     const int va = row * (int)lda_b + grp * LB;
-    const int vb0 = row * (int)ldb_b + grp * LB, vb1 = vb0 + 16 * (int)ldb_b;
+    const int vb0 = row * (int)ldb_b + grp * (W4 ? LB / 4 : LB), vb1 = vb0 + 16 * (int)ldb_b;
+    // W4A16 group scales / zero points of the block's 32 columns
+    const int64_t wgr = W4 ? g.K / g.wgs : 0;
+    const __amdgpu_buffer_rsrc_t rws =
+        tile_rsrc((const uint8_t *)g.ws + n_blk * wgr * 2, W4 ? (g.e.N - n_blk) * wgr * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rwz = tile_rsrc(g.wz ? g.wz + n_blk * wgr : (const uint8_t *)g.B,
+                                                 W4 && g.wz ? (g.e.N - n_blk) * wgr : 0);
+    const bool has_wz = g.wz != nullptr;
 
-    u4_t pa[2][NLD], pb[2][2][NLD];
+    u4_t pa[2][NLD], pb[2][2][W4 ? 1 : NLD];
+    uint32_t wsb[2][2], wzb[2][2];
     auto load = [&](auto set, int c) STG_AI {
         constexpr int S = decltype(set)::value;
         const int soff = c * CB;
 #pragma unroll
-        for (int j = 0; j < NLD; ++j) {
+        for (int j = 0; j < NLD; ++j)
             pa[S][j] = buf_load16(ra, va + 16 * j, soff);
-            pb[S][0][j] = buf_load16(rb, vb0 + 16 * j, soff);
-            pb[S][1][j] = buf_load16(rb, vb1 + 16 * j, soff);
+        if constexpr (W4) {
+            // K chunk c covers K (CB/2) c ..; this lane's 32 K sit in one group
+            const int kg = (int)(((int64_t)c * (CB / 2) + 32 * grp) / g.wgs);
+            pb[S][0][0] = buf_load16(rb, vb0, c * (CB / 4));
+            pb[S][1][0] = buf_load16(rb, vb1, c * (CB / 4));
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const int o = (16 * f + row) * (int)wgr + kg;
+                wsb[S][f] = __builtin_amdgcn_raw_buffer_load_b16(rws, 2 * o, 0, 0);
+                wzb[S][f] = __builtin_amdgcn_raw_buffer_load_b8(rwz, o, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NLD; ++j) {
+                pb[S][0][j] = buf_load16(rb, vb0 + 16 * j, soff);
+                pb[S][1][j] = buf_load16(rb, vb1 + 16 * j, soff);
+            }
         }
     };
     typename OP::acc_t acc[2] = {typename OP::acc_t{}, typename OP::acc_t{}};
     auto compute = [&](auto set) STG_AI {
         constexpr int S = decltype(set)::value;
         const uint32_t *a = (const uint32_t *)pa[S];
+        if constexpr (W4) {
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st)
+            for (int f = 0; f < 2; ++f) {
+                // 32 codes -> the 64 bytes the 16-bit path would have loaded
+                u4_t bq[NLD];
+                const float sc = w4_scale<BF>(wsb[S][f]);
+                const int z = has_wz ? (int)wzb[S][f] : 8;
 #pragma unroll
-            for (int f = 0; f < 2; ++f)
-                acc[f] = OP::mma(a + st * FW, (const uint32_t *)pb[S][f] + st * FW, acc[f]);
+                for (int j = 0; j < NLD; ++j)
+                    w4_dequant8<BF>(pb[S][f][0][j], z, sc, (uint32_t *)&bq[j]);
+#pragma unroll
+                for (int st = 0; st < STEPS; ++st)
+                    acc[f] = OP::mma(a + st * FW, (const uint32_t *)bq + st * FW, acc[f]);
+            }
+        } else {
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+                    acc[f] = OP::mma(a + st * FW, (const uint32_t *)pb[S][f] + st * FW, acc[f]);
+        }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -1151,6 +1195,19 @@ static hipError_t launch_mx_tiled_t(const GemmArgs &g, hipStream_t s)
     const int tiles_m = (int)((g.e.M + 255) / 256), tiles_n = (int)((g.e.N + 255) / 256);
     hipLaunchKernelGGL((k_tiled<OP, 256, 256>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0,
                        s, g, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+// W4A16 with M <= 16 on the skinny kernel.
+hipError_t launch_w4_skinny(int op, const GemmArgs &g, hipStream_t s)
+{
+    const unsigned blocks = (unsigned)((g.e.N + 31) / 32);
+    if (op == OPK_F16)
+        hipLaunchKernelGGL(k_skinny<OpW4<Op16F16>>, dim3(blocks), dim3(512), 0, s, g);
+    else if (op == OPK_BF16)
+        hipLaunchKernelGGL(k_skinny<OpW4<Op16BF16>>, dim3(blocks), dim3(512), 0, s, g);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

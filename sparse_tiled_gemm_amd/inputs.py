@@ -351,5 +351,6 @@ WORKLOADS = {
     "mxfp8_8192": lambda: mx_problem(8192, 8192, 8192, "e4m3", "e4m3", 9),
     "mxfp6_8192": lambda: mx_problem(8192, 8192, 8192, "e2m3", "e2m3", 10),
     "w4a16_bf16_8192": lambda: w4a16_problem(8192, 8192, 8192, "bf16", 128, 12),
+    "w4a16_bf16_16x8192x8192": lambda: w4a16_problem(16, 8192, 8192, "bf16", 128, 13),
     "mxfp4_8192": lambda: mx_problem(8192, 8192, 8192, "e2m1", "e2m1", 11),
 }

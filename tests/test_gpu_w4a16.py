@@ -75,6 +75,23 @@ def test_w4_generic(orc, a_type):
         assert r.ok, r
 
 
+@pytest.mark.parametrize("a_type", ["bf16", "f16"])
+@pytest.mark.parametrize("gs", [32, 128])
+def test_w4_skinny(orc, a_type, gs):
+    """M <= 16: the skinny kernel, codes streamed and dequantised in registers."""
+    for (M, N, K) in [(1, 700, 1024), (5, 96, 2048), (16, 8192, 1024), (16, 130, 4096)]:
+        p = inputs.w4a16_problem(M, N, K, a_type, gs, workload=65)
+        C = _C(M, N, 5)
+        D, name = gpu_w4(p, "f32", C=C)
+        assert name.startswith("w4_skinny"), name
+        r = _vs_oracle(orc, p, D, "f32", C=C)
+        say("  skinny", a_type, gs, (M, N, K), r)
+        assert r.ok, r
+    p = inputs.w4a16_problem(16, 512, 1024, a_type, gs, workload=66, zeros=False)
+    D, name = gpu_w4(p, a_type)
+    assert name.startswith("w4_skinny") and _vs_oracle(orc, p, D, a_type).ok
+
+
 @pytest.mark.parametrize("algo", ["auto", "generic"])
 def test_w4_without_zero_points(orc, algo):
     M, N, K = 300, 264, 512
@@ -117,6 +134,10 @@ def test_w4_plan_choice_and_errors():
         return G.gemm_plan(G.make_desc(512, 512, K, "bf16", "u4", "bf16", has_c=False,
                                        block_scale=gs, **kw))
     assert plan(512, 128).name.startswith("w4_tiled")
+    assert G.gemm_plan(G.make_desc(16, 512, 512, "bf16", "u4", "bf16", has_c=False,
+                                   block_scale=128)).name.startswith("w4_skinny")
+    assert G.gemm_plan(G.make_desc(16, 512, 480, "bf16", "u4", "bf16", has_c=False,
+                                   block_scale=32)).name.startswith("w4_tiled")  # K % 128
     assert plan(512, 128, lda=520).name.startswith("w4_tiled")     # 1040-byte A rows
     assert plan(512, 128, lda=516).name.startswith("w4_generic")   # A rows not 16-byte
     assert plan(512, 128, ldb=520).name.startswith("w4_generic")   # code rows of 260 bytes
