@@ -173,6 +173,21 @@ int oracle_encode(int type, double x, void *base, int64_t idx)
         ((uint16_t *)base)[idx] = (uint16_t)pack_binary(r, 8, 7, 127, 0x7FC0u);
         return 0;
     }
+    case OR_E4M3:
+    case OR_E5M2: {
+        /* round to nearest even, saturating: a result beyond the largest
+         * finite value (or infinite) becomes that value with its sign; NaN
+         * is 0x7F */
+        const int e4 = type == OR_E4M3;
+        const double maxv = e4 ? 448.0 : 57344.0;
+        double r = e4 ? round_binary(x, 4, -6, maxv) : round_binary(x, 3, -14, maxv);
+        if (isinf(r))
+            r = copysign(maxv, r);
+        uint32_t bits = isnan(r) ? 0x7Fu : (e4 ? pack_binary(r, 4, 3, 7, 0x7Fu)
+                                                : pack_binary(r, 5, 2, 15, 0x7Fu));
+        ((uint8_t *)base)[idx] = (uint8_t)bits;
+        return 0;
+    }
     case OR_F32: {
         double r = round_binary(x, 24, -126, ldexp(16777215.0, 104)); /* (2 - 2^-23) * 2^127 */
         uint32_t bits = pack_binary(r, 8, 23, 127, 0x7FC00000u);
@@ -213,6 +228,11 @@ static int is_float_in(int t) { return t == OR_F16 || t == OR_BF16 || t == OR_E4
  * accumulate / output": float inputs accumulate in fp32 (here fp64, exact
  * products) and may be cast to fp32/fp16/bf16; s8 inputs accumulate in int32
  * and are written as int32 with no epilogue. */
+static int is_float_out(int t)
+{
+    return t == OR_F32 || t == OR_F16 || t == OR_BF16 || t == OR_E4M3 || t == OR_E5M2;
+}
+
 static int check_desc(const oracle_gemm_t *g)
 {
     if (g->M < 0 || g->N < 0 || g->K < 0)
@@ -220,19 +240,19 @@ static int check_desc(const oracle_gemm_t *g)
     if (g->a_type == OR_S8 || g->b_type == OR_S8) {
         if (g->a_type != OR_S8 || g->b_type != OR_S8)
             return -1;
-        if (g->c_type != OR_S32 || g->d_type != OR_S32)
-            return -1;
-        if (g->alpha != 1.0f || g->has_bias || g->relu)
-            return -1;
-        return 0;
+        if (g->d_type == OR_S32) {
+            if (g->c_type != OR_S32 || g->alpha != 1.0f || g->has_bias || g->relu)
+                return -1;
+            return 0;
+        }
+        /* int8 -> float: the wrapped int32 sum, then the float epilogue */
+        return (g->c_type == OR_F32 && is_float_out(g->d_type)) ? 0 : -1;
     }
     if (!is_float_in(g->a_type) || !is_float_in(g->b_type))
         return -1;
     if (g->c_type != OR_F32)
         return -1;
-    if (g->d_type != OR_F32 && g->d_type != OR_F16 && g->d_type != OR_BF16)
-        return -1;
-    return 0;
+    return is_float_out(g->d_type) ? 0 : -1;
 }
 
 static int64_t a_index(const oracle_gemm_t *g, int64_t m, int64_t k)
@@ -266,6 +286,8 @@ static void finish(const oracle_gemm_t *g, int64_t m, int64_t n, double acc, dou
             *y_out = (double)w;
         return;
     }
+    if (is_int_type(g->a_type)) /* int8 -> float: the int32 accumulator's value */
+        acc = (double)(int32_t)(uint32_t)(uint64_t)(int64_t)acc;
     double t = acc + c;
     double y = (double)g->alpha * t;
     if (g->has_bias)
@@ -487,7 +509,7 @@ int oracle_w4a16_dequant(int w_type, int64_t N, int64_t K, int64_t gs, const uin
 int oracle_epilogue_f32(int64_t M, int64_t N, const float *T, float alpha, const float *bias,
                         int relu, int d_type, void *D)
 {
-    if (d_type != OR_F32 && d_type != OR_F16 && d_type != OR_BF16)
+    if (!is_float_out(d_type))
         return -1;
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n) {

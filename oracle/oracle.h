@@ -18,6 +18,10 @@
  *     round-to-nearest-even cast to the output type.
  *   - same page, section "Ampere: FP16/BF16 and integer MMA baseline": integer
  *     results that do not fit wrap modulo 2^32 (no saturation requested).
+ *     s8 inputs may also produce a float output (the int8 -> float dequant
+ *     epilogue): the wrapped int32 sum, then the float epilogue with an fp32
+ *     C.  FP8 outputs (E4M3 / E5M2) round to nearest even and saturate at
+ *     the largest finite value (NaN -> 0x7F).
  *   - same page, section "Dense and 2:4 structured sparse multiplication": the
  *     2:4 format keeps 2 of every 4 consecutive K positions of A, with their
  *     positions as metadata; ascending positions per the "ordered metadata"

@@ -126,7 +126,7 @@ def gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, *, a_col_major=False,
     (D_bits, Y, S): the encoded output, the fp64 pre-cast result and the
     error scale sum_k |a b| + |c|.
     """
-    integer = a_type == "s8"
+    integer = a_type == "s8" and d_type == "s32"
     c_type = "s32" if integer else "f32"
     lda, ldb, ldc, ldd = _lds(M, N, K, a_col_major, b_col_major)
     g = _desc(M, N, K, a_type, b_type, c_type, d_type, a_col_major, b_col_major,
@@ -150,7 +150,7 @@ def gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, *, a_col_major=False,
 def gemm_entries(A, B, C, bias, M, N, K, a_type, b_type, d_type, rows, cols, *,
                  a_col_major=False, b_col_major=True, alpha=1.0, relu=False):
     """The oracle definition at chosen (rows[i], cols[i]) only: (D_bits, Y, S)."""
-    integer = a_type == "s8"
+    integer = a_type == "s8" and d_type == "s32"
     c_type = "s32" if integer else "f32"
     lda, ldb, ldc, ldd = _lds(M, N, K, a_col_major, b_col_major)
     g = _desc(M, N, K, a_type, b_type, c_type, d_type, a_col_major, b_col_major,

@@ -109,3 +109,38 @@ def test_s32_encode_wraps(orc):
     x = np.array([0, 1, -1, 2 ** 31 - 1, 2 ** 31, -2 ** 31, -2 ** 31 - 1, 2 ** 32 + 5], np.float64)
     got = orc.encode("s32", x)
     assert got.tolist() == [0, 1, -1, 2 ** 31 - 1, -2 ** 31, -2 ** 31, 2 ** 31 - 1, 5]
+
+
+# ---------------------------------------------------------------- fp8 outputs
+# FP8 outputs round to nearest even and saturate at the largest finite value
+# (E4M3 has no infinity; the reading is the satfinite conversion).  Within
+# range the result must equal torch's own conversion.
+
+@pytest.mark.parametrize("t,maxv", [("e4m3", 448.0), ("e5m2", 57344.0)])
+def test_fp8_output_encode_against_torch_and_saturation(orc, t, maxv):
+    rng = np.random.default_rng(8)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 1.0, 30.0, maxv / 4)])
+    x = x[np.abs(x) <= maxv]
+    ours = orc.encode(t, x)
+    tt = torch.float8_e4m3fn if t == "e4m3" else torch.float8_e5m2
+    ref = torch.from_numpy(x.astype(np.float32)).to(tt).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+    # beyond the range: +-max, also past the rounding boundary and at infinity
+    big = np.array([maxv * 1.01, maxv * 3, 1e30, np.inf, -maxv * 1.5, -np.inf])
+    dec = orc.decode(t, orc.encode(t, big))
+    assert dec.tolist() == [maxv, maxv, maxv, maxv, -maxv, -maxv]
+    assert orc.encode(t, np.array([np.nan]))[0] == 0x7F
+
+
+def test_s8_float_output_is_the_wrapped_int32_sum(orc):
+    """int8 -> float: the int32 accumulator (wrapping modulo 2^32) as a value,
+    then C and the float epilogue."""
+    M, N, K = 2, 3, 70000  # 127*127*70000 > 2^31: the sum wraps
+    A = np.full((M, K), 127, np.int8)
+    B = np.full((N, K), 127, np.int8)
+    C = np.full((M, N), 0.5, np.float32)
+    D, Y, S = orc.gemm(A, B, C, None, M, N, K, "s8", "s8", "f32")
+    wrapped = ((127 * 127 * K + 2 ** 31) % 2 ** 32) - 2 ** 31
+    assert np.all(Y == wrapped + 0.5)
+    D2, Y2, _ = orc.gemm(A[:, :8], B[:, :8], None, None, M, N, 8, "s8", "s8", "bf16", alpha=0.25)
+    assert np.all(Y2 == 127 * 127 * 8 * 0.25)
