@@ -417,9 +417,7 @@ static int check_mx_desc(const oracle_gemm_t *g)
         return -1;
     if (g->c_type != OR_F32)
         return -1;
-    if (g->d_type != OR_F32 && g->d_type != OR_F16 && g->d_type != OR_BF16)
-        return -1;
-    return 0;
+    return is_float_out(g->d_type) ? 0 : -1;
 }
 
 /* One output of the block-scaled sum ("NVIDIA MMA", section "Blackwell:
