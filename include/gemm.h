@@ -99,24 +99,31 @@ typedef enum {
  *
  * Support matrix (everything else is GEMM_ERR_UNSUPPORTED):
  *   a, b in {F16}, {BF16}, or {F8_E4M3, F8_E5M2} (the two fp8 formats may
- *   differ): c_type F32, d_type F32 / F16 / BF16, any epilogue.
- *   a = b = S8: c_type S32, d_type S32, alpha == 1, no bias, no activation;
- *   the int32 sum wraps modulo 2^32 (no saturation).
+ *   differ): c_type F32, d_type F32 / F16 / BF16 / F8_E4M3 / F8_E5M2, any
+ *   epilogue.
+ *   a = b = S8: either c_type S32, d_type S32, alpha == 1, no bias, no
+ *   activation; or (dequantising epilogue) c_type F32, d_type F32 / F16 /
+ *   BF16 / F8_E4M3 / F8_E5M2, any epilogue, where the int32 sum is first
+ *   rounded to fp32 (to nearest even).  The int32 sum wraps modulo 2^32 (no
+ *   saturation) in both.
  *   sparse_a = 1: any of the pairs above, A row-major and packed,
  *   K % 4 == 0; used with gemm_sparse24_run (A is then given in compressed
  *   form).
  *   block_scale = 32 (MX): a, b any of F8_E4M3, F8_E5M2, F6_E2M3, F6_E3M2,
  *   F4_E2M1 (they may differ), A row-major, B column-major, K % 32 == 0,
- *   rows of whole bytes (lda, ldb in elements); c_type F32, d_type F32 /
- *   F16 / BF16, any epilogue; used with gemm_mx_run.  The 6- and 4-bit
+ *   rows of whole bytes (lda, ldb in elements); c_type F32, any float
+ *   d_type, any epilogue; used with gemm_mx_run.  The 6- and 4-bit
  *   formats exist only here.
  *   b = U4 (W4A16): a F16 or BF16, A row-major, B column-major (codes along
  *   K, ldb even), block_scale = the weight group size (a multiple of 32
- *   dividing K); c_type F32, d_type F32 / F16 / BF16, any epilogue; used
- *   with gemm_w4a16_run.
+ *   dividing K); c_type F32, any float d_type, any epilogue; used with
+ *   gemm_w4a16_run.
  * Epilogue, in fp32 for float outputs:  t = acc (+ C[m,n] if has_c);
  *   y = has_bias ? fmaf(alpha, t, bias[n]) : alpha * t;
  *   z = (act == RELU) ? (y > 0 ? y : +0) : y;  D = round-to-nearest-even(z).
+ * FP8 outputs saturate: a finite z beyond the largest finite value (448 for
+ * E4M3, 57344 for E5M2), and an infinity, become that value with z's sign;
+ * a NaN becomes the canonical NaN byte 0x7F.
  * bias is fp32, N values, one per output column. */
 typedef struct {
     int64_t M, N, K;

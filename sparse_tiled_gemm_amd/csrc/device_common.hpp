@@ -290,6 +290,37 @@ __device__ STG_AI inline float w4_scale(uint32_t bits)
               : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
+// fp32 -> OCP FP8 (E4M3 when E4, else E5M2): round to nearest even,
+// saturating at the largest finite value (448 / 57344); NaN -> 0x7F.
+template <bool E4>
+__device__ STG_AI inline uint32_t f32_to_fp8_bits(float x)
+{
+    constexpr int MB = E4 ? 3 : 2, BIAS = E4 ? 7 : 15;
+    constexpr float MAXV = E4 ? 448.0f : 57344.0f;
+    const uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
+    float a = __builtin_fabsf(x);
+    if (!(a == a))
+        return 0x7Fu;
+    a = __builtin_fminf(a, MAXV); // every value past MAXV rounds to it
+    // spacing of the format at a: 2^(e - MB), e = a's exponent (at least the
+    // smallest normal exponent, below which the spacing stays fixed)
+    int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;
+    e = e < 1 - BIAS ? 1 - BIAS : e;
+    const float q = __builtin_bit_cast(float, (uint32_t)(e - MB + 127) << 23);
+    const float r = __builtin_rintf(a / q) * q; // exact quotient, RNE
+    // encode r (0, subnormal, or normal - possibly one binade up)
+    const int er = (int)((__builtin_bit_cast(uint32_t, r) >> 23) & 0xFFu) - 127;
+    uint32_t code;
+    if (r == 0.0f)
+        code = 0;
+    else if (er < 1 - BIAS)
+        code = (uint32_t)(r / __builtin_bit_cast(float, (uint32_t)(1 - BIAS - MB + 127) << 23));
+    else
+        code = ((uint32_t)(er + BIAS) << MB) |
+               ((__builtin_bit_cast(uint32_t, r) >> (23 - MB)) & ((1u << MB) - 1));
+    return sign | code;
+}
+
 // Epilogue of one accumulator value at (row, col), both in range, for output
 // kind KIND: t = acc (+C); y = has_bias ? fmaf(alpha, t, bias[col]) : alpha*t;
 // relu; round-to-nearest-even cast and store.  Integer: D = acc + C mod 2^32.
@@ -308,21 +339,98 @@ __device__ STG_AI inline void epilogue_store(const EpiArgs &e, int64_t row, int6
         ((float *)e.D)[o] = y;
     else if constexpr (KIND == OUT_F16)
         ((uint16_t *)e.D)[o] = f32_to_f16_bits(y);
-    else
+    else if constexpr (KIND == OUT_BF16)
         ((uint16_t *)e.D)[o] = f32_to_bf16_bits(y);
+    else
+        ((uint8_t *)e.D)[o] = (uint8_t)f32_to_fp8_bits<KIND == OUT_E4M3>(y);
 }
 
+// Integer accumulator: D = acc + C mod 2^32 for int32 output; for a float
+// output (the int8 -> float epilogue) the accumulator's value (RNE to fp32)
+// goes through the float epilogue.
 template <int KIND>
 __device__ STG_AI inline void epilogue_store(const EpiArgs &e, int64_t row, int64_t col, int acc)
 {
-    uint32_t t = (uint32_t)acc;
+    if constexpr (KIND == OUT_S32) {
+        uint32_t t = (uint32_t)acc;
+        if (e.C)
+            t += (uint32_t)((const int32_t *)e.C)[row * e.ldc + col];
+        ((int32_t *)e.D)[row * e.ldd + col] = (int32_t)t;
+    } else {
+        epilogue_store<KIND>(e, row, col, (float)acc);
+    }
+}
+
+// Calls f(std::integral_constant<int, KIND>) for the output kind d_kind:
+// OUT_S32 only for integer accumulators; the FP8 kinds only when EXT
+// (kernels built without them are never planned for FP8 outputs).
+template <bool INT, bool EXT, class F>
+__device__ STG_AI inline void with_out_kind(int d_kind, F &&f)
+{
+    switch (d_kind) {
+    case OUT_F32: f(std::integral_constant<int, OUT_F32>{}); break;
+    case OUT_F16: f(std::integral_constant<int, OUT_F16>{}); break;
+    case OUT_E4M3:
+        if constexpr (EXT)
+            f(std::integral_constant<int, OUT_E4M3>{});
+        break;
+    case OUT_E5M2:
+        if constexpr (EXT)
+            f(std::integral_constant<int, OUT_E5M2>{});
+        break;
+    case OUT_S32:
+        if constexpr (INT)
+            f(std::integral_constant<int, OUT_S32>{});
+        break;
+    default: f(std::integral_constant<int, OUT_BF16>{}); break;
+    }
+}
+
+// Bytes of a D element of output kind `kind`.
+__device__ STG_AI inline int out_bytes(int kind)
+{
+    return kind == OUT_F32 || kind == OUT_S32 ? 4 : (kind == OUT_E4M3 || kind == OUT_E5M2 ? 1 : 2);
+}
+
+// The finished float value y stored as element o of D in output kind
+// `kind` (a uniform branch around the cast and store alone).
+__device__ STG_AI inline void store_kind(const EpiArgs &e, int64_t o, float y)
+{
+    switch (e.d_kind) {
+    case OUT_F32: ((float *)e.D)[o] = y; break;
+    case OUT_F16: ((uint16_t *)e.D)[o] = f32_to_f16_bits(y); break;
+    case OUT_E4M3: ((uint8_t *)e.D)[o] = (uint8_t)f32_to_fp8_bits<true>(y); break;
+    case OUT_E5M2: ((uint8_t *)e.D)[o] = (uint8_t)f32_to_fp8_bits<false>(y); break;
+    default: ((uint16_t *)e.D)[o] = f32_to_bf16_bits(y); break;
+    }
+}
+
+// epilogue_store for the output kind e.d_kind, float accumulator: the
+// epilogue arithmetic once, then the cast for the kind.
+__device__ STG_AI inline void epilogue_store_any(const EpiArgs &e, int64_t row, int64_t col, float acc)
+{
+    float t = acc;
     if (e.C)
-        t += (uint32_t)((const int32_t *)e.C)[row * e.ldc + col];
-    ((int32_t *)e.D)[row * e.ldd + col] = (int32_t)t;
+        t += ((const float *)e.C)[row * e.ldc + col];
+    float y = e.bias ? __builtin_fmaf(e.alpha, t, e.bias[col]) : e.alpha * t;
+    asm("" : "+v"(y)); // keep y an fp32 value: no fused multiply-add-convert
+    if (e.relu)
+        y = (y > 0.0f) ? y : 0.0f;
+    store_kind(e, row * e.ldd + col, y);
+}
+
+// Integer accumulator: int32 output (acc + C mod 2^32), or its value (RNE
+// to fp32) through the float epilogue.
+__device__ STG_AI inline void epilogue_store_any(const EpiArgs &e, int64_t row, int64_t col, int acc)
+{
+    if (e.d_kind == OUT_S32)
+        epilogue_store<OUT_S32>(e, row, col, acc);
+    else
+        epilogue_store_any(e, row, col, (float)acc);
 }
 
 // Store one 32x32 accumulator fragment whose top-left output is (m0, n0).
-template <class OP, int KIND>
+template <class OP>
 __device__ STG_AI inline void epilogue_fragment_k(const EpiArgs &e, const typename OP::acc_t &acc,
                                            int64_t m0, int64_t n0, int lane)
 {
@@ -333,7 +441,7 @@ __device__ STG_AI inline void epilogue_fragment_k(const EpiArgs &e, const typena
     for (int i = 0; i < 16; ++i) {
         const int64_t row = m0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
         if (row < e.M)
-            epilogue_store<KIND>(e, row, col, acc[i]);
+            epilogue_store_any(e, row, col, acc[i]);
     }
 }
 
@@ -343,23 +451,11 @@ template <class OP, int FM, int FN>
 __device__ STG_AI inline void epilogue_grid(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
                                      int64_t m0, int64_t n0, int lane)
 {
-    auto run = [&](auto kind) STG_AI {
-        constexpr int K = decltype(kind)::value;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                epilogue_fragment_k<OP, K>(e, acc[i][j], m0 + 32 * i, n0 + 32 * j, lane);
-    };
-    if constexpr (OP::INT) {
-        run(std::integral_constant<int, OUT_S32>{});
-    } else {
-        switch (e.d_kind) {
-        case OUT_F32: run(std::integral_constant<int, OUT_F32>{}); break;
-        case OUT_F16: run(std::integral_constant<int, OUT_F16>{}); break;
-        default: run(std::integral_constant<int, OUT_BF16>{}); break;
-        }
-    }
+        for (int j = 0; j < FN; ++j)
+            epilogue_fragment_k<OP>(e, acc[i][j], m0 + 32 * i, n0 + 32 * j, lane);
 }
 
 // ---------------------------------------------------------------- tile helpers
@@ -484,6 +580,11 @@ __device__ STG_AI inline void epi_store4(__amdgpu_buffer_rsrc_t rd, int voff, in
 {
     if constexpr (KIND == OUT_F32) {
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, y), rd, voff, soff, EPI_CPOL);
+    } else if constexpr (KIND == OUT_E4M3 || KIND == OUT_E5M2) {
+        constexpr bool E4 = KIND == OUT_E4M3;
+        const uint32_t w = f32_to_fp8_bits<E4>(y[0]) | (f32_to_fp8_bits<E4>(y[1]) << 8) |
+                           (f32_to_fp8_bits<E4>(y[2]) << 16) | (f32_to_fp8_bits<E4>(y[3]) << 24);
+        __builtin_amdgcn_raw_buffer_store_b32(w, rd, voff, soff, EPI_CPOL);
     } else {
         typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
         u2_t w;
@@ -522,6 +623,8 @@ __device__ STG_AI inline i4_t add_c(i4_t v, i4_t c)
 // branches, the row step between passes is a scalar offset, and all C loads
 // of a slab are issued before the slab is staged (their latency is paid
 // once per slab).  Other blocks take an element-by-element path.
+// KIND: the output kind (OUT_S32: int32 output of an integer accumulator;
+// a float kind takes integer accumulators' values, RNE to fp32, first).
 template <class OP, int FM, int FN, int KIND>
 __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
                                       int64_t m0, int64_t n0, int lane, uint32_t *lds_wave)
@@ -529,8 +632,11 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
     constexpr int COLS = 32 * FN, PITCH = COLS + 4, LPR = COLS / 4; // lanes per row
     constexpr int RPP = 64 / LPR;                                    // rows per pass
     constexpr int NP = 32 / RPP;                                     // passes per slab
-    constexpr int DB = KIND == OUT_F32 || KIND == OUT_S32 ? 4 : 2;  // D element bytes
-    typedef std::conditional_t<OP::INT, i4_t, f4_t> v4_t;
+    constexpr bool IOUT = KIND == OUT_S32;
+    constexpr int DB = IOUT || KIND == OUT_F32 ? 4 : (KIND == OUT_E4M3 || KIND == OUT_E5M2 ? 1 : 2);
+    // what the LDS slab holds: int32 sums for an int32 output, else fp32
+    // values (integer accumulators converted, RNE, as they are staged)
+    typedef std::conditional_t<IOUT, i4_t, f4_t> v4_t;
     // m0 and n0 are the same in every lane; saying so keeps the buffer
     // resources built from them in scalar registers
     m0 = wave_uniform(m0);
@@ -554,14 +660,15 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
     const int vd = rl * ldd_b + (int)(col * DB);
     const int vc = rl * ldc_b + (int)(col * 4);
     f4_t bv{};
-    if constexpr (!OP::INT) {
+    if constexpr (!IOUT) {
         if (fast && e.bias)
             bv = *(const f4_t *)(e.bias + col);
     }
 
-    // fully unrolled, so the accumulator indices are constants
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    // one slab per fragment row i, expanded at compile time so that the
+    // accumulator indices are constants however large the body
+    auto slab = [&](auto ic) STG_AI {
+        constexpr int i = decltype(ic)::value;
         // keep each slab's C loads from being hoisted above earlier slabs
         // (that would need C registers for the whole block at once)
         __builtin_amdgcn_sched_barrier(0);
@@ -581,22 +688,26 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
                 // copy the element out first: a bit_cast applied to a
                 // vector-element expression would read element 0
                 const auto x = acc[i][j][r];
-                lds_wave[row * PITCH + j * 32 + (lane & 31)] = __builtin_bit_cast(uint32_t, x);
+                if constexpr (IOUT || !OP::INT)
+                    lds_wave[row * PITCH + j * 32 + (lane & 31)] = __builtin_bit_cast(uint32_t, x);
+                else
+                    lds_wave[row * PITCH + j * 32 + (lane & 31)] = __builtin_bit_cast(uint32_t, (float)x);
             }
         wave_lds_sync(); // the slab is in LDS
         if (fast) {
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
                 const int rr = p * RPP + rl;
-                v4_t v = __builtin_bit_cast(v4_t, *(const u4_t *)(lds_wave + rr * PITCH + c4));
-                if (has_c)
-                    v = add_c(v, __builtin_bit_cast(v4_t, cv[p]));
+                const v4_t v = __builtin_bit_cast(v4_t, *(const u4_t *)(lds_wave + rr * PITCH + c4));
                 const int soff = (32 * i + p * RPP) * ldd_b;
-                if constexpr (OP::INT)
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v), rd, vd, soff,
+                if constexpr (IOUT) {
+                    const v4_t w = has_c ? add_c(v, __builtin_bit_cast(v4_t, cv[p])) : v;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, w), rd, vd, soff,
                                                            EPI_CPOL);
-                else
-                    epi_store4<KIND>(rd, vd, soff, epi_affine(e, v, bv));
+                } else {
+                    const f4_t f = has_c ? add_c(v, __builtin_bit_cast(f4_t, cv[p])) : v;
+                    epi_store4<KIND>(rd, vd, soff, epi_affine(e, f, bv));
+                }
             }
         } else {
             for (int p = 0; p < NP; ++p) {
@@ -606,29 +717,29 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
                 if (row < e.M) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        if (col + q < e.N)
+                        if (col + q < e.N) {
                             epilogue_store<KIND>(e, row, col + q, v[q]);
+                        }
                 }
             }
         }
         wave_lds_sync(); // reads done before the next slab overwrites
-    }
+    };
+    [&]<int... I>(std::integer_sequence<int, I...>) STG_AI {
+        (slab(std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, FM>{});
 }
 
 
-template <class OP, int FM, int FN>
+// EXT: also the FP8 output kinds (the tuning-only kernel variants are built
+// without them).
+template <class OP, int FM, int FN, bool EXT = true>
 __device__ STG_AI inline void epilogue_grid_lds(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
                                          int64_t m0, int64_t n0, int lane, uint32_t *lds_wave)
 {
-    if constexpr (OP::INT) {
-        epilogue_slabs<OP, FM, FN, OUT_S32>(e, acc, m0, n0, lane, lds_wave);
-    } else {
-        switch (e.d_kind) {
-        case OUT_F32: epilogue_slabs<OP, FM, FN, OUT_F32>(e, acc, m0, n0, lane, lds_wave); break;
-        case OUT_F16: epilogue_slabs<OP, FM, FN, OUT_F16>(e, acc, m0, n0, lane, lds_wave); break;
-        default: epilogue_slabs<OP, FM, FN, OUT_BF16>(e, acc, m0, n0, lane, lds_wave); break;
-        }
-    }
+    with_out_kind<OP::INT, EXT>(e.d_kind, [&](auto kind) STG_AI {
+        epilogue_slabs<OP, FM, FN, decltype(kind)::value>(e, acc, m0, n0, lane, lds_wave);
+    });
 }
 
 } // namespace stg

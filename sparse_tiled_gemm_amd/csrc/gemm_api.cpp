@@ -58,6 +58,7 @@ const char *mx_name(int sel)
     return sel >= 0 && sel < 5 ? n[sel] : "?";
 }
 bool is_float_in(int t) { return t == GEMM_F16 || t == GEMM_BF16 || is_fp8(t); }
+bool is_float_out(int t) { return t == GEMM_F32 || t == GEMM_F16 || t == GEMM_BF16 || is_fp8(t); }
 int elem_bytes(int t)
 {
     switch (t) {
@@ -98,6 +99,8 @@ int out_kind(int d)
     case GEMM_F32: return OUT_F32;
     case GEMM_F16: return OUT_F16;
     case GEMM_BF16: return OUT_BF16;
+    case GEMM_F8_E4M3: return OUT_E4M3;
+    case GEMM_F8_E5M2: return OUT_E5M2;
     default: return OUT_S32;
     }
 }
@@ -275,8 +278,8 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
             return fail(GEMM_ERR_UNSUPPORTED, "W4A16: packed weight rows must be whole bytes");
         if (!(d.c_type == GEMM_F32 || (d.c_type == 0 && !d.has_c)))
             return fail(GEMM_ERR_UNSUPPORTED, "float inputs take an f32 C");
-        if (d.d_type != GEMM_F32 && d.d_type != GEMM_F16 && d.d_type != GEMM_BF16)
-            return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16 or bf16");
+        if (!is_float_out(d.d_type))
+            return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16, bf16 or fp8");
         return ok();
     }
     if (d.block_scale != 0 && d.block_scale != 32)
@@ -299,8 +302,8 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
             return fail(GEMM_ERR_UNSUPPORTED, "packed rows must be whole bytes");
         if (!(d.c_type == GEMM_F32 || (d.c_type == 0 && !d.has_c)))
             return fail(GEMM_ERR_UNSUPPORTED, "float inputs take an f32 C");
-        if (d.d_type != GEMM_F32 && d.d_type != GEMM_F16 && d.d_type != GEMM_BF16)
-            return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16 or bf16");
+        if (!is_float_out(d.d_type))
+            return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16, bf16 or fp8");
         return ok();
     }
     if (d.a_type > GEMM_S32 || d.b_type > GEMM_S32)
@@ -311,12 +314,18 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
     if (d.a_type == GEMM_S8 || d.b_type == GEMM_S8) {
         if (d.a_type != GEMM_S8 || d.b_type != GEMM_S8)
             return fail(GEMM_ERR_UNSUPPORTED, "s8 must be paired with s8");
-        if (!(d.c_type == GEMM_S32 || (d.c_type == 0 && !d.has_c)))
-            return fail(GEMM_ERR_UNSUPPORTED, "s8 inputs take an s32 C");
-        if (d.d_type != GEMM_S32)
-            return fail(GEMM_ERR_UNSUPPORTED, "s8 inputs produce s32 output");
-        if (d.alpha != 1.0f || d.has_bias || d.act != GEMM_ACT_NONE)
-            return fail(GEMM_ERR_UNSUPPORTED, "s32 output takes no alpha, bias or activation");
+        if (d.d_type == GEMM_S32) {
+            if (!(d.c_type == GEMM_S32 || (d.c_type == 0 && !d.has_c)))
+                return fail(GEMM_ERR_UNSUPPORTED, "s32 output takes an s32 C");
+            if (d.alpha != 1.0f || d.has_bias || d.act != GEMM_ACT_NONE)
+                return fail(GEMM_ERR_UNSUPPORTED, "s32 output takes no alpha, bias or activation");
+        } else {
+            // the int8 -> float epilogue: the int32 sum through the float epilogue
+            if (!is_float_out(d.d_type))
+                return fail(GEMM_ERR_UNSUPPORTED, "s8 inputs produce s32 or a float output");
+            if (!(d.c_type == GEMM_F32 || (d.c_type == 0 && !d.has_c)))
+                return fail(GEMM_ERR_UNSUPPORTED, "a float output takes an f32 C");
+        }
     } else {
         if (!is_float_in(d.a_type) || !is_float_in(d.b_type))
             return fail(GEMM_ERR_UNSUPPORTED, "A/B must be f16, bf16, fp8 or s8");
@@ -325,8 +334,8 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
                                               "bf16/bf16 or fp8/fp8)");
         if (!(d.c_type == GEMM_F32 || (d.c_type == 0 && !d.has_c)))
             return fail(GEMM_ERR_UNSUPPORTED, "float inputs take an f32 C");
-        if (d.d_type != GEMM_F32 && d.d_type != GEMM_F16 && d.d_type != GEMM_BF16)
-            return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16 or bf16");
+        if (!is_float_out(d.d_type))
+            return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16, bf16 or fp8");
     }
     if (d.sparse_a) {
         // every supported pair has a 2:4 form (the A/B pairs above)
@@ -509,11 +518,19 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     // Tuning override: STGEMM_FORCE_KERNEL=<family name> replaces the choice
     // for descriptors that family can serve (ignored otherwise).
     if (const char *force = getenv("STGEMM_FORCE_KERNEL")) {
-        for (int f = 0; f < KF_COUNT; ++f)
+        // the direct-copy, ping-pong and 128-byte-K variants are built
+        // without the FP8 output kinds
+        const bool tuning_only_ok = !is_fp8(d.d_type);
+        for (int f = 0; f < KF_COUNT; ++f) {
+            const bool tuning_only = f == KF_TILED_DMA4 || f == KF_TILED_DMA5 ||
+                                     f == KF_PINGPONG4 || f == KF_PINGPONG5 || f == KF_TILED_256W8L;
             if (strcmp(force, family_name(f)) == 0 &&
-                (f == KF_GENERIC || (tiled && is_tiled(f) && (f != KF_TILED_256W8L || long_k)) ||
+                (f == KF_GENERIC ||
+                 (tiled && is_tiled(f) && (f != KF_TILED_256W8L || long_k) &&
+                  (!tuning_only || tuning_only_ok)) ||
                  (skinny && f == KF_SKINNY)))
                 fam = f;
+        }
     }
     p->family = fam;
     snprintf(p->name, sizeof p->name, "%s_%s", family_name(fam), op_name(p->op));

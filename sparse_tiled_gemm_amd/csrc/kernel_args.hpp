@@ -5,7 +5,7 @@
 
 namespace stg {
 
-enum OutKind { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2, OUT_S32 = 3 };
+enum OutKind { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2, OUT_S32 = 3, OUT_E4M3 = 4, OUT_E5M2 = 5 };
 
 // Epilogue inputs.  C == nullptr: no C term; bias == nullptr: no bias.
 struct EpiArgs {

@@ -569,7 +569,7 @@ __global__ __launch_bounds__(256, 1) void k_tiled_dma(GemmArgs g, int tiles_m, i
     STG_WAIT_VMCNT(0); // drain the requests past the last tile before exit
     __syncthreads();   // every wave is done with the LDS stages
 
-    epilogue_grid_lds<OP, FM, FN>(g.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
+    epilogue_grid_lds<OP, FM, FN, false>(g.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
                                   (uint32_t *)lds + wave * 32 * (WN + 4));
 }
 
@@ -733,7 +733,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled_w8l(GemmArgs g, int tiles_m, i
     }
 
     __syncthreads(); // every wave is done with the LDS stages
-    epilogue_grid_lds<OP, FM, FN>(g.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
+    epilogue_grid_lds<OP, FM, FN, false>(g.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
                                   (uint32_t *)lds + wave * 32 * (WN + 4));
 }
 
@@ -877,7 +877,7 @@ __global__ __launch_bounds__(512, 1) void k_pingpong(GemmArgs g, int tiles_m, in
     }
     STG_WAIT_VMCNT(0);
     __syncthreads();
-    epilogue_grid_lds<OP, FM, FN>(g.e, acc, m_blk + wm * WM, n_blk + grp * 128 + wn * WN, lane,
+    epilogue_grid_lds<OP, FM, FN, false>(g.e, acc, m_blk + wm * WM, n_blk + grp * 128 + wn * WN, lane,
                                   (uint32_t *)lds + wave * 32 * (WN + 4));
 }
 
@@ -1022,23 +1022,11 @@ __global__ __launch_bounds__(512, 1) void k_skinny(GemmArgs g)
                         t[i] += __builtin_bit_cast(float, u);
                 }
             const int64_t col = n_blk + 16 * f + (lane & 15);
-            auto store = [&](auto kind) STG_AI {
-                constexpr int KD = decltype(kind)::value;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t r = 4 * (lane >> 4) + i;
-                    if (r < g.e.M && col < g.e.N)
-                        epilogue_store<KD>(g.e, r, col, t[i]);
-                }
-            };
-            if constexpr (OP::INT) {
-                store(std::integral_constant<int, OUT_S32>{});
-            } else {
-                switch (g.e.d_kind) {
-                case OUT_F32: store(std::integral_constant<int, OUT_F32>{}); break;
-                case OUT_F16: store(std::integral_constant<int, OUT_F16>{}); break;
-                default: store(std::integral_constant<int, OUT_BF16>{}); break;
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int64_t r = 4 * (lane >> 4) + i;
+                if (r < g.e.M && col < g.e.N)
+                    epilogue_store_any(g.e, r, col, t[i]);
             }
         }
     }

@@ -136,7 +136,7 @@ def make_desc(M, N, K, a_type, b_type, d_type, *, c_type=None, has_c=True, has_b
               alpha=1.0, act="none", a_layout="row", b_layout="col", lda=0, ldb=0, ldc=0,
               ldd=0, sparse_a=False, algo="auto", block_scale=0):
     """Build a gemm_desc_t from readable arguments (type names as in DTYPES)."""
-    integer = a_type == "s8"
+    integer = a_type == "s8" and d_type == "s32"
     if c_type is None:
         c_type = "s32" if integer else "f32"
     d = gemm_desc_t()

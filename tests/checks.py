@@ -8,14 +8,18 @@
   (distance of the ordered bit patterns), or, where fp32 accumulation error
   alone can exceed one output ulp (results near 0),
   |D - Y| <= ulp_out(Y) + tol * |alpha| * S.
-tol = 1e-5 for fp16/bf16 inputs and 1e-4 for fp8 inputs (and the MX formats).
+tol = 1e-5 for fp16/bf16 inputs and 1e-4 for fp8 inputs (and the MX formats); 1e-6
+for s8 inputs with a float output (the int32 sum is exact; only its fp32
+conversion and the epilogue round).
+- fp8 outputs: within 1 ulp of the format, or the bound above with an fp8 ulp;
+  results beyond the largest finite value must equal the saturated value.
 """
 import numpy as np
 
 from exact import lib_decode
 
 TOL = {"f16": 1e-5, "bf16": 1e-5, "e4m3": 1e-4, "e5m2": 1e-4, "e2m3": 1e-4, "e3m2": 1e-4,
-       "e2m1": 1e-4}
+       "e2m1": 1e-4, "s8": 1e-6}
 
 
 def ordered16(bits):
@@ -27,6 +31,21 @@ def ulp16(y, d_type):
     """Spacing of fp16 / bf16 values at |y|."""
     a = np.abs(np.asarray(y, dtype=np.float64))
     fbits, emin = (10, -14) if d_type == "f16" else (7, -126)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, emin)
+    return np.ldexp(1.0, (e - fbits).astype(np.int64))
+
+
+def ordered8(bits):
+    b = np.asarray(bits).astype(np.uint8).astype(np.int64)
+    return np.where(b & 0x80, -(b & 0x7F), b)
+
+
+def ulp8(y, d_type):
+    """Spacing of E4M3 / E5M2 values at |y|."""
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    fbits, emin = (3, -6) if d_type == "e4m3" else (2, -14)
     with np.errstate(divide="ignore"):
         e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
     e = np.maximum(e, emin)
@@ -81,19 +100,31 @@ def check(D, d_type, D_ref, Y, S, in_type, alpha=1.0):
                 det = "first bad flat %d: D=%r Y=%r S=%r" % (i, d.reshape(-1)[i], Y.reshape(-1)[i],
                                                             S.reshape(-1)[i])
             return Result(nb == 0, n, float(norm.max()) if n else 0.0, 0, nb, det)
-        d = lib_decode(d_type, np.asarray(D).astype(np.uint16))
-        dist = np.abs(ordered16(D) - ordered16(D_ref))
-        first = dist <= 1
-        err = np.abs(d - Y)
-        second = err <= ulp16(Y, d_type) + tol * scale
+        if d_type in ("e4m3", "e5m2"):
+            # FP8 outputs: 1 ulp of the format (ordered 8-bit codes), or the
+            # accumulation bound; results past the largest finite value
+            # must be that value exactly (saturation)
+            d = lib_decode(d_type, np.asarray(D).astype(np.uint8))
+            dist = np.abs(ordered8(D) - ordered8(D_ref))
+            vmax = 448.0 if d_type == "e4m3" else 57344.0
+            sat = np.abs(Y) >= vmax
+            first = (dist <= 1) & ~sat | (sat & (np.asarray(D) == np.asarray(D_ref)))
+            err = np.abs(d - Y)
+            second = ~sat & (err <= ulp8(Y, d_type) + tol * scale)
+        else:
+            d = lib_decode(d_type, np.asarray(D).astype(np.uint16))
+            dist = np.abs(ordered16(D) - ordered16(D_ref))
+            first = dist <= 1
+            err = np.abs(d - Y)
+            second = err <= ulp16(Y, d_type) + tol * scale
         ok = first | second
         norm = np.where(scale > 0, err / np.where(scale > 0, scale, 1), 0.0)
         nb = int((~ok).sum())
         det = ""
         if nb:
             i = np.flatnonzero(~ok.reshape(-1))[0]
-            det = "first bad flat %d: D=%r Dref=%r Y=%r S=%r" % (
-                i, d.reshape(-1)[i], lib_decode(d_type, np.asarray(D_ref).astype(np.uint16)).reshape(-1)[i],
-                Y.reshape(-1)[i], S.reshape(-1)[i])
+            det = "first bad flat %d: D=%r Dref bits=%r Y=%r S=%r" % (
+                i, d.reshape(-1)[i], np.asarray(D_ref).reshape(-1)[i], Y.reshape(-1)[i],
+                S.reshape(-1)[i])
         return Result(nb == 0, n, float(norm.max()) if n else 0.0, int((~first & second).sum()),
                       nb, det)

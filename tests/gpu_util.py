@@ -8,7 +8,8 @@ import torch
 from sparse_tiled_gemm_amd import gemm as G
 
 _VIEW = {1: np.uint8, 2: np.int16, 4: np.int32, 8: np.int64}
-OUT_NP = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "s32": np.int32}
+OUT_NP = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "s32": np.int32,
+          "e4m3": np.uint8, "e5m2": np.uint8}
 
 
 def say(*a):

@@ -56,16 +56,20 @@ def _ok(**kw):
     (dict(a_type="s8", b_type="s8", d_type="s32", alpha=2.0), G.GEMM_ERR_UNSUPPORTED),
     (dict(a_type="s8", b_type="s8", d_type="s32", has_bias=True), G.GEMM_ERR_UNSUPPORTED),
     (dict(a_type="s8", b_type="s8", d_type="s32", act="relu"), G.GEMM_ERR_UNSUPPORTED),
-    (dict(a_type="s8", b_type="s8", d_type="f32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="s8", b_type="s8", d_type="f32"), G.GEMM_OK),          # int8 -> float
+    (dict(a_type="s8", b_type="s8", d_type="e4m3", alpha=0.5, act="relu"), G.GEMM_OK),
+    (dict(a_type="s8", b_type="s8", d_type="bf16", c_type="s32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="bf16", b_type="bf16", d_type="e5m2"), G.GEMM_OK),      # fp8 output
+    (dict(a_type="e4m3", b_type="e5m2", d_type="e4m3", has_c=False), G.GEMM_OK),
     (dict(d_type="s32"), G.GEMM_ERR_UNSUPPORTED),
-    (dict(d_type="e4m3"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(d_type="e2m1"), G.GEMM_ERR_UNSUPPORTED),
     (dict(c_type="bf16"), G.GEMM_ERR_UNSUPPORTED),
     (dict(sparse_a=True), G.GEMM_OK),                  # 2:4 bf16
     (dict(sparse_a=True, a_type="s8", b_type="s8", d_type="s32"), G.GEMM_OK),
     (dict(sparse_a=True, a_type="e4m3", b_type="e5m2", d_type="f16"), G.GEMM_OK),
     (dict(sparse_a=True, a_type="e5m2", b_type="e5m2", d_type="f32"), G.GEMM_OK),
     (dict(sparse_a=True, a_type="f16", b_type="bf16", d_type="f32"), G.GEMM_ERR_UNSUPPORTED),
-    (dict(sparse_a=True, a_type="s8", b_type="s8", d_type="f32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(sparse_a=True, a_type="s8", b_type="s8", d_type="f32"), G.GEMM_OK),
     (dict(sparse_a=True, a_type="f16", b_type="f16", K=66), G.GEMM_ERR_UNSUPPORTED),
     (dict(sparse_a=True, a_type="f16", b_type="f16", a_layout="col"), G.GEMM_ERR_UNSUPPORTED),
     (dict(sparse_a=True, a_type="f16", b_type="f16", d_type="f32"), G.GEMM_OK),

@@ -1,0 +1,162 @@
+"""GPU parity of the output signatures beyond the basic ones: FP8 (E4M3 /
+E5M2) outputs of every kernel family (round to nearest even, saturating),
+and the int8 -> float epilogue (s8 inputs, int32 sum, float output) -
+against the oracle, and each fused epilogue bit for bit against the
+oracle's fp32 epilogue applied to the same kernel's fp32 output."""
+import numpy as np
+import pytest
+import torch
+
+from checks import check
+from gpu_util import gpu_compress, gpu_gemm, gpu_sparse_gemm, say, to_dev
+from sparse_tiled_gemm_amd import gemm as G
+from sparse_tiled_gemm_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+FP8 = ["e4m3", "e5m2"]
+
+
+def _bias(N, seed=7):
+    return np.random.default_rng(seed).standard_normal(N).astype(np.float32)
+
+
+def _dense(a_type, M, N, K):
+    if a_type == "bf16":
+        return inputs.dense_bf16(M, N, K, d_type="f32")
+    if a_type == "f16":
+        return inputs.dense_f16(M, N, K)
+    if a_type == "s8":
+        return inputs.dense_s8(M, N, K)
+    return inputs.dense_fp8(M, N, K)
+
+
+def _fused_vs_f32(orc, run, d_type, alpha, bias, relu):
+    """run(d_type, alpha, bias, relu) -> D bits; the fused result must equal the
+    oracle's fp32 epilogue on the same kernel's fp32 output."""
+    T = run("f32", 1.0, None, False)
+    D = run(d_type, alpha, bias, relu)
+    ref = orc.epilogue_f32(T, alpha, bias, relu, d_type)
+    return int((D != ref).sum())
+
+
+# (family forced, a_type, shape): the float kernels with an fp8 output
+DENSE_FAMILIES = [("tiled256w8", "bf16", (300, 520, 256)), ("tiled256", "e4m3", (384, 264, 512)),
+                  ("tiled128", "f16", (130, 200, 128)), ("generic", "bf16", (67, 45, 96)),
+                  ("skinny", "bf16", (16, 300, 1024))]
+
+
+@pytest.mark.parametrize("fam,a_type,shape", DENSE_FAMILIES, ids=[f[0] for f in DENSE_FAMILIES])
+@pytest.mark.parametrize("d_type", FP8)
+def test_dense_fp8_output(orc, monkeypatch, fam, a_type, shape, d_type):
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", fam)
+    M, N, K = shape
+    p = _dense(a_type, M, N, K)
+    bias = _bias(N)
+    # scale results toward the fp8 range: 30 (e4m3) / 2000 (e5m2) times the
+    # unit-variance sums, so some outputs saturate
+    alpha = 30.0 if d_type == "e4m3" else 2000.0
+    if a_type == "e4m3":
+        alpha *= p["alpha"]
+
+    def run(dt, al, bi, relu):
+        D, name = gpu_gemm(p["A"], p["B"], p["C"], bi, M, N, K, p["a_type"], p["b_type"], dt,
+                           alpha=al, relu=relu)
+        assert name.startswith(fam), name
+        return D
+    D = run(d_type, alpha, bias, True)
+    Dr, Y, S = orc.gemm(p["A"], p["B"], p["C"], bias, M, N, K, p["a_type"], p["b_type"], d_type,
+                        alpha=alpha, relu=True)
+    r = check(D, d_type, Dr, Y, S, p["a_type"], alpha)
+    say(fam, d_type, r, "saturated:", int((np.abs(Y) >= (448 if d_type == "e4m3" else 57344)).sum()))
+    assert r.ok, r
+    assert _fused_vs_f32(orc, run, d_type, alpha, bias, True) == 0
+
+
+S8_FAMILIES = [("tiled256w8t", (300, 520, 256)), ("tiled128", (130, 200, 128)),
+               ("generic", (67, 45, 96)), ("skinny", (16, 300, 1024))]
+
+
+@pytest.mark.parametrize("fam,shape", S8_FAMILIES, ids=[f[0] for f in S8_FAMILIES])
+@pytest.mark.parametrize("d_type", ["f32", "bf16", "f16", "e4m3"])
+def test_s8_dequant_epilogue(orc, monkeypatch, fam, shape, d_type):
+    """s8 x s8 -> int32 sum -> float output with C (fp32), alpha, bias, relu."""
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", fam)
+    M, N, K = shape
+    p = inputs.dense_s8(M, N, K)
+    C = np.random.default_rng(9).uniform(-1e4, 1e4, (M, N)).astype(np.float32)
+    bias = _bias(N) * 100
+    alpha = 1.0 / 4096 if d_type == "e4m3" else 1.0 / 512
+
+    def run(dt, al, bi, relu):
+        D, name = gpu_gemm(p["A"], p["B"], C, bi, M, N, K, "s8", "s8", dt, alpha=al, relu=relu)
+        assert name.startswith(fam), name
+        return D
+    D = run(d_type, alpha, bias, True)
+    Dr, Y, S = orc.gemm(p["A"], p["B"], C, bias, M, N, K, "s8", "s8", d_type, alpha=alpha,
+                        relu=True)
+    r = check(D, d_type, Dr, Y, S, "s8", alpha)
+    say(fam, d_type, r)
+    assert r.ok, r
+    if d_type != "f32":
+        assert _fused_vs_f32(orc, run, d_type, alpha, bias, True) == 0
+
+
+@pytest.mark.parametrize("t", ["f16", "s8"])
+def test_sparse_outputs(orc, t):
+    """2:4 kernels (8-wave and generic): f16 A -> e4m3, s8 A -> bf16."""
+    M, N, K = 300, 264, 512
+    p = inputs.sparse24(t, M, N, K)
+    d_type = "e4m3" if t == "f16" else "bf16"
+    C = p["C"].astype(np.float32) if t == "f16" else \
+        np.random.default_rng(5).uniform(-1e4, 1e4, (M, N)).astype(np.float32)
+    alpha = 30.0 if t == "f16" else 1.0 / 512
+    vals, meta, _, _ = gpu_compress(p["A_logical"], t)
+    for algo in ("tiled", "generic"):
+        D, name = gpu_sparse_gemm(vals, meta, p["B"], C, M, N, K, d_type, algo=algo, alpha=alpha,
+                                  a_type=t)
+        Dr, Y, S = orc.gemm(p["A_logical"], p["B"], C, None, M, N, K, t, t, d_type, alpha=alpha)
+        r = check(D, d_type, Dr, Y, S, t, alpha)
+        say("sparse", t, algo, name, r)
+        assert r.ok, r
+
+
+def test_mx_and_w4_fp8_outputs(orc):
+    """The MX tiled kernel and the W4A16 tiled / skinny kernels with an E4M3 output."""
+    M, N, K = 256, 256, 512
+    p = inputs.mx_problem(M, N, K, "e4m3", "e4m3", workload=70, d_type="f32")
+    desc = G.make_desc(M, N, K, "e4m3", "e4m3", "e4m3", has_c=False, alpha=4.0, block_scale=32)
+    plan = G.gemm_plan(desc)
+    D = torch.empty(M * N, dtype=torch.uint8, device="cuda")
+    G.gemm_mx_run(plan, to_dev(p["A"]), to_dev(p["SA"]), to_dev(p["B"]), to_dev(p["SB"]), None,
+                  None, D)
+    torch.cuda.synchronize()
+    Dr, Y, S = orc.mx_gemm(p["A"], p["SA"], p["B"], p["SB"], None, None, M, N, K, "e4m3", "e4m3",
+                           "e4m3", alpha=4.0)
+    r = check(D.cpu().numpy().reshape(M, N), "e4m3", Dr, Y, S, "e4m3", 4.0)
+    assert plan.name.startswith("mx_tiled") and r.ok, (plan.name, r)
+    for Mw in (256, 16):
+        q = inputs.w4a16_problem(Mw, N, K, "bf16", 128, workload=71)
+        desc = G.make_desc(Mw, N, K, "bf16", "u4", "e5m2", has_c=False, alpha=100.0,
+                           block_scale=128)
+        plan = G.gemm_plan(desc)
+        D = torch.empty(Mw * N, dtype=torch.uint8, device="cuda")
+        G.gemm_w4a16_run(plan, to_dev(q["A"]), to_dev(q["B"]), to_dev(q["scales"]),
+                         to_dev(q["zeros"]), None, None, D)
+        torch.cuda.synchronize()
+        W = orc.w4a16_dequant(q["B"], q["scales"], q["zeros"], N, K, 128, "bf16")
+        Dr, Y, S = orc.gemm(q["A"], W, None, None, Mw, N, K, "bf16", "bf16", "e5m2", alpha=100.0)
+        r = check(D.cpu().numpy().reshape(Mw, N), "e5m2", Dr, Y, S, "bf16", 100.0)
+        say("w4", plan.name, r)
+        assert r.ok, r
+
+
+@pytest.mark.parametrize("fam", ["pingpong4", "tiled256dma4", "tiled256w8l"])
+def test_tuning_only_families_refuse_fp8_outputs(monkeypatch, fam):
+    """Those variants are built without the FP8 output kinds: forcing them for
+    an FP8 output keeps the plan's own choice."""
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", fam)
+    bf = G.gemm_plan(G.make_desc(512, 512, 512, "bf16", "bf16", "bf16", has_c=False))
+    assert bf.name.startswith(fam)
+    f8 = G.gemm_plan(G.make_desc(512, 512, 512, "bf16", "bf16", "e4m3", has_c=False))
+    assert not f8.name.startswith(fam), f8.name
