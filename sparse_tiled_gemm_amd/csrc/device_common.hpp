@@ -174,6 +174,33 @@ struct OpW4 : Base {
     static constexpr bool W4 = true;
 };
 
+// Operands stored MN-major ("CUDA 014 - MMA 指令的用法详解", section "加载时转置":
+// a load that transposes as it reads fits an operand whose memory order is
+// the transpose of the MMA's register order): A column-major (M contiguous)
+// and / or B row-major (N contiguous), 16-bit types, in the LDS-tiled
+// kernel.  The tile keeps its memory order in LDS (K rows of MN values) and
+// the fragments are fetched with the transposing LDS read.
+template <class Base, bool AM, bool BM>
+struct OpMN : Base {
+    static constexpr bool A_MN = AM, B_MN = BM;
+};
+template <class OP>
+constexpr bool a_mn_v()
+{
+    if constexpr (requires { OP::A_MN; })
+        return OP::A_MN;
+    else
+        return false;
+}
+template <class OP>
+constexpr bool b_mn_v()
+{
+    if constexpr (requires { OP::B_MN; })
+        return OP::B_MN;
+    else
+        return false;
+}
+
 // 16x16 MFMA forms (skinny kernel).  Lane l holds row (or column) l % 16 and
 // LANE_BYTES K bytes; accumulator register i of lane l is row 4 (l / 16) + i,
 // column l % 16.  KB16 = K bytes one instruction consumes (4 lane groups).
@@ -471,6 +498,24 @@ __device__ STG_AI inline __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, int6
 __device__ STG_AI inline u4_t buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
 {
     return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Transposing 8-byte LDS read of 16-bit values (ds_read_b64_tr_b16), lane
+// layout as measured on gfx950: inside each group of 16 lanes, lane i
+// fetches the four values at its own address, and lane j receives value
+// j % 4 of lane 4 e + j / 4 in result slot e (e = 0..3).  So when lane i of
+// a group addresses row i / 4, columns 4 (i % 4) .. 4 (i % 4) + 3 of a 4 x 16
+// block stored by rows, lane j receives column j, rows 0..3: four
+// consecutive K values of one M (or N) index, the MFMA operand order.
+__device__ STG_AI inline void lds_read_tr16(const uint8_t *p, uint32_t *w)
+{
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+    const s4_t r =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t *)p);
+    const u2_t v = __builtin_bit_cast(u2_t, r);
+    w[0] = v.x;
+    w[1] = v.y;
 }
 
 // 16-byte chunk slot inside a 64-byte LDS row: chunk c of row r sits at slot

@@ -159,12 +159,22 @@ gemm_status_t check_device(int *dev_out, DeviceInfo *info_out)
 // Can the LDS-tiled kernel serve this descriptor (ignoring pointer alignment)?
 bool tiled_ok(const gemm_desc_t &d)
 {
-    // 64-byte K tiles; 32-bit buffer offsets cover 256 rows plus the K extent
+    // 64-byte K tiles, 16-byte rows; 32-bit buffer offsets cover 256 rows
+    // plus the K extent.  An MN-major operand (A column-major, B row-major;
+    // 16-bit types only) is read in 16-byte chunks along M (N), which must
+    // not straddle the end of the data (M, N multiples of 8), and its whole
+    // offset, K rows included, goes through 32 bits.
     const int eb = elem_bytes(d.a_type);
     const int64_t lim = (int64_t)1 << 30;
-    return d.a_layout == GEMM_ROW_MAJOR && d.b_layout == GEMM_COL_MAJOR && d.K > 0 &&
-           (d.K * eb) % 64 == 0 && (d.lda * eb) % 16 == 0 && (d.ldb * eb) % 16 == 0 &&
-           d.lda * eb * 256 < lim && d.ldb * eb * 256 < lim;
+    const bool a_mn = d.a_layout == GEMM_COL_MAJOR, b_mn = d.b_layout == GEMM_ROW_MAJOR;
+    if ((a_mn || b_mn) && eb != 2)
+        return false;
+    const bool a_ok = a_mn ? d.M % 8 == 0 && (d.K + 128) * d.lda * eb < lim
+                           : d.lda * eb * 256 < lim;
+    const bool b_ok = b_mn ? d.N % 8 == 0 && (d.K + 128) * d.ldb * eb < lim
+                           : d.ldb * eb * 256 < lim;
+    return d.K > 0 && (d.K * eb) % 64 == 0 && (d.lda * eb) % 16 == 0 && (d.ldb * eb) % 16 == 0 &&
+           a_ok && b_ok;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -489,6 +499,7 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     }
 
     const bool tiled = tiled_ok(d);
+    const int layout = (d.a_layout == GEMM_COL_MAJOR ? 1 : 0) | (d.b_layout == GEMM_ROW_MAJOR ? 2 : 0);
     // K in whole 128-byte tiles (the 128-byte-K-tile kernel)
     const bool long_k = tiled && (d.K * elem_bytes(d.a_type)) % 128 == 0;
     const bool skinny = skinny_ok(d);
@@ -520,20 +531,26 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     if (const char *force = getenv("STGEMM_FORCE_KERNEL")) {
         // the direct-copy, ping-pong and 128-byte-K variants are built
         // without the FP8 output kinds
+        // without the FP8 output kinds; MN-major operands only on the
+        // 8-wave 256 x 256 and the 128 x 128 tiles
         const bool tuning_only_ok = !is_fp8(d.d_type);
         for (int f = 0; f < KF_COUNT; ++f) {
             const bool tuning_only = f == KF_TILED_DMA4 || f == KF_TILED_DMA5 ||
                                      f == KF_PINGPONG4 || f == KF_PINGPONG5 || f == KF_TILED_256W8L;
+            const bool layout_ok = layout == 0 || f == KF_TILED_256W8 || f == KF_TILED_128;
             if (strcmp(force, family_name(f)) == 0 &&
                 (f == KF_GENERIC ||
                  (tiled && is_tiled(f) && (f != KF_TILED_256W8L || long_k) &&
-                  (!tuning_only || tuning_only_ok)) ||
+                  (!tuning_only || tuning_only_ok) && layout_ok) ||
                  (skinny && f == KF_SKINNY)))
                 fam = f;
         }
     }
     p->family = fam;
-    snprintf(p->name, sizeof p->name, "%s_%s", family_name(fam), op_name(p->op));
+    p->layout = layout;
+    static const char *const layout_sfx[4] = {"", "_acol", "_brow", "_acol_brow"};
+    snprintf(p->name, sizeof p->name, "%s_%s%s", family_name(fam), op_name(p->op),
+             layout_sfx[layout]);
     *out = p;
     return ok();
 }
@@ -642,7 +659,7 @@ gemm_status_t gemm_run(const gemm_plan_t *plan, const void *A, const void *B, co
     int fam = plan->family;
     if (fam != KF_GENERIC && (!aligned(A, 16) || !aligned(B, 16)))
         fam = plan->fallback;
-    hipError_t e = launch_dense(fam, plan->op, g, (hipStream_t)stream);
+    hipError_t e = launch_dense(fam, plan->op, plan->layout, g, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "kernel launch");
     return ok();

@@ -44,7 +44,9 @@ enum KernelFamily {
     KF_COUNT
 };
 
-hipError_t launch_dense(int family, int op, const GemmArgs &g, hipStream_t s);
+// layout: 0 A row-major and B column-major (K contiguous); bit 0 A
+// column-major, bit 1 B row-major (generic, tiled256w8 and tiled128 only)
+hipError_t launch_dense(int family, int op, int layout, const GemmArgs &g, hipStream_t s);
 // MX block-scaled: afmt / bfmt are the element-format selectors of OpMX
 // (0 E4M3, 1 E5M2, 2 E2M3, 3 E3M2, 4 E2M1); g.sa / g.sb hold the scales.
 hipError_t launch_mx(int family, int afmt, int bfmt, const GemmArgs &g, hipStream_t s);
@@ -70,6 +72,7 @@ struct gemm_plan {
     int op;          // stg::OpKind
     int family;      // stg::KernelFamily
     int fallback;    // family used when run-time alignment rules out `family`
+    int layout;      // dense operand layout (see launch_dense)
     int device;      // HIP device the plan was made on
     char name[96];
 };

@@ -78,7 +78,18 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     constexpr int WM = BM / GM, WN = BN / GN; // wave sub-tile
     constexpr int FM = WM / 32, FN = WN / 32;
     constexpr int NSTAGE = 3;
-    constexpr int STAGE = (BM + BN) * BKB;
+    // MN-major operands (16-bit; A column-major, B row-major): the tile stays
+    // in LDS as 32 K rows of MN values, pitch MN bytes + 64, K row r stored at
+    // row slot mn_slot(r) (bits 2 and 3 swapped), so that the 8 K rows one
+    // transposing fragment read touches fall on 8 different 64-byte bank
+    // groups and every offset inside a step is an immediate
+    constexpr bool AMN = a_mn_v<OP>(), BMN = b_mn_v<OP>();
+    static_assert(!(AMN || BMN) || (OP::BITS == 16 && !OP::MX && !OP::W4), "MN-major: 16-bit");
+    constexpr int KR = BKB / 2; // K rows of an MN-major tile
+    constexpr int APITCH = BM * 2 + 64, BPITCH = BN * 2 + 64;
+    constexpr int A_TILE = AMN ? KR * APITCH : BM * BKB;
+    constexpr int B_TILE = BMN ? KR * BPITCH : BN * BKB;
+    constexpr int STAGE = A_TILE + B_TILE;
     constexpr int NV = OP::LANE_BYTES / 16; // 16-byte LDS reads per operand
     constexpr int FW = OP::LANE_BYTES / 4;  // 32-bit words per operand fragment
     constexpr int KS = BKB / OP::KB;        // MFMA K steps per tile
@@ -105,15 +116,21 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     // 16-bit B tile on its way into LDS
     constexpr bool W4 = OP::W4;
     static_assert(!W4 || (BN == 256 && NT == 256), "one B row per thread");
-    const int64_t lda_b = g.a_rs * OP::BITS / 8;
-    const int64_t ldb_b = W4 ? g.b_cs / 2 : g.b_cs * OP::BITS / 8;
+    // (row pitch in bytes: of the M or N rows, or of the K rows when MN-major)
+    const int64_t lda_b = (AMN ? g.a_cs : g.a_rs) * OP::BITS / 8;
+    const int64_t ldb_b = W4 ? g.b_cs / 2 : (BMN ? g.b_rs : g.b_cs) * OP::BITS / 8;
     const int64_t kbytes = g.K * OP::BITS / 8, kbytes_b = W4 ? g.K / 2 : kbytes;
     const int KT = (int)(kbytes / BKB);
     // bounded by the last byte of the last row: loads past it return zero
-    const __amdgpu_buffer_rsrc_t ra = tile_rsrc((const uint8_t *)g.A + m_blk * lda_b,
-                                                (g.e.M - m_blk - 1) * lda_b + kbytes);
-    const __amdgpu_buffer_rsrc_t rb = tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b,
-                                                (g.e.N - n_blk - 1) * ldb_b + kbytes_b);
+    // (MN-major: the tile's columns start at the base, and the whole offset
+    // goes through the checked vector offset)
+    const __amdgpu_buffer_rsrc_t ra =
+        AMN ? tile_rsrc((const uint8_t *)g.A + m_blk * 2, ((g.K - 1) * g.a_cs + g.e.M - m_blk) * 2)
+            : tile_rsrc((const uint8_t *)g.A + m_blk * lda_b, (g.e.M - m_blk - 1) * lda_b + kbytes);
+    const __amdgpu_buffer_rsrc_t rb =
+        BMN ? tile_rsrc((const uint8_t *)g.B + n_blk * 2, ((g.K - 1) * g.b_rs + g.e.N - n_blk) * 2)
+            : tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b,
+                        (g.e.N - n_blk - 1) * ldb_b + kbytes_b);
     // W4A16 group scales and zero points of the tile's columns (zero points
     // absent: a zero-length resource, whose loads return 0, and z = 8)
     const int64_t wgr = W4 ? g.K / g.wgs : 0; // groups per column
@@ -125,8 +142,16 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
 
     // global -> LDS copy: thread owns chunk `ch` of rows r0 + i*RPP
     const int ch = tid % CH, r0 = tid / CH;
-    const int va0 = r0 * (int)lda_b + ch * 16, vb0 = r0 * (int)ldb_b + ch * 16;
-    const int va_step = RPP * (int)lda_b, vb_step = RPP * (int)ldb_b;
+    // (MN-major: chunk tid % CHX of K rows tid / CHX + i * RPX; the K offset
+    // of tile kt is kt * KR rows)
+    constexpr int CHA = BM * 2 / 16, CHB = BN * 2 / 16, RPA = NT / CHA, RPB = NT / CHB;
+    static_assert(!AMN || KR / RPA == A_LD, "MN-major A: same load count");
+    static_assert(!BMN || KR / RPB == B_LD, "MN-major B: same load count");
+    auto mn_slot = [](int r) STG_AI { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); };
+    const int va0 = AMN ? (tid / CHA) * (int)lda_b + (tid % CHA) * 16 : r0 * (int)lda_b + ch * 16;
+    const int vb0 = BMN ? (tid / CHB) * (int)ldb_b + (tid % CHB) * 16 : r0 * (int)ldb_b + ch * 16;
+    const int va_step = (AMN ? RPA : RPP) * (int)lda_b, vb_step = (BMN ? RPB : RPP) * (int)ldb_b;
+    const int va_tile = AMN ? KR * (int)lda_b : 0, vb_tile = BMN ? KR * (int)ldb_b : 0;
     // 8-bit MX operands: chunks 1 and 2 of every 64-byte K tile trade places in
     // LDS, so that a lane half's two consecutive chunks hold K 16h .. and
     // 32+16h .. (the instruction's K blocks are the two 16-byte halves of
@@ -134,6 +159,11 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     constexpr bool perm = OP::MX && OP::SPLIT;
     const int lch = perm ? (((ch & 1) << 1) | (ch >> 1)) : ch;
     const int l0 = r0 * BKB + ((lch ^ swz64(r0)) << 4); // + i*RPP*BKB (swz64 is RPP-periodic)
+    const int la0 = AMN ? mn_slot(tid / CHA) * APITCH + (tid % CHA) * 16 : l0;
+    const int lb0 = A_TILE + (BMN ? mn_slot(tid / CHB) * BPITCH + (tid % CHB) * 16 : l0);
+    // LDS offset of load pass i (mn_slot(r + i RPX) = mn_slot(r) + mn_slot(i RPX))
+    auto a_pass = [&](int i) STG_AI { return AMN ? mn_slot(i * RPA) * APITCH : i * RPP * BKB; };
+    auto b_pass = [&](int i) STG_AI { return BMN ? mn_slot(i * RPB) * BPITCH : i * RPP * BKB; };
 
     // register staging of global tiles, two sets (prefetch distance 2 tiles)
     u4_t ga[2][A_LD], gb[2][B_LD];
@@ -143,7 +173,8 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         const int soff = kt * BKB;
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
-            ga[S][i] = buf_load16(ra, va0 + i * va_step, soff);
+            ga[S][i] = AMN ? buf_load16(ra, va0 + i * va_step + kt * va_tile, 0)
+                           : buf_load16(ra, va0 + i * va_step, soff);
         if constexpr (W4) {
             // thread t: the 16 code bytes (32 K) of column n_blk + t, and its
             // group's scale and zero point
@@ -154,21 +185,21 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         } else {
 #pragma unroll
             for (int i = 0; i < B_LD; ++i)
-                gb[S][i] = buf_load16(rb, vb0 + i * vb_step, soff);
+                gb[S][i] = BMN ? buf_load16(rb, vb0 + i * vb_step + kt * vb_tile, 0)
+                               : buf_load16(rb, vb0 + i * vb_step, soff);
         }
     };
     auto lstore = [&](auto set, uint8_t *__restrict__ stage_base) STG_AI {
         constexpr int S = decltype(set)::value;
-        uint8_t *base = stage_base + l0;
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
-            *(u4_t *)(base + i * RPP * BKB) = ga[S][i];
+            *(u4_t *)(stage_base + la0 + a_pass(i)) = ga[S][i];
         if constexpr (W4) {
             // 32 codes -> 32 16-bit values: row t of the B tile, four chunks
             constexpr bool BF = std::is_same<OP, OpW4<OpBF16>>::value;
             const float sc = w4_scale<BF>(wsb[S]);
             const int z = has_wz ? (int)wzb[S] : 8;
-            uint8_t *brow = stage_base + BM * BKB + tid * BKB;
+            uint8_t *brow = stage_base + A_TILE + tid * BKB;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 u4_t v;
@@ -179,7 +210,7 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         } else {
 #pragma unroll
             for (int i = 0; i < B_LD; ++i)
-                *(u4_t *)(base + BM * BKB + i * RPP * BKB) = gb[S][i];
+                *(u4_t *)(stage_base + lb0 + b_pass(i)) = gb[S][i];
         }
     };
 
@@ -188,7 +219,15 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     const int arow = wm * WM + (lane & 31), brow = wn * WN + (lane & 31);
     const int half = lane >> 5;
     const int sa = swz64(arow), sb = swz64(brow); // same for every fragment row
-    const int a_off = arow * BKB, b_off = BM * BKB + brow * BKB;
+    const int a_off = arow * BKB, b_off = A_TILE + brow * BKB;
+    // MN-major fragments: two transposing reads per fragment and step, K
+    // values 4 t .. 4 t + 3 of the lane half (t = 0, 1).  Lane 16 q + j reads
+    // K row 16 s + 8 (q / 2) + 4 t + j / 4 (slot 16 s + 8 t + 4 (q / 2) + j / 4)
+    // at MN columns 16 (q % 2) + 4 (j % 4) .. + 3 of fragment i (+ 32 i)
+    const int tr_slot = 4 * (lane >> 5) + ((lane >> 2) & 3);
+    const int tr_col = 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    const int a_tr = tr_slot * APITCH + 2 * wm * WM + tr_col;
+    const int b_tr = A_TILE + tr_slot * BPITCH + 2 * wn * WN + tr_col;
 
     uint32_t fa[2][FM][FW], fb[2][FN][FW];
     auto lread = [&](auto set, const uint8_t *__restrict__ stage_base, int s) STG_AI {
@@ -196,15 +235,33 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         const uint8_t *lsa = stage_base + a_off;
         const uint8_t *lsb = stage_base + b_off;
         const int c0 = (s * OP::KB + half * OP::LANE_BYTES) >> 4;
+        if constexpr (AMN) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    lds_read_tr16(stage_base + a_tr + (16 * s + 8 * t) * APITCH + 64 * i,
+                                  &fa[S][i][2 * t]);
+        }
+        if constexpr (BMN) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    lds_read_tr16(stage_base + b_tr + (16 * s + 8 * t) * BPITCH + 64 * j,
+                                  &fb[S][j][2 * t]);
+        }
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const int oa = ((c0 + v) ^ sa) << 4, ob = ((c0 + v) ^ sb) << 4;
+            if constexpr (!AMN)
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                *(u4_t *)&fa[S][i][4 * v] = *(const u4_t *)(lsa + i * 32 * BKB + oa);
+                for (int i = 0; i < FM; ++i)
+                    *(u4_t *)&fa[S][i][4 * v] = *(const u4_t *)(lsa + i * 32 * BKB + oa);
+            if constexpr (!BMN)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                *(u4_t *)&fb[S][j][4 * v] = *(const u4_t *)(lsb + j * 32 * BKB + ob);
+                for (int j = 0; j < FN; ++j)
+                    *(u4_t *)&fb[S][j][4 * v] = *(const u4_t *)(lsb + j * 32 * BKB + ob);
         }
     };
 
@@ -318,7 +375,7 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     // LDS read rate) backs up and stalls MFMA issue.
     // (W4A16: three loads and four LDS writes for B)
     constexpr int NL = A_LD + (W4 ? 3 : B_LD), NLW = A_LD + (W4 ? 4 : B_LD);
-    constexpr int NM = FM * FN, NR = (FM + FN) * NV;
+    constexpr int NM = FM * FN, NR = FM * (AMN ? 2 : NV) + FN * (BMN ? 2 : NV);
     constexpr int NMT = KS * NM;
     auto schedule = [&]() STG_AI {
         [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
@@ -1082,6 +1139,29 @@ static dense_launch_fn tiled_table_t(int op)
     }
 }
 
+// MN-major operands (layout bit 0: A column-major, bit 1: B row-major) on
+// the LDS-tiled kernel, 16-bit types
+template <class OP, int BM, int BN, int GM, int GN>
+static dense_launch_fn mn_pick(int layout)
+{
+    switch (layout) {
+    case 1: return launch_tiled_t<OpMN<OP, true, false>, BM, BN, GM, GN>;
+    case 2: return launch_tiled_t<OpMN<OP, false, true>, BM, BN, GM, GN>;
+    case 3: return launch_tiled_t<OpMN<OP, true, true>, BM, BN, GM, GN>;
+    default: return nullptr;
+    }
+}
+
+template <int BM, int BN, int GM = 2, int GN = 2>
+static dense_launch_fn tiled_mn_table_t(int op, int layout)
+{
+    switch (op) {
+    case OPK_F16: return mn_pick<OpF16, BM, BN, GM, GN>(layout);
+    case OPK_BF16: return mn_pick<OpBF16, BM, BN, GM, GN>(layout);
+    default: return nullptr;
+    }
+}
+
 template <class OP>
 static hipError_t launch_w8l_t(const GemmArgs &g, hipStream_t s)
 {
@@ -1226,9 +1306,20 @@ hipError_t launch_mx_tiled(int afmt, int bfmt, const GemmArgs &g, hipStream_t s)
     }
 }
 
-hipError_t launch_dense(int family, int op, const GemmArgs &g, hipStream_t s)
+hipError_t launch_dense(int family, int op, int layout, const GemmArgs &g, hipStream_t s)
 {
     dense_launch_fn fn = nullptr;
+    if (layout != 0) {
+        switch (family) {
+        case KF_GENERIC: fn = generic_table(op); break;
+        case KF_TILED_256W8: fn = tiled_mn_table_t<256, 256, 2, 4>(op, layout); break;
+        case KF_TILED_128: fn = tiled_mn_table_t<128, 128>(op, layout); break;
+        default: break;
+        }
+        if (!fn)
+            return hipErrorInvalidValue;
+        return fn(g, s);
+    }
     switch (family) {
     case KF_GENERIC: fn = generic_table(op); break;
     case KF_TILED_256: fn = tiled_table_t<256, 256>(op); break;

@@ -160,3 +160,39 @@ def test_tuning_only_families_refuse_fp8_outputs(monkeypatch, fam):
     assert bf.name.startswith(fam)
     f8 = G.gemm_plan(G.make_desc(512, 512, 512, "bf16", "bf16", "e4m3", has_c=False))
     assert not f8.name.startswith(fam), f8.name
+
+
+@pytest.mark.parametrize("fam,shape", [("tiled256w8", (256, 256, 128)), ("skinny", (16, 256, 256)),
+                                       ("generic", (40, 72, 64))],
+                         ids=["tiled256w8", "skinny", "generic"])
+@pytest.mark.parametrize("d_type", FP8)
+@pytest.mark.parametrize("relu", [False, True])
+def test_fp8_output_specials(orc, monkeypatch, fam, shape, d_type, relu):
+    """NaN, infinities and values around the largest finite value reach the FP8
+    cast through C: NaN -> 0x7F (relu maps it to +0), +-inf and finite values
+    beyond the maximum -> +-max, the rest rounded to nearest even - bit for bit
+    against the oracle's fp32 epilogue of the same kernel's fp32 output."""
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", fam)
+    M, N, K = shape
+    p = _dense("bf16", M, N, K)
+    mx = 448.0 if d_type == "e4m3" else 57344.0
+    specials = np.array([np.nan, np.inf, -np.inf, 1e30, -1e30, mx, -mx, mx * 1.03, mx * 1.07,
+                         -mx * 1.07, mx * 0.97, 2.0 ** -12, -(2.0 ** -18), 0.0], np.float32)
+    rng = np.random.default_rng(13)
+    C = p["C"].astype(np.float32).copy()
+    flat = C.reshape(-1)
+    pos = rng.choice(flat.size, size=4 * specials.size, replace=False)
+    flat[pos] = np.tile(specials, 4)
+
+    def run(dt, al, bi, rl):
+        D, name = gpu_gemm(p["A"], p["B"], C, bi, M, N, K, "bf16", "bf16", dt, alpha=al, relu=rl)
+        assert name.startswith(fam), name
+        return D
+    T = run("f32", 1.0, None, False)
+    D = run(d_type, 1.0, None, relu)
+    ref = orc.epilogue_f32(T, 1.0, None, relu, d_type)
+    bad = int((D != ref).sum())
+    nan_pos = pos[np.isnan(np.tile(specials, 4))]
+    want_nan = 0 if relu else 0x7F
+    assert np.all(D.reshape(-1)[nan_pos] == want_nan), D.reshape(-1)[nan_pos]
+    assert bad == 0, bad
