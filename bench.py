@@ -41,6 +41,7 @@ def _workloads():
         "f16_128": (lambda: inputs.dense_f16(128, 128, 128), "f16"),
         "bf16_8192": (lambda: inputs.dense_bf16(8192, 8192, 8192), "bf16"),
         "bf16_skinny_16x8192x8192": (lambda: inputs.dense_bf16(16, 8192, 8192), "bf16"),
+        "bf16_8192_acol_brow": (lambda: _mn_major(inputs.dense_bf16(8192, 8192, 8192)), "bf16"),
         "s8_8192": (lambda: inputs.dense_s8(8192, 8192, 8192), "s8"),
         "fp8_8192": (lambda: inputs.dense_fp8(8192, 8192, 8192), "fp8"),
         "sparse24_f16_8192": (lambda: inputs.sparse24_f16(8192, 8192, 8192), "sparse_f16"),
@@ -55,6 +56,15 @@ def _workloads():
         "w4a16_bf16_16x8192x8192": (lambda: inputs.w4a16_problem(16, 8192, 8192, "bf16", 128, 13),
                                     "w4a16_bf16"),
     }
+
+
+def _mn_major(p):
+    """The same problem with A stored column-major ([K,M]) and B row-major
+    ([K,N])."""
+    p["A"] = np.ascontiguousarray(p["A"].T)
+    p["B"] = np.ascontiguousarray(p["B"].T)
+    p["a_col"], p["b_col"] = True, False
+    return p
 
 
 def _dev(a):
@@ -100,7 +110,9 @@ def run_workload(name, steps, warmup, rotate_b=1):
     desc = G.make_desc(M, N, K, p["a_type"], p["b_type"], p["d_type"], has_c=p["C"] is not None,
                        has_bias=p["bias"] is not None, alpha=p["alpha"],
                        act="relu" if p["relu"] else "none", sparse_a=sparse,
-                       block_scale=32 if mx else (p["gs"] if w4 else 0))
+                       block_scale=32 if mx else (p["gs"] if w4 else 0),
+                       a_layout="col" if p.get("a_col") else "row",
+                       b_layout="row" if p.get("b_col") is False else "col")
     plan = G.gemm_plan(desc)
     Bs = [_dev(p["B"]) for _ in range(rotate_b)]
     tC = _dev(p["C"]) if p["C"] is not None else None
