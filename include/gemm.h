@@ -89,11 +89,11 @@ typedef enum { GEMM_ACT_NONE = 0, GEMM_ACT_RELU = 1 } gemm_act_t;
 typedef enum {
     GEMM_ALGO_AUTO = 0,
     GEMM_ALGO_TILED = 1,   /* LDS-staged, double-buffered MFMA kernel: K-contiguous
-                              operands (A row-major, B column-major) of any dense type,
-                              or, for F16 / BF16, A column-major and / or B row-major
-                              with M (resp. N) a multiple of 8, fetched from LDS with
-                              transposing reads; K * element size a multiple of 64 and
-                              16-byte rows in every case */
+                              operands (A row-major, B column-major), or A column-major
+                              and / or B row-major with M (resp. N) in whole 16-byte
+                              chunks, fetched from LDS with transposing reads; any dense
+                              type; K * element size a multiple of 64 and 16-byte rows
+                              in every case */
     GEMM_ALGO_GENERIC = 2, /* any layout / shape / alignment, MFMA, no LDS */
     GEMM_ALGO_SKINNY = 3,  /* small M, bandwidth-oriented */
     GEMM_ALGO_TILED_128 = 4, /* GEMM_ALGO_TILED with 128 x 128 workgroup tiles */

@@ -177,7 +177,7 @@ struct OpW4 : Base {
 // Operands stored MN-major ("CUDA 014 - MMA 指令的用法详解", section "加载时转置":
 // a load that transposes as it reads fits an operand whose memory order is
 // the transpose of the MMA's register order): A column-major (M contiguous)
-// and / or B row-major (N contiguous), 16-bit types, in the LDS-tiled
+// and / or B row-major (N contiguous), 16- and 8-bit types, in the LDS-tiled
 // kernel.  The tile keeps its memory order in LDS (K rows of MN values) and
 // the fragments are fetched with the transposing LDS read.
 template <class Base, bool AM, bool BM>
@@ -507,13 +507,27 @@ __device__ STG_AI inline u4_t buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int
 // a group addresses row i / 4, columns 4 (i % 4) .. 4 (i % 4) + 3 of a 4 x 16
 // block stored by rows, lane j receives column j, rows 0..3: four
 // consecutive K values of one M (or N) index, the MFMA operand order.
-__device__ STG_AI inline void lds_read_tr16(const uint8_t *p, uint32_t *w)
+// The 8-bit form (ds_read_b64_tr_b8), measured the same way: lane j
+// receives byte j % 8 of lane 2 e + j / 8 in result byte e (e = 0..7), so
+// lane i addressing row i / 2, columns 8 (i % 2) .. + 7 of an 8 x 16 block
+// gives lane j column j, rows 0..7.  lds_read_tr<EB> picks the form for
+// elements of EB bytes.
+template <int EB>
+__device__ STG_AI inline void lds_read_tr(const uint8_t *p, uint32_t *w)
 {
-    typedef short s4_t __attribute__((ext_vector_type(4)));
     typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
-    const s4_t r =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t *)p);
-    const u2_t v = __builtin_bit_cast(u2_t, r);
+    u2_t v;
+    if constexpr (EB == 2) {
+        typedef short s4_t __attribute__((ext_vector_type(4)));
+        const s4_t r =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t *)p);
+        v = __builtin_bit_cast(u2_t, r);
+    } else {
+        typedef int i2_t __attribute__((ext_vector_type(2)));
+        const i2_t r =
+            __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i2_t *)p);
+        v = __builtin_bit_cast(u2_t, r);
+    }
     w[0] = v.x;
     w[1] = v.y;
 }

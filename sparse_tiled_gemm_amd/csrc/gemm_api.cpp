@@ -160,18 +160,16 @@ gemm_status_t check_device(int *dev_out, DeviceInfo *info_out)
 bool tiled_ok(const gemm_desc_t &d)
 {
     // 64-byte K tiles, 16-byte rows; 32-bit buffer offsets cover 256 rows
-    // plus the K extent.  An MN-major operand (A column-major, B row-major;
-    // 16-bit types only) is read in 16-byte chunks along M (N), which must
-    // not straddle the end of the data (M, N multiples of 8), and its whole
-    // offset, K rows included, goes through 32 bits.
+    // plus the K extent.  An MN-major operand (A column-major, B row-major)
+    // is read in 16-byte chunks along M (N), which must not straddle the end
+    // of the data (M, N in whole 16-byte chunks), and its whole offset, K
+    // rows included, goes through 32 bits.
     const int eb = elem_bytes(d.a_type);
     const int64_t lim = (int64_t)1 << 30;
     const bool a_mn = d.a_layout == GEMM_COL_MAJOR, b_mn = d.b_layout == GEMM_ROW_MAJOR;
-    if ((a_mn || b_mn) && eb != 2)
-        return false;
-    const bool a_ok = a_mn ? d.M % 8 == 0 && (d.K + 128) * d.lda * eb < lim
+    const bool a_ok = a_mn ? (d.M * eb) % 16 == 0 && (d.K + 256) * d.lda * eb < lim
                            : d.lda * eb * 256 < lim;
-    const bool b_ok = b_mn ? d.N % 8 == 0 && (d.K + 128) * d.ldb * eb < lim
+    const bool b_ok = b_mn ? (d.N * eb) % 16 == 0 && (d.K + 256) * d.ldb * eb < lim
                            : d.ldb * eb * 256 < lim;
     return d.K > 0 && (d.K * eb) % 64 == 0 && (d.lda * eb) % 16 == 0 && (d.ldb * eb) % 16 == 0 &&
            a_ok && b_ok;
@@ -532,12 +530,12 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
         // the direct-copy, ping-pong and 128-byte-K variants are built
         // without the FP8 output kinds
         // without the FP8 output kinds; MN-major operands only on the
-        // 8-wave 256 x 256 and the 128 x 128 tiles
+        // type's 256 x 256 arrangement and the 128 x 128 tile
         const bool tuning_only_ok = !is_fp8(d.d_type);
         for (int f = 0; f < KF_COUNT; ++f) {
             const bool tuning_only = f == KF_TILED_DMA4 || f == KF_TILED_DMA5 ||
                                      f == KF_PINGPONG4 || f == KF_PINGPONG5 || f == KF_TILED_256W8L;
-            const bool layout_ok = layout == 0 || f == KF_TILED_256W8 || f == KF_TILED_128;
+            const bool layout_ok = layout == 0 || f == fam256 || f == KF_TILED_128;
             if (strcmp(force, family_name(f)) == 0 &&
                 (f == KF_GENERIC ||
                  (tiled && is_tiled(f) && (f != KF_TILED_256W8L || long_k) &&

@@ -45,8 +45,12 @@ enum KernelFamily {
 };
 
 // layout: 0 A row-major and B column-major (K contiguous); bit 0 A
-// column-major, bit 1 B row-major (generic, tiled256w8 and tiled128 only)
+// column-major, bit 1 B row-major (generic, or see launch_dense_mn)
 hipError_t launch_dense(int family, int op, int layout, const GemmArgs &g, hipStream_t s);
+// MN-major layouts (layout 1..3) on the tiled families that take them: the
+// 128 x 128 tile, and the 256 x 256 arrangement of each input type
+// (tiled256w8 16-bit, tiled256 fp8, tiled256w8t int8)
+hipError_t launch_dense_mn(int family, int op, int layout, const GemmArgs &g, hipStream_t s);
 // MX block-scaled: afmt / bfmt are the element-format selectors of OpMX
 // (0 E4M3, 1 E5M2, 2 E2M3, 3 E3M2, 4 E2M1); g.sa / g.sb hold the scales.
 hipError_t launch_mx(int family, int afmt, int bfmt, const GemmArgs &g, hipStream_t s);
