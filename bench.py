@@ -42,6 +42,8 @@ def _workloads():
         "bf16_8192": (lambda: inputs.dense_bf16(8192, 8192, 8192), "bf16"),
         "bf16_skinny_16x8192x8192": (lambda: inputs.dense_bf16(16, 8192, 8192), "bf16"),
         "bf16_8192_acol_brow": (lambda: _mn_major(inputs.dense_bf16(8192, 8192, 8192)), "bf16"),
+        "fp8_8192_acol_brow": (lambda: _mn_major(inputs.dense_fp8(8192, 8192, 8192)), "fp8"),
+        "s8_8192_acol_brow": (lambda: _mn_major(inputs.dense_s8(8192, 8192, 8192)), "s8"),
         "s8_8192": (lambda: inputs.dense_s8(8192, 8192, 8192), "s8"),
         "fp8_8192": (lambda: inputs.dense_fp8(8192, 8192, 8192), "fp8"),
         "sparse24_f16_8192": (lambda: inputs.sparse24_f16(8192, 8192, 8192), "sparse_f16"),
