@@ -227,7 +227,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the first calls after the operands are allocated run 5-20 % slower
+    # than the steady state (about 25 calls); the default warm-up covers them
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(_workloads().keys()))
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
