@@ -237,6 +237,8 @@ static int check_desc(const oracle_gemm_t *g)
 {
     if (g->M < 0 || g->N < 0 || g->K < 0)
         return -1;
+    if (g->saturate && g->d_type != OR_S32) /* saturation applies to int32 outputs */
+        return -1;
     if (g->a_type == OR_S8 || g->b_type == OR_S8) {
         if (g->a_type != OR_S8 || g->b_type != OR_S8)
             return -1;
@@ -267,8 +269,10 @@ static int64_t b_index(const oracle_gemm_t *g, int64_t k, int64_t n)
 
 /* Epilogue of one element: t = acc + C, then scale, bias, activation, cast,
  * in that order ("NVIDIA MMA", section "Input / accumulate / output").  The
- * integer path reduces t modulo 2^32 ("wrap unless saturating", section
- * "Ampere: FP16/BF16 and integer MMA baseline"). */
+ * integer path reduces the exact t modulo 2^32, or, when saturating, clamps
+ * it to [-2^31, 2^31 - 1] (section "Ampere: FP16/BF16 and integer MMA
+ * baseline": integer instructions wrap on overflow unless .satfinite asks
+ * for saturation to the INT32 bounds). */
 static void finish(const oracle_gemm_t *g, int64_t m, int64_t n, double acc, double sabs,
                    const void *C, const float *bias, void *D, int64_t d_idx, double *y_out,
                    double *s_out)
@@ -280,6 +284,8 @@ static void finish(const oracle_gemm_t *g, int64_t m, int64_t n, double acc, dou
         *s_out = sabs + fabs(c);
     if (is_int_type(g->d_type)) {
         int64_t t = (int64_t)acc + (int64_t)c;
+        if (g->saturate)
+            t = t > INT32_MAX ? INT32_MAX : (t < INT32_MIN ? INT32_MIN : t);
         int32_t w = (int32_t)(uint32_t)(uint64_t)t;
         oracle_encode(OR_S32, (double)w, D, d_idx);
         if (y_out)

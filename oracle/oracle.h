@@ -79,6 +79,7 @@ typedef struct {
     int has_c;
     int has_bias;  /* bias is fp32, one value per output column n */
     int relu;
+    int saturate;  /* int32 output: clamp acc + C to the int32 range (else wrap) */
 } oracle_gemm_t;
 
 /* Decode element idx of an array of the given type to fp64 (s8/s32 exact). */

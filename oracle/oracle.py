@@ -34,6 +34,7 @@ class _Desc(ctypes.Structure):
         ("ldc", ctypes.c_int64), ("ldd", ctypes.c_int64),
         ("alpha", ctypes.c_float),
         ("has_c", ctypes.c_int), ("has_bias", ctypes.c_int), ("relu", ctypes.c_int),
+        ("saturate", ctypes.c_int),
     ]
 
 
@@ -105,10 +106,10 @@ def encode(type_name, values):
 
 
 def _desc(M, N, K, a_type, b_type, c_type, d_type, a_col_major, b_col_major,
-          lda, ldb, ldc, ldd, alpha, has_c, has_bias, relu):
+          lda, ldb, ldc, ldd, alpha, has_c, has_bias, relu, saturate=False):
     return _Desc(M, N, K, TYPES[a_type], TYPES[b_type], TYPES[c_type], TYPES[d_type],
                  int(a_col_major), int(b_col_major), lda, ldb, ldc, ldd,
-                 float(alpha), int(has_c), int(has_bias), int(relu))
+                 float(alpha), int(has_c), int(has_bias), int(relu), int(saturate))
 
 
 def _lds(M, N, K, a_col_major, b_col_major):
@@ -118,19 +119,20 @@ def _lds(M, N, K, a_col_major, b_col_major):
 
 
 def gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, *, a_col_major=False,
-         b_col_major=True, alpha=1.0, relu=False, want_y=True, want_s=True):
+         b_col_major=True, alpha=1.0, relu=False, want_y=True, want_s=True, saturate=False):
     """Full oracle GEMM on packed operands.
 
     A is [M,K] row-major (or [K,M] when a_col_major), B is stored [N,K] when
     b_col_major (else [K,N]), C and D are [M,N] row-major.  Returns
     (D_bits, Y, S): the encoded output, the fp64 pre-cast result and the
-    error scale sum_k |a b| + |c|.
+    error scale sum_k |a b| + |c|.  saturate: an int32 output clamps the exact
+    acc + C to the int32 range instead of wrapping.
     """
     integer = a_type == "s8" and d_type == "s32"
     c_type = "s32" if integer else "f32"
     lda, ldb, ldc, ldd = _lds(M, N, K, a_col_major, b_col_major)
     g = _desc(M, N, K, a_type, b_type, c_type, d_type, a_col_major, b_col_major,
-              lda, ldb, ldc, ldd, alpha, C is not None, bias is not None, relu)
+              lda, ldb, ldc, ldd, alpha, C is not None, bias is not None, relu, saturate)
     A = np.ascontiguousarray(A, dtype=STORAGE[a_type])
     B = np.ascontiguousarray(B, dtype=STORAGE[b_type])
     if C is not None:
@@ -148,13 +150,13 @@ def gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, *, a_col_major=False,
 
 
 def gemm_entries(A, B, C, bias, M, N, K, a_type, b_type, d_type, rows, cols, *,
-                 a_col_major=False, b_col_major=True, alpha=1.0, relu=False):
+                 a_col_major=False, b_col_major=True, alpha=1.0, relu=False, saturate=False):
     """The oracle definition at chosen (rows[i], cols[i]) only: (D_bits, Y, S)."""
     integer = a_type == "s8" and d_type == "s32"
     c_type = "s32" if integer else "f32"
     lda, ldb, ldc, ldd = _lds(M, N, K, a_col_major, b_col_major)
     g = _desc(M, N, K, a_type, b_type, c_type, d_type, a_col_major, b_col_major,
-              lda, ldb, ldc, ldd, alpha, C is not None, bias is not None, relu)
+              lda, ldb, ldc, ldd, alpha, C is not None, bias is not None, relu, saturate)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     cols = np.ascontiguousarray(cols, dtype=np.int64)
     n = rows.size

@@ -144,3 +144,24 @@ def test_s8_float_output_is_the_wrapped_int32_sum(orc):
     assert np.all(Y == wrapped + 0.5)
     D2, Y2, _ = orc.gemm(A[:, :8], B[:, :8], None, None, M, N, 8, "s8", "s8", "bf16", alpha=0.25)
     assert np.all(Y2 == 127 * 127 * 8 * 0.25)
+
+
+def test_s32_saturation_clamps_the_exact_sum(orc):
+    """The saturating int32 output ("NVIDIA MMA", section "Ampere: FP16/BF16
+    and integer MMA baseline": integer MMA saturates to the INT32 bounds with
+    .satfinite, else wraps): D = clamp(sum_k a b + c, -2^31, 2^31 - 1), the
+    expected values worked out by hand.  Row 0: 4 * (127 * 127) = 64516 on top
+    of c = 2^31 - 10000 -> clamps to 2^31 - 1 (wrapping gives
+    -2^31 + 54516).  Row 1: 4 * (-128 * 127) = -65024 below c = -2^31 + 5 ->
+    clamps to -2^31 (wraps to 2^31 - 65019).  Row 2: in range, identical to
+    wrapping."""
+    A = np.array([[127] * 4, [-128] * 4, [3, -2, 1, 0]], dtype=np.int8)
+    B = np.array([[127, 127, 127, 127]], dtype=np.int8)  # N x K (column-major)
+    C = np.array([[2**31 - 10000], [-(2**31) + 5], [7]], dtype=np.int32)
+    D, _, _ = orc.gemm(A, B, C, None, 3, 1, 4, "s8", "s8", "s32", saturate=True)
+    assert D[:, 0].tolist() == [2**31 - 1, -(2**31), 3 * 127 - 2 * 127 + 127 + 7]
+    W, _, _ = orc.gemm(A, B, C, None, 3, 1, 4, "s8", "s8", "s32")
+    assert W[:, 0].tolist() == [-(2**31) + 54516, 2**31 - 65019, 3 * 127 - 2 * 127 + 127 + 7]
+    with pytest.raises(ValueError):  # saturation is an int32-output option
+        orc.gemm(A.astype(np.int8), B, C.astype(np.float32), None, 3, 1, 4, "s8", "s8", "f32",
+                 saturate=True)
