@@ -109,8 +109,12 @@ typedef enum {
  *   a = b = S8: either c_type S32, d_type S32, alpha == 1, no bias, no
  *   activation; or (dequantising epilogue) c_type F32, d_type F32 / F16 /
  *   BF16 / F8_E4M3 / F8_E5M2, any epilogue, where the int32 sum is first
- *   rounded to fp32 (to nearest even).  The int32 sum wraps modulo 2^32 (no
- *   saturation) in both.
+ *   rounded to fp32 (to nearest even).  The int32 sum wraps modulo 2^32 in
+ *   both.  With saturate = 1 (int32 output only, K < 131072, where the sum of
+ *   products cannot leave the int32 range) D = clamp(acc + C) to
+ *   [-2^31, 2^31 - 1] instead ("NVIDIA MMA", section "Ampere: FP16/BF16 and
+ *   integer MMA baseline": integer MMA saturates with .satfinite, else
+ *   wraps).
  *   sparse_a = 1: any of the pairs above, A row-major and packed,
  *   K % 4 == 0; used with gemm_sparse24_run (A is then given in compressed
  *   form).
@@ -143,6 +147,8 @@ typedef struct {
     int32_t algo;                           /* gemm_algo_t, normally AUTO */
     int32_t block_scale;                    /* 0; 32: MX block-scaled (gemm_mx_run);
                                                W4A16: the weight group size */
+    int32_t saturate;                       /* int32 output: 1 clamps acc + C to the
+                                               int32 range, 0 wraps modulo 2^32 */
 } gemm_desc_t;
 
 typedef struct gemm_plan gemm_plan_t;

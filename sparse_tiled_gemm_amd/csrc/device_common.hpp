@@ -379,10 +379,12 @@ template <int KIND>
 __device__ STG_AI inline void epilogue_store(const EpiArgs &e, int64_t row, int64_t col, int acc)
 {
     if constexpr (KIND == OUT_S32) {
-        uint32_t t = (uint32_t)acc;
-        if (e.C)
-            t += (uint32_t)((const int32_t *)e.C)[row * e.ldc + col];
-        ((int32_t *)e.D)[row * e.ldd + col] = (int32_t)t;
+        int t = acc;
+        if (e.C) {
+            const int c = ((const int32_t *)e.C)[row * e.ldc + col];
+            t = e.sat ? __builtin_elementwise_add_sat(acc, c) : (int)((uint32_t)acc + (uint32_t)c);
+        }
+        ((int32_t *)e.D)[row * e.ldd + col] = t;
     } else {
         epilogue_store<KIND>(e, row, col, (float)acc);
     }
@@ -659,9 +661,12 @@ __device__ STG_AI inline void epi_store4(__amdgpu_buffer_rsrc_t rd, int voff, in
 }
 
 // acc + C, four elements: fp32 addition, or int32 addition modulo 2^32
+// (saturating to the int32 range when `sat`)
 __device__ STG_AI inline f4_t add_c(f4_t v, f4_t c) { return v + c; }
-__device__ STG_AI inline i4_t add_c(i4_t v, i4_t c)
+__device__ STG_AI inline i4_t add_c(i4_t v, i4_t c, int sat)
 {
+    if (sat)
+        return __builtin_elementwise_add_sat(v, c);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
         v[q] = (int)((uint32_t)v[q] + (uint32_t)c[q]);
@@ -760,7 +765,7 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
                 const v4_t v = __builtin_bit_cast(v4_t, *(const u4_t *)(lds_wave + rr * PITCH + c4));
                 const int soff = (32 * i + p * RPP) * ldd_b;
                 if constexpr (IOUT) {
-                    const v4_t w = has_c ? add_c(v, __builtin_bit_cast(v4_t, cv[p])) : v;
+                    const v4_t w = has_c ? add_c(v, __builtin_bit_cast(v4_t, cv[p]), e.sat) : v;
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, w), rd, vd, soff,
                                                            EPI_CPOL);
                 } else {

@@ -260,6 +260,13 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
         return fail(GEMM_ERR_INVALID_VALUE, "unknown layout code");
     if (d.act != GEMM_ACT_NONE && d.act != GEMM_ACT_RELU)
         return fail(GEMM_ERR_INVALID_VALUE, "unknown activation code");
+    // saturation: int32 outputs, with K small enough that the int32 MFMA sum
+    // itself cannot overflow (|sum| <= K 2^14 < 2^31), so that clamping acc + C
+    // is the exact saturated result
+    if (d.saturate != 0 && d.saturate != 1)
+        return fail(GEMM_ERR_INVALID_VALUE, "saturate must be 0 or 1");
+    if (d.saturate && (d.d_type != GEMM_S32 || d.K >= 131072))
+        return fail(GEMM_ERR_UNSUPPORTED, "saturation applies to int32 outputs with K < 131072");
     if ((d.has_c != 0 && d.has_c != 1) || (d.has_bias != 0 && d.has_bias != 1) ||
         (d.sparse_a != 0 && d.sparse_a != 1))
         return fail(GEMM_ERR_INVALID_VALUE, "has_c / has_bias / sparse_a must be 0 or 1");
@@ -595,6 +602,7 @@ static EpiArgs make_epi(const gemm_desc_t &d, const void *C, const void *bias, v
     e.alpha = d.alpha;
     e.relu = d.act == GEMM_ACT_RELU;
     e.d_kind = out_kind(d.d_type);
+    e.sat = d.saturate;
     e.D = D;
     e.ldd = d.ldd;
     const int db = elem_bytes(d.d_type);

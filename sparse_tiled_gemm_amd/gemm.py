@@ -53,7 +53,7 @@ class gemm_desc_t(ctypes.Structure):
         ("alpha", ctypes.c_float),
         ("has_c", ctypes.c_int32), ("has_bias", ctypes.c_int32), ("act", ctypes.c_int32),
         ("sparse_a", ctypes.c_int32), ("algo", ctypes.c_int32),
-        ("block_scale", ctypes.c_int32),
+        ("block_scale", ctypes.c_int32), ("saturate", ctypes.c_int32),
     ]
 
 
@@ -134,7 +134,7 @@ def _stream(stream):
 
 def make_desc(M, N, K, a_type, b_type, d_type, *, c_type=None, has_c=True, has_bias=False,
               alpha=1.0, act="none", a_layout="row", b_layout="col", lda=0, ldb=0, ldc=0,
-              ldd=0, sparse_a=False, algo="auto", block_scale=0):
+              ldd=0, sparse_a=False, algo="auto", block_scale=0, saturate=False):
     """Build a gemm_desc_t from readable arguments (type names as in DTYPES)."""
     integer = a_type == "s8" and d_type == "s32"
     if c_type is None:
@@ -152,6 +152,7 @@ def make_desc(M, N, K, a_type, b_type, d_type, *, c_type=None, has_c=True, has_b
     d.sparse_a = int(bool(sparse_a))
     d.algo = ALGO[algo] if isinstance(algo, str) else int(algo)
     d.block_scale = int(block_scale)
+    d.saturate = int(bool(saturate))
     return d
 
 

@@ -34,12 +34,12 @@ def empty_out(M, N, d_type, ldd=0):
 
 def gpu_gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, *, alpha=1.0, relu=False,
              a_col=False, b_col=True, algo="auto", lda=0, ldb=0, ldc=0, ldd=0,
-             a_dev=None, b_dev=None, c_dev=None, out=None):
+             a_dev=None, b_dev=None, c_dev=None, out=None, saturate=False):
     """Run D = epilogue(A*B + C) on the GPU; returns (D bits [M,N], plan name)."""
     desc = G.make_desc(M, N, K, a_type, b_type, d_type, has_c=C is not None or c_dev is not None,
                        has_bias=bias is not None, alpha=alpha, act="relu" if relu else "none",
                        a_layout="col" if a_col else "row", b_layout="col" if b_col else "row",
-                       lda=lda, ldb=ldb, ldc=ldc, ldd=ldd, algo=algo)
+                       lda=lda, ldb=ldb, ldc=ldc, ldd=ldd, algo=algo, saturate=saturate)
     plan = G.gemm_plan(desc)
     tA = a_dev if a_dev is not None else to_dev(A)
     tB = b_dev if b_dev is not None else to_dev(B)
@@ -65,10 +65,12 @@ def gpu_compress(A_logical, a_type="f16"):
 
 
 def gpu_sparse_gemm(vals, meta, B, C, M, N, K, d_type="f32", *, algo="auto", bias=None,
-                    alpha=1.0, relu=False, b_col=True, a_type="f16", b_type=None):
+                    alpha=1.0, relu=False, b_col=True, a_type="f16", b_type=None,
+                    saturate=False):
     desc = G.make_desc(M, N, K, a_type, b_type or a_type, d_type, has_c=C is not None,
                        has_bias=bias is not None, alpha=alpha, act="relu" if relu else "none",
-                       b_layout="col" if b_col else "row", sparse_a=True, algo=algo)
+                       b_layout="col" if b_col else "row", sparse_a=True, algo=algo,
+                       saturate=saturate)
     plan = G.gemm_plan(desc)
     tB = to_dev(B)
     tC = to_dev(C) if C is not None else None
