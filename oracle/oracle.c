@@ -233,6 +233,11 @@ static int is_float_out(int t)
     return t == OR_F32 || t == OR_F16 || t == OR_BF16 || t == OR_E4M3 || t == OR_E5M2;
 }
 
+/* C of a float output: fp32, or fp16 / bf16 (decoded exactly; the pages
+ * keep the C type a separate choice, "NVIDIA MMA", section "Input /
+ * accumulate / output") */
+static int float_c_ok(int t) { return t == OR_F32 || t == OR_F16 || t == OR_BF16; }
+
 static int check_desc(const oracle_gemm_t *g)
 {
     if (g->M < 0 || g->N < 0 || g->K < 0)
@@ -248,11 +253,11 @@ static int check_desc(const oracle_gemm_t *g)
             return 0;
         }
         /* int8 -> float: the wrapped int32 sum, then the float epilogue */
-        return (g->c_type == OR_F32 && is_float_out(g->d_type)) ? 0 : -1;
+        return (float_c_ok(g->c_type) && is_float_out(g->d_type)) ? 0 : -1;
     }
     if (!is_float_in(g->a_type) || !is_float_in(g->b_type))
         return -1;
-    if (g->c_type != OR_F32)
+    if (!float_c_ok(g->c_type))
         return -1;
     return is_float_out(g->d_type) ? 0 : -1;
 }
@@ -421,7 +426,7 @@ static int check_mx_desc(const oracle_gemm_t *g)
         return -1;
     if (!is_mx_elem(g->a_type) || !is_mx_elem(g->b_type) || g->a_col_major || !g->b_col_major)
         return -1;
-    if (g->c_type != OR_F32)
+    if (!float_c_ok(g->c_type))
         return -1;
     return is_float_out(g->d_type) ? 0 : -1;
 }

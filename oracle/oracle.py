@@ -119,7 +119,8 @@ def _lds(M, N, K, a_col_major, b_col_major):
 
 
 def gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, *, a_col_major=False,
-         b_col_major=True, alpha=1.0, relu=False, want_y=True, want_s=True, saturate=False):
+         b_col_major=True, alpha=1.0, relu=False, want_y=True, want_s=True, saturate=False,
+         c_type=None):
     """Full oracle GEMM on packed operands.
 
     A is [M,K] row-major (or [K,M] when a_col_major), B is stored [N,K] when
@@ -129,7 +130,7 @@ def gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, *, a_col_major=False,
     acc + C to the int32 range instead of wrapping.
     """
     integer = a_type == "s8" and d_type == "s32"
-    c_type = "s32" if integer else "f32"
+    c_type = c_type or ("s32" if integer else "f32")
     lda, ldb, ldc, ldd = _lds(M, N, K, a_col_major, b_col_major)
     g = _desc(M, N, K, a_type, b_type, c_type, d_type, a_col_major, b_col_major,
               lda, ldb, ldc, ldd, alpha, C is not None, bias is not None, relu, saturate)
@@ -150,10 +151,11 @@ def gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, *, a_col_major=False,
 
 
 def gemm_entries(A, B, C, bias, M, N, K, a_type, b_type, d_type, rows, cols, *,
-                 a_col_major=False, b_col_major=True, alpha=1.0, relu=False, saturate=False):
+                 a_col_major=False, b_col_major=True, alpha=1.0, relu=False, saturate=False,
+                 c_type=None):
     """The oracle definition at chosen (rows[i], cols[i]) only: (D_bits, Y, S)."""
     integer = a_type == "s8" and d_type == "s32"
-    c_type = "s32" if integer else "f32"
+    c_type = c_type or ("s32" if integer else "f32")
     lda, ldb, ldc, ldd = _lds(M, N, K, a_col_major, b_col_major)
     g = _desc(M, N, K, a_type, b_type, c_type, d_type, a_col_major, b_col_major,
               lda, ldb, ldc, ldd, alpha, C is not None, bias is not None, relu, saturate)
