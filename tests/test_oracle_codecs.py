@@ -6,6 +6,8 @@ import numpy as np
 import pytest
 import torch
 
+from sparse_tiled_gemm_amd import inputs
+
 
 def _torch_decode(bits, dtype):
     t = torch.from_numpy(np.ascontiguousarray(bits))
@@ -165,3 +167,20 @@ def test_s32_saturation_clamps_the_exact_sum(orc):
     with pytest.raises(ValueError):  # saturation is an int32-output option
         orc.gemm(A.astype(np.int8), B, C.astype(np.float32), None, 3, 1, 4, "s8", "s8", "f32",
                  saturate=True)
+
+
+@pytest.mark.parametrize("ct", ["f16", "bf16"])
+def test_16bit_c_is_its_exact_widening(orc, ct):
+    """A 16-bit C enters as its exact value: the result equals the fp32-C
+    result on the widened values (every f16 / bf16 value is an fp32 value)."""
+    rng = np.random.default_rng(8)
+    M, N, K = 5, 7, 16
+    A = inputs.to_bf16(rng.standard_normal((M, K)))
+    B = inputs.to_bf16(rng.standard_normal((N, K)))
+    conv = inputs.to_f16 if ct == "f16" else inputs.to_bf16
+    C16 = conv(rng.uniform(-3, 3, (M, N)) * 2.0 ** rng.integers(-20, 10, (M, N)))
+    C32 = orc.decode(ct, C16).astype(np.float32).reshape(M, N)
+    D16, Y16, _ = orc.gemm(A, B, C16, None, M, N, K, "bf16", "bf16", "f32", c_type=ct)
+    D32, Y32, _ = orc.gemm(A, B, C32, None, M, N, K, "bf16", "bf16", "f32")
+    assert np.array_equal(D16.view(np.uint32), D32.view(np.uint32))
+    assert np.array_equal(Y16, Y32)
