@@ -104,10 +104,11 @@ typedef enum {
  *
  * Support matrix (everything else is GEMM_ERR_UNSUPPORTED):
  *   a, b in {F16}, {BF16}, or {F8_E4M3, F8_E5M2} (the two fp8 formats may
- *   differ): c_type F32, d_type F32 / F16 / BF16 / F8_E4M3 / F8_E5M2, any
- *   epilogue.
+ *   differ): c_type F32, F16 or BF16 (a 16-bit C is widened exactly to fp32;
+ *   it takes the element-wise epilogue), d_type F32 / F16 / BF16 / F8_E4M3 /
+ *   F8_E5M2, any epilogue.
  *   a = b = S8: either c_type S32, d_type S32, alpha == 1, no bias, no
- *   activation; or (dequantising epilogue) c_type F32, d_type F32 / F16 /
+ *   activation; or (dequantising epilogue) c_type F32 / F16 / BF16, d_type F32 / F16 /
  *   BF16 / F8_E4M3 / F8_E5M2, any epilogue, where the int32 sum is first
  *   rounded to fp32 (to nearest even).  The int32 sum wraps modulo 2^32 in
  *   both.  With saturate = 1 (int32 output only, K < 131072, where the sum of
@@ -125,8 +126,8 @@ typedef enum {
  *   formats exist only here.
  *   b = U4 (W4A16): a F16 or BF16, A row-major, B column-major (codes along
  *   K, ldb even), block_scale = the weight group size (a multiple of 32
- *   dividing K); c_type F32, any float d_type, any epilogue; used with
- *   gemm_w4a16_run.
+ *   dividing K); c_type F32 / F16 / BF16, any float d_type, any epilogue;
+ *   used with gemm_w4a16_run.
  * Epilogue, in fp32 for float outputs:  t = acc (+ C[m,n] if has_c);
  *   y = has_bias ? fmaf(alpha, t, bias[n]) : alpha * t;
  *   z = (act == RELU) ? (y > 0 ? y : +0) : y;  D = round-to-nearest-even(z).

@@ -349,6 +349,18 @@ __device__ STG_AI inline uint32_t f32_to_fp8_bits(float x)
 }
 
 // Epilogue of one accumulator value at (row, col), both in range, for output
+// C element idx of a float-output epilogue, widened exactly to fp32 (fp32,
+// fp16 or bf16 storage).
+__device__ STG_AI inline float load_c(const EpiArgs &e, int64_t idx)
+{
+    if (e.c_kind == 0)
+        return ((const float *)e.C)[idx];
+    const uint16_t h = ((const uint16_t *)e.C)[idx];
+    if (e.c_kind == 1)
+        return (float)__builtin_bit_cast(_Float16, h);
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
 // kind KIND: t = acc (+C); y = has_bias ? fmaf(alpha, t, bias[col]) : alpha*t;
 // relu; round-to-nearest-even cast and store.  Integer: D = acc + C mod 2^32.
 template <int KIND>
@@ -356,7 +368,7 @@ __device__ STG_AI inline void epilogue_store(const EpiArgs &e, int64_t row, int6
 {
     float t = acc;
     if (e.C)
-        t += ((const float *)e.C)[row * e.ldc + col];
+        t += load_c(e, row * e.ldc + col);
     float y = e.bias ? __builtin_fmaf(e.alpha, t, e.bias[col]) : e.alpha * t;
     asm("" : "+v"(y)); // keep y an fp32 value: no fused multiply-add-convert
     if (e.relu)
@@ -440,7 +452,7 @@ __device__ STG_AI inline void epilogue_store_any(const EpiArgs &e, int64_t row, 
 {
     float t = acc;
     if (e.C)
-        t += ((const float *)e.C)[row * e.ldc + col];
+        t += load_c(e, row * e.ldc + col);
     float y = e.bias ? __builtin_fmaf(e.alpha, t, e.bias[col]) : e.alpha * t;
     asm("" : "+v"(y)); // keep y an fp32 value: no fused multiply-add-convert
     if (e.relu)

@@ -59,6 +59,12 @@ const char *mx_name(int sel)
 }
 bool is_float_in(int t) { return t == GEMM_F16 || t == GEMM_BF16 || is_fp8(t); }
 bool is_float_out(int t) { return t == GEMM_F32 || t == GEMM_F16 || t == GEMM_BF16 || is_fp8(t); }
+// C of a float output: fp32, or fp16 / bf16 widened exactly in the epilogue
+bool float_c_ok(const gemm_desc_t &d)
+{
+    return d.c_type == GEMM_F32 || d.c_type == GEMM_F16 || d.c_type == GEMM_BF16 ||
+           (d.c_type == 0 && !d.has_c);
+}
 int elem_bytes(int t)
 {
     switch (t) {
@@ -291,8 +297,8 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
             return fail(GEMM_ERR_UNSUPPORTED, "W4A16: A row-major, B column-major (codes along K)");
         if (d.ldb % 2)
             return fail(GEMM_ERR_UNSUPPORTED, "W4A16: packed weight rows must be whole bytes");
-        if (!(d.c_type == GEMM_F32 || (d.c_type == 0 && !d.has_c)))
-            return fail(GEMM_ERR_UNSUPPORTED, "float inputs take an f32 C");
+        if (!float_c_ok(d))
+            return fail(GEMM_ERR_UNSUPPORTED, "float inputs take an f32, f16 or bf16 C");
         if (!is_float_out(d.d_type))
             return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16, bf16 or fp8");
         return ok();
@@ -316,7 +322,7 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
         if ((d.lda * mx_bits(d.a_type)) % 8 || (d.ldb * mx_bits(d.b_type)) % 8)
             return fail(GEMM_ERR_UNSUPPORTED, "packed rows must be whole bytes");
         if (!(d.c_type == GEMM_F32 || (d.c_type == 0 && !d.has_c)))
-            return fail(GEMM_ERR_UNSUPPORTED, "float inputs take an f32 C");
+            return fail(GEMM_ERR_UNSUPPORTED, "block-scaled GEMM takes an f32 C");
         if (!is_float_out(d.d_type))
             return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16, bf16 or fp8");
         return ok();
@@ -338,8 +344,8 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
             // the int8 -> float epilogue: the int32 sum through the float epilogue
             if (!is_float_out(d.d_type))
                 return fail(GEMM_ERR_UNSUPPORTED, "s8 inputs produce s32 or a float output");
-            if (!(d.c_type == GEMM_F32 || (d.c_type == 0 && !d.has_c)))
-                return fail(GEMM_ERR_UNSUPPORTED, "a float output takes an f32 C");
+            if (!float_c_ok(d))
+                return fail(GEMM_ERR_UNSUPPORTED, "a float output takes an f32, f16 or bf16 C");
         }
     } else {
         if (!is_float_in(d.a_type) || !is_float_in(d.b_type))
@@ -347,8 +353,8 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
         if (op_kind(d.a_type, d.b_type) < 0)
             return fail(GEMM_ERR_UNSUPPORTED, "A/B type pair not supported (f16/f16, "
                                               "bf16/bf16 or fp8/fp8)");
-        if (!(d.c_type == GEMM_F32 || (d.c_type == 0 && !d.has_c)))
-            return fail(GEMM_ERR_UNSUPPORTED, "float inputs take an f32 C");
+        if (!float_c_ok(d))
+            return fail(GEMM_ERR_UNSUPPORTED, "float inputs take an f32, f16 or bf16 C");
         if (!is_float_out(d.d_type))
             return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16, bf16 or fp8");
     }
@@ -585,7 +591,8 @@ static gemm_status_t check_epilogue_ptrs(const gemm_desc_t &d, const void *C, co
         return fail(GEMM_ERR_NULL_POINTER, "C is NULL but the plan reads C");
     if (d.has_bias && !bias)
         return fail(GEMM_ERR_NULL_POINTER, "bias is NULL but the plan adds a bias");
-    if ((d.has_c && !aligned(C, 4)) || (d.has_bias && !aligned(bias, 4)) ||
+    const size_t c_align = (d.c_type == GEMM_F16 || d.c_type == GEMM_BF16) ? 2 : 4;
+    if ((d.has_c && !aligned(C, c_align)) || (d.has_bias && !aligned(bias, 4)) ||
         !aligned(D, elem_bytes(d.d_type)))
         return fail(GEMM_ERR_MISALIGNED, "C, bias or D not aligned to its element size");
     return GEMM_OK;
@@ -609,7 +616,9 @@ static EpiArgs make_epi(const gemm_desc_t &d, const void *C, const void *bias, v
     // the vector epilogue addresses a block's C and D rows with 32-bit
     // offsets: 257 rows of each must span less than 2^31 bytes
     const int64_t lim = 0x7fffffff / 257;
-    e.vec = (!d.has_c || (aligned(C, 16) && d.ldc % 4 == 0 && d.ldc * 4 < lim)) &&
+    // a 16-bit C (float outputs) is read element by element
+    e.c_kind = !d.has_c ? 0 : (d.c_type == GEMM_F16 ? 1 : (d.c_type == GEMM_BF16 ? 2 : 0));
+    e.vec = (!d.has_c || (e.c_kind == 0 && aligned(C, 16) && d.ldc % 4 == 0 && d.ldc * 4 < lim)) &&
             (!d.has_bias || aligned(bias, 16)) && aligned(D, 4 * db) && d.ldd % 4 == 0 &&
             d.ldd * db < lim;
     return e;

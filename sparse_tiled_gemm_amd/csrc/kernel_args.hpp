@@ -21,6 +21,7 @@ struct EpiArgs {
     int vec; // 1: C, bias and D rows allow 16-byte (C, f32/s32 D) / 8-byte accesses
              //    at multiples of 4 columns
     int sat; // int32 output: acc + C saturates to the int32 range (else wraps)
+    int c_kind; // float outputs: C elements are 0 fp32, 1 fp16, 2 bf16
 };
 
 // Dense operands.  Element (m,k) of A is at A[m*a_rs + k*a_cs] and element

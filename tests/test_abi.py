@@ -63,7 +63,9 @@ def _ok(**kw):
     (dict(a_type="e4m3", b_type="e5m2", d_type="e4m3", has_c=False), G.GEMM_OK),
     (dict(d_type="s32"), G.GEMM_ERR_UNSUPPORTED),
     (dict(d_type="e2m1"), G.GEMM_ERR_UNSUPPORTED),
-    (dict(c_type="bf16"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(c_type="s32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(c_type="bf16"), G.GEMM_OK),
+    (dict(c_type="f16"), G.GEMM_OK),
     (dict(sparse_a=True), G.GEMM_OK),                  # 2:4 bf16
     (dict(sparse_a=True, a_type="s8", b_type="s8", d_type="s32"), G.GEMM_OK),
     (dict(sparse_a=True, a_type="e4m3", b_type="e5m2", d_type="f16"), G.GEMM_OK),

@@ -196,3 +196,81 @@ def test_fp8_output_specials(orc, monkeypatch, fam, shape, d_type, relu):
     want_nan = 0 if relu else 0x7F
     assert np.all(D.reshape(-1)[nan_pos] == want_nan), D.reshape(-1)[nan_pos]
     assert bad == 0, bad
+
+
+# 16-bit C ("NVIDIA MMA", section "Input / accumulate / output": the C type is
+# a separate choice): C given as fp16 or bf16, widened exactly to fp32 and
+# then the same epilogue
+C16_FAMILIES = [("tiled256w8", "bf16", (300, 264, 256)), ("tiled128", "f16", (130, 200, 128)),
+                ("generic", "bf16", (67, 45, 96)), ("skinny", "f16", (16, 300, 1024)),
+                ("tiled256", "e4m3", (264, 300, 256)), ("tiled256w8t", "s8", (264, 300, 256))]
+
+
+@pytest.mark.parametrize("fam,a_type,shape", C16_FAMILIES, ids=[f[0] + "_" + f[1] for f in C16_FAMILIES])
+@pytest.mark.parametrize("c_type", ["f16", "bf16"])
+def test_16bit_c(orc, monkeypatch, fam, a_type, shape, c_type):
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", fam)
+    M, N, K = shape
+    p = _dense(a_type, M, N, K)
+    rng = np.random.default_rng(21)
+    conv = inputs.to_f16 if c_type == "f16" else inputs.to_bf16
+    C = conv(rng.uniform(-4, 4, size=(M, N)))
+    d_type = "bf16" if a_type != "f16" else "f32"
+    alpha = (1.0 / 512 if a_type == "s8" else (p["alpha"] if a_type == "e4m3" else 1.0))
+    bias = _bias(N)
+    desc = G.make_desc(M, N, K, p["a_type"], p["b_type"], d_type, c_type=c_type, has_c=True,
+                       has_bias=True, alpha=alpha, act="relu")
+    plan = G.gemm_plan(desc)
+    assert plan.name.startswith(fam), plan.name
+    D = torch.empty(M * N * G.ELEM_BYTES[d_type], dtype=torch.uint8, device="cuda")
+    G.gemm_run(plan, to_dev(p["A"]), to_dev(p["B"]), to_dev(C), to_dev(bias), D)
+    torch.cuda.synchronize()
+    out = D.cpu().numpy().view({"bf16": np.uint16, "f32": np.float32}[d_type]).reshape(M, N)
+    Dr, Y, S = orc.gemm(p["A"], p["B"], C, bias, M, N, K, p["a_type"], p["b_type"], d_type,
+                        alpha=alpha, relu=True, c_type=c_type)
+    r = check(out, d_type, Dr, Y, S, p["a_type"], alpha)
+    say("c16", plan.name, c_type, r)
+    assert r.ok, r
+
+
+@pytest.mark.parametrize("c_type", ["f16", "bf16"])
+def test_16bit_c_sparse_and_w4(orc, c_type):
+    """2:4 (direct-copy kernel) and W4A16 (tiled and skinny) with a 16-bit C."""
+    conv = inputs.to_f16 if c_type == "f16" else inputs.to_bf16
+    M, N, K = 300, 264, 512
+    p = inputs.sparse24("f16", M, N, K)
+    C = conv(np.random.default_rng(4).uniform(-2, 2, size=(M, N)))
+    vals, meta, _, _ = gpu_compress(p["A_logical"], "f16")
+    desc = G.make_desc(M, N, K, "f16", "f16", "f32", c_type=c_type, has_c=True, sparse_a=True)
+    plan = G.gemm_plan(desc)
+    D = torch.empty(M * N * 4, dtype=torch.uint8, device="cuda")
+    G.gemm_sparse24_run(plan, vals, meta, to_dev(p["B"]), to_dev(C), None, D)
+    torch.cuda.synchronize()
+    Dr, Y, S = orc.gemm(p["A_logical"], p["B"], C, None, M, N, K, "f16", "f16", "f32",
+                        c_type=c_type)
+    r = check(D.cpu().numpy().view(np.float32).reshape(M, N), "f32", Dr, Y, S, "f16", 1.0)
+    say("c16 sparse", plan.name, r)
+    assert r.ok, r
+    for Mw in (256, 16):
+        q = inputs.w4a16_problem(Mw, N, K, "bf16", 128, workload=72)
+        Cw = conv(np.random.default_rng(6).uniform(-1, 1, size=(Mw, N)))
+        desc = G.make_desc(Mw, N, K, "bf16", "u4", "bf16", c_type=c_type, has_c=True,
+                           block_scale=128)
+        plan = G.gemm_plan(desc)
+        D = torch.empty(Mw * N * 2, dtype=torch.uint8, device="cuda")
+        G.gemm_w4a16_run(plan, to_dev(q["A"]), to_dev(q["B"]), to_dev(q["scales"]),
+                         to_dev(q["zeros"]), to_dev(Cw), None, D)
+        torch.cuda.synchronize()
+        W = orc.w4a16_dequant(q["B"], q["scales"], q["zeros"], N, K, 128, "bf16")
+        Dr, Y, S = orc.gemm(q["A"], W, Cw, None, Mw, N, K, "bf16", "bf16", "bf16", c_type=c_type)
+        r = check(D.cpu().numpy().view(np.uint16).reshape(Mw, N), "bf16", Dr, Y, S, "bf16", 1.0)
+        say("c16 w4", plan.name, r)
+        assert r.ok, r
+
+
+def test_16bit_c_validation():
+    with pytest.raises(G.GemmError):  # int32 outputs take an int32 C
+        G.gemm_plan(G.make_desc(256, 256, 256, "s8", "s8", "s32", c_type="f16"))
+    with pytest.raises(G.GemmError):  # block-scaled GEMM keeps an fp32 C
+        G.gemm_plan(G.make_desc(256, 256, 512, "e4m3", "e4m3", "bf16", c_type="bf16",
+                                block_scale=32))
