@@ -107,6 +107,7 @@ double oracle_decode(int type, const void *base, int64_t idx)
     case OR_E4M3: return dec_e4m3(((const uint8_t *)base)[idx]);
     case OR_E5M2: return dec_e5m2(((const uint8_t *)base)[idx]);
     case OR_S8: return (double)((const int8_t *)base)[idx];
+    case OR_U8: return (double)((const uint8_t *)base)[idx];
     case OR_F32: return (double)((const float *)base)[idx];
     case OR_S32: return (double)((const int32_t *)base)[idx];
     default: return NAN;
@@ -221,7 +222,8 @@ int oracle_encode_array(int type, const double *x, int64_t n, void *base)
 
 /* ------------------------------------------------------------------ GEMM */
 
-static int is_int_type(int t) { return t == OR_S8 || t == OR_S32; }
+static int is_int_in(int t) { return t == OR_S8 || t == OR_U8; }
+static int is_int_type(int t) { return is_int_in(t) || t == OR_S32; }
 static int is_float_in(int t) { return t == OR_F16 || t == OR_BF16 || t == OR_E4M3 || t == OR_E5M2; }
 
 /* Input/accumulator/output pairing of "NVIDIA MMA", section "Input /
@@ -244,8 +246,9 @@ static int check_desc(const oracle_gemm_t *g)
         return -1;
     if (g->saturate && g->d_type != OR_S32) /* saturation applies to int32 outputs */
         return -1;
-    if (g->a_type == OR_S8 || g->b_type == OR_S8) {
-        if (g->a_type != OR_S8 || g->b_type != OR_S8)
+    if (is_int_in(g->a_type) || is_int_in(g->b_type)) {
+        /* s8 and u8 pair freely (the INT8 rows of the Ampere table) */
+        if (!is_int_in(g->a_type) || !is_int_in(g->b_type))
             return -1;
         if (g->d_type == OR_S32) {
             if (g->c_type != OR_S32 || g->alpha != 1.0f || g->has_bias || g->relu)
@@ -541,14 +544,15 @@ static int sp_bytes(int type)
     case OR_BF16: return 2;
     case OR_E4M3:
     case OR_E5M2:
-    case OR_S8: return 1;
+    case OR_S8:
+    case OR_U8: return 1;
     default: return 0;
     }
 }
 
 /* A zero of the format: +0 or -0 for the float formats (all bits but the
- * sign clear), 0 for s8 (whose 0x80 is -128, not a zero).  Every other code,
- * NaN and infinity included, is a non-zero. */
+ * sign clear), 0 for s8 (whose 0x80 is -128, not a zero) and u8.  Every
+ * other code, NaN and infinity included, is a non-zero. */
 static int sp_is_zero(int type, uint32_t bits)
 {
     switch (type) {

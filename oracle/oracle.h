@@ -66,7 +66,12 @@ enum {
     OR_E2M3 = 7,
     OR_E3M2 = 8,
     OR_E2M1 = 9,
-    OR_E8M0 = 10 /* block scale: 2^(e - 127), 0xFF = NaN; one byte each */
+    OR_E8M0 = 10, /* block scale: 2^(e - 127), 0xFF = NaN; one byte each */
+    /* unsigned 8-bit integer 0..255: the INT8 rows of the instruction tables
+     * ("NVIDIA MMA", section "Ampere: FP16/BF16 and integer MMA baseline")
+     * let A and B each be signed or unsigned; any pairing of OR_S8 and OR_U8
+     * accumulates in int32 like s8 x s8 */
+    OR_U8 = 11
 };
 
 typedef struct {
@@ -118,14 +123,15 @@ int oracle_epilogue_f32(int64_t M, int64_t N, const float *T, float alpha, const
                         int relu, int d_type, void *D);
 
 /* 2:4 compression of a row-major [M,K] matrix of type `type` (OR_F16,
- * OR_BF16, OR_E4M3, OR_E5M2 or OR_S8; elements of 2 or 1 bytes), K % 4 == 0.
+ * OR_BF16, OR_E4M3, OR_E5M2, OR_S8 or OR_U8; elements of 2 or 1 bytes),
+ * K % 4 == 0.
  * Group g of row m is K positions 4g..4g+3.  Its kept positions i0 < i1 give
  *   values[m*(K/2) + 2g]   = A[m, 4g+i0]
  *   values[m*(K/2) + 2g+1] = A[m, 4g+i1]   (elements of the same type)
  *   nibble (i0 | i1 << 2) at bits 4*(g%8) .. 4*(g%8)+3 of meta[m*W + g/8],
  * with W = ceil(K/32) words per row and unused high nibbles 0.
  * The dropped positions are zeros: +0 and -0 of the float formats, 0 of s8
- * (0x80 is -128 there).  A group with fewer than two non-zeros keeps its
+ * (0x80 is -128 there) and of u8.  A group with fewer than two non-zeros keeps its
  * non-zero positions and fills up with the lowest unused positions; NaN and
  * infinity count as non-zero.
  * Returns 0, -1 for a bad type or shape, or the 1-based row index of the

@@ -1,7 +1,7 @@
 """ctypes wrapper over the CPU oracle (liboracle.so).  TEST INFRASTRUCTURE ONLY.
 
 Arrays are numpy arrays holding raw element bits:
-  f16, bf16 -> uint16    e4m3, e5m2 -> uint8    s8 -> int8
+  f16, bf16 -> uint16    e4m3, e5m2 -> uint8    s8 -> int8    u8 -> uint8
   f32 -> float32         s32 -> int32
 The library is built from oracle.c on first use when it is missing.
 """
@@ -13,12 +13,13 @@ import numpy as np
 from . import build as _build
 
 TYPES = {"f16": 0, "bf16": 1, "e4m3": 2, "e5m2": 3, "s8": 4, "f32": 5, "s32": 6,
-         "e2m3": 7, "e3m2": 8, "e2m1": 9, "e8m0": 10}
+         "e2m3": 7, "e3m2": 8, "e2m1": 9, "e8m0": 10, "u8": 11}
+INT_IN = ("s8", "u8")
 # bits per element of the MX element formats (6- and 4-bit ones are stored packed)
 MX_BITS = {"e4m3": 8, "e5m2": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}
 STORAGE = {
     "f16": np.uint16, "bf16": np.uint16, "e4m3": np.uint8, "e5m2": np.uint8,
-    "s8": np.int8, "f32": np.float32, "s32": np.int32,
+    "s8": np.int8, "u8": np.uint8, "f32": np.float32, "s32": np.int32,
 }
 
 _lib = None
@@ -129,7 +130,7 @@ def gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, *, a_col_major=False,
     error scale sum_k |a b| + |c|.  saturate: an int32 output clamps the exact
     acc + C to the int32 range instead of wrapping.
     """
-    integer = a_type == "s8" and d_type == "s32"
+    integer = a_type in INT_IN and d_type == "s32"
     c_type = c_type or ("s32" if integer else "f32")
     lda, ldb, ldc, ldd = _lds(M, N, K, a_col_major, b_col_major)
     g = _desc(M, N, K, a_type, b_type, c_type, d_type, a_col_major, b_col_major,
@@ -154,7 +155,7 @@ def gemm_entries(A, B, C, bias, M, N, K, a_type, b_type, d_type, rows, cols, *,
                  a_col_major=False, b_col_major=True, alpha=1.0, relu=False, saturate=False,
                  c_type=None):
     """The oracle definition at chosen (rows[i], cols[i]) only: (D_bits, Y, S)."""
-    integer = a_type == "s8" and d_type == "s32"
+    integer = a_type in INT_IN and d_type == "s32"
     c_type = c_type or ("s32" if integer else "f32")
     lda, ldb, ldc, ldd = _lds(M, N, K, a_col_major, b_col_major)
     g = _desc(M, N, K, a_type, b_type, c_type, d_type, a_col_major, b_col_major,
@@ -190,7 +191,7 @@ class NotSparse24(ValueError):
     pass
 
 
-SPARSE24_TYPES = ("f16", "bf16", "e4m3", "e5m2", "s8")
+SPARSE24_TYPES = ("f16", "bf16", "e4m3", "e5m2", "s8", "u8")
 
 
 def sparse24_compress(A, type_name="f16"):
