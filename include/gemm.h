@@ -22,7 +22,9 @@
  *    (both contiguous along K); the fast kernels here use that pairing.
  *
  * Conventions
- *  - Sizes and leading dimensions are in elements.  A is M x K, row-major
+ *  - Sizes and leading dimensions are in elements.  M, N and K must be below
+ *    2^31 and every matrix (rows times leading dimension) at most 2^40
+ *    elements (GEMM_ERR_INVALID_VALUE otherwise).  A is M x K, row-major
  *    (A[m*lda + k]) or column-major (A[k*lda + m]).  B is K x N, column-major
  *    (stored N x K, B[n*ldb + k]) or row-major (B[k*ldb + n]).  C and D are
  *    M x N row-major (C[m*ldc + n]).  A leading dimension of 0 means packed.
@@ -162,7 +164,9 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc);
 
 /* Validate, check that the current HIP device is gfx950, select the kernel
  * and return a new plan in *out (host memory, owned by the caller, released
- * with gemm_plan_destroy).  On failure *out is set to NULL. */
+ * with gemm_plan_destroy).  On failure *out is set to NULL.  With GEMM_LOG=1
+ * in the environment each successful call prints its kernel choice to
+ * stderr. */
 gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out);
 
 /* Release a plan (NULL is accepted). */
@@ -176,8 +180,11 @@ gemm_status_t gemm_plan_describe(const gemm_plan_t *plan, char *buf, size_t len)
  * when the plan has has_c == 0; bias may be NULL only when has_bias == 0.
  * Returns after the launch is enqueued.  Pointers need only element
  * alignment: the fast kernels need 16-byte aligned A and B and fall back to
- * the generic kernel otherwise.  D must not overlap A, B or bias; D == C
- * (in-place accumulate) is allowed. */
+ * the generic kernel otherwise.  D must not share bytes with A, B, C or
+ * bias, with one exception: D == C (in-place accumulate) when C and D have
+ * the same element size and ldc == ldd.  Any other overlap is rejected with
+ * GEMM_ERR_UNSUPPORTED before anything is launched (the same rule holds for
+ * every run function below, with its own operands). */
 gemm_status_t gemm_run(const gemm_plan_t *plan, const void *A, const void *B, const void *C,
                        const void *bias, void *D, gemm_stream_t stream);
 

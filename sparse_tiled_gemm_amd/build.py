@@ -1,8 +1,10 @@
 """Compile the HIP library libstgemm.so in-tree for gfx950.
 
 Each source is compiled on its own (in parallel) with hipcc, then linked.
-Run `python -m sparse_tiled_gemm_amd.build [-v] [--asm]`; --asm also keeps
-the gfx950 assembly under _build/ for inspection.
+Run `python -m sparse_tiled_gemm_amd.build [-v] [--asm] [--incremental]`;
+--asm also keeps the gfx950 assembly under _build/ for inspection;
+--incremental recompiles only the sources whose object file is older than the
+source or a header (build() called without it compiles everything).
 """
 import concurrent.futures
 import os
@@ -48,10 +50,27 @@ def _compile(src, asm, verbose):
     return obj
 
 
-def build(verbose=False, asm=False):
+def _stale(src):
+    """True when src's object is missing or older than src or any header."""
+    obj = os.path.join(BUILD, src + ".o")
+    if not os.path.exists(obj):
+        return True
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                                        if f.endswith((".hpp", ".h"))]
+    deps += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(verbose=False, asm=False, incremental=False):
+    """Compile every source (incremental=True: only those whose object is
+    older than the source or a header) and link libstgemm.so."""
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, asm, verbose), SOURCES))
+    todo = [s for s in SOURCES if not incremental or asm or _stale(s)]
+    if todo:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(todo)) as ex:
+            list(ex.map(lambda s: _compile(s, asm, verbose), todo))
+    objs = [os.path.join(BUILD, s + ".o") for s in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
@@ -62,4 +81,5 @@ def build(verbose=False, asm=False):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, asm="--asm" in sys.argv))
+    print(build(verbose="-v" in sys.argv, asm="--asm" in sys.argv,
+                incremental="--incremental" in sys.argv))

@@ -402,23 +402,16 @@ __device__ STG_AI inline void epilogue_store(const EpiArgs &e, int64_t row, int6
     }
 }
 
-// Calls f(std::integral_constant<int, KIND>) for the output kind d_kind:
-// OUT_S32 only for integer accumulators; the FP8 kinds only when EXT
-// (kernels built without them are never planned for FP8 outputs).
-template <bool INT, bool EXT, class F>
+// Calls f(std::integral_constant<int, KIND>) for the output kind d_kind
+// (OUT_S32 only for integer accumulators).
+template <bool INT, class F>
 __device__ STG_AI inline void with_out_kind(int d_kind, F &&f)
 {
     switch (d_kind) {
     case OUT_F32: f(std::integral_constant<int, OUT_F32>{}); break;
     case OUT_F16: f(std::integral_constant<int, OUT_F16>{}); break;
-    case OUT_E4M3:
-        if constexpr (EXT)
-            f(std::integral_constant<int, OUT_E4M3>{});
-        break;
-    case OUT_E5M2:
-        if constexpr (EXT)
-            f(std::integral_constant<int, OUT_E5M2>{});
-        break;
+    case OUT_E4M3: f(std::integral_constant<int, OUT_E4M3>{}); break;
+    case OUT_E5M2: f(std::integral_constant<int, OUT_E5M2>{}); break;
     case OUT_S32:
         if constexpr (INT)
             f(std::integral_constant<int, OUT_S32>{});
@@ -807,13 +800,11 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
 }
 
 
-// EXT: also the FP8 output kinds (the tuning-only kernel variants are built
-// without them).
-template <class OP, int FM, int FN, bool EXT = true>
+template <class OP, int FM, int FN>
 __device__ STG_AI inline void epilogue_grid_lds(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
                                          int64_t m0, int64_t n0, int lane, uint32_t *lds_wave)
 {
-    with_out_kind<OP::INT, EXT>(e.d_kind, [&](auto kind) STG_AI {
+    with_out_kind<OP::INT>(e.d_kind, [&](auto kind) STG_AI {
         epilogue_slabs<OP, FM, FN, decltype(kind)::value>(e, acc, m0, n0, lane, lds_wave);
     });
 }

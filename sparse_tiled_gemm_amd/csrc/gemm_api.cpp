@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <new>
 
@@ -111,6 +112,12 @@ int out_kind(int d)
     }
 }
 
+// a * b for a, b >= 0, saturating at INT64_MAX (size checks never overflow)
+int64_t smul(int64_t a, int64_t b)
+{
+    return (a != 0 && b > INT64_MAX / a) ? INT64_MAX : a * b;
+}
+
 // Fill packed leading dimensions; returns false if a given one is too small.
 bool normalise(gemm_desc_t &d)
 {
@@ -148,7 +155,7 @@ gemm_status_t check_device(int *dev_out, DeviceInfo *info_out)
         e = hipGetDeviceProperties(&p, dev);
         if (e != hipSuccess)
             return hip_fail(e, "hipGetDeviceProperties");
-        snprintf(di.arch, sizeof di.arch, "%s", p.gcnArchName);
+        snprintf(di.arch, sizeof di.arch, "%.63s", p.gcnArchName);
         di.is_gfx950 = strncmp(p.gcnArchName, "gfx950", 6) == 0;
         di.num_cu = p.multiProcessorCount;
         di.checked = 1;
@@ -173,9 +180,9 @@ bool tiled_ok(const gemm_desc_t &d)
     const int eb = elem_bytes(d.a_type);
     const int64_t lim = (int64_t)1 << 30;
     const bool a_mn = d.a_layout == GEMM_COL_MAJOR, b_mn = d.b_layout == GEMM_ROW_MAJOR;
-    const bool a_ok = a_mn ? (d.M * eb) % 16 == 0 && (d.K + 256) * d.lda * eb < lim
+    const bool a_ok = a_mn ? (d.M * eb) % 16 == 0 && smul(smul(d.K + 256, d.lda), eb) < lim
                            : d.lda * eb * 256 < lim;
-    const bool b_ok = b_mn ? (d.N * eb) % 16 == 0 && (d.K + 256) * d.ldb * eb < lim
+    const bool b_ok = b_mn ? (d.N * eb) % 16 == 0 && smul(smul(d.K + 256, d.ldb), eb) < lim
                            : d.ldb * eb * 256 < lim;
     return d.K > 0 && (d.K * eb) % 64 == 0 && (d.lda * eb) % 16 == 0 && (d.ldb * eb) % 16 == 0 &&
            a_ok && b_ok;
@@ -195,13 +202,8 @@ const char *family_name(int f)
     case KF_SPARSE_GENERIC: return "sparse24_generic";
     case KF_SPARSE_TILED: return "sparse24_tiled";
     case KF_SPARSE_DMA8: return "sparse24_dma8";
-    case KF_TILED_256W8L: return "tiled256w8l";
-    case KF_TILED_DMA4: return "tiled256dma4";
-    case KF_TILED_DMA5: return "tiled256dma5";
     case KF_TILED_256W8: return "tiled256w8";
     case KF_TILED_256W8T: return "tiled256w8t";
-    case KF_PINGPONG4: return "pingpong4";
-    case KF_PINGPONG5: return "pingpong5";
     case KF_MX_GENERIC: return "mx_generic";
     case KF_MX_TILED: return "mx_tiled";
     case KF_W4_GENERIC: return "w4_generic";
@@ -223,9 +225,7 @@ bool skinny_ok(const gemm_desc_t &d)
 
 bool is_tiled(int f)
 {
-    return f == KF_TILED_256 || f == KF_TILED_128 || f == KF_TILED_DMA4 || f == KF_TILED_DMA5 ||
-           f == KF_TILED_256W8 || f == KF_TILED_256W8T || f == KF_PINGPONG4 ||
-           f == KF_PINGPONG5 || f == KF_TILED_256W8L;
+    return f == KF_TILED_256 || f == KF_TILED_128 || f == KF_TILED_256W8 || f == KF_TILED_256W8T;
 }
 
 } // namespace
@@ -280,8 +280,21 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
         return fail(GEMM_ERR_INVALID_VALUE, "unknown algo code");
     if (d.lda < 0 || d.ldb < 0 || d.ldc < 0 || d.ldd < 0)
         return fail(GEMM_ERR_INVALID_VALUE, "negative leading dimension");
+    // sizes the kernels' index arithmetic covers: M, N, K below 2^31, and
+    // every matrix (rows x leading dimension) at most 2^40 elements
+    const int64_t max_elems = (int64_t)1 << 40;
+    if (d.M > INT32_MAX || d.N > INT32_MAX || d.K > INT32_MAX)
+        return fail(GEMM_ERR_INVALID_VALUE, "M, N and K must be below 2^31");
+    if (d.lda > max_elems || d.ldb > max_elems || d.ldc > max_elems || d.ldd > max_elems)
+        return fail(GEMM_ERR_INVALID_VALUE, "leading dimension above 2^40");
     if (!normalise(d))
         return fail(GEMM_ERR_INVALID_VALUE, "leading dimension smaller than the matrix extent");
+    {
+        const bool ar = d.a_layout == GEMM_ROW_MAJOR, bc = d.b_layout == GEMM_COL_MAJOR;
+        if (smul(ar ? d.M : d.K, d.lda) > max_elems || smul(bc ? d.N : d.K, d.ldb) > max_elems ||
+            smul(d.M, d.ldc) > max_elems || smul(d.M, d.ldd) > max_elems)
+            return fail(GEMM_ERR_INVALID_VALUE, "a matrix spans more than 2^40 elements");
+    }
     if (d.b_type == GEMM_U4 || d.a_type == GEMM_U4) {
         // W4A16 ("NVIDIA MMA", section "How quantisation configurations map
         // to MMA"): fp16 / bf16 activations, 4-bit weight codes with a scale
@@ -372,7 +385,36 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
     return ok();
 }
 
+static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out);
+
+// GEMM_LOG=1 in the environment: every plan prints its kernel choice (one
+// line on stderr) - the shape, types, layouts and the family selected.
+static void log_plan(const gemm_plan_t *p)
+{
+    static const int on = [] {
+        const char *v = getenv("GEMM_LOG");
+        return v && *v && strcmp(v, "0") != 0;
+    }();
+    if (!on)
+        return;
+    const gemm_desc_t &d = p->d;
+    fprintf(stderr,
+            "[stgemm] plan M=%lld N=%lld K=%lld a=%d b=%d c=%d d=%d a_layout=%s b_layout=%s "
+            "sparse_a=%d block_scale=%d algo=%d -> %s (fallback on misaligned pointers: %s)\n",
+            (long long)d.M, (long long)d.N, (long long)d.K, d.a_type, d.b_type, d.c_type, d.d_type,
+            d.a_layout == GEMM_ROW_MAJOR ? "row" : "col", d.b_layout == GEMM_ROW_MAJOR ? "row" : "col",
+            d.sparse_a, d.block_scale, d.algo, p->name, family_name(p->fallback));
+}
+
 gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
+{
+    const gemm_status_t st = plan_impl(desc, out);
+    if (st == GEMM_OK)
+        log_plan(*out);
+    return st;
+}
+
+static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
 {
     if (!out)
         return fail(GEMM_ERR_NULL_POINTER, "out is NULL");
@@ -511,8 +553,6 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
 
     const bool tiled = tiled_ok(d);
     const int layout = (d.a_layout == GEMM_COL_MAJOR ? 1 : 0) | (d.b_layout == GEMM_ROW_MAJOR ? 2 : 0);
-    // K in whole 128-byte tiles (the 128-byte-K-tile kernel)
-    const bool long_k = tiled && (d.K * elem_bytes(d.a_type)) % 128 == 0;
     const bool skinny = skinny_ok(d);
     int fam = -1;
     const int64_t big_tiles = ceil_div(d.M, 256) * ceil_div(d.N, 256);
@@ -540,19 +580,12 @@ gemm_status_t gemm_plan(const gemm_desc_t *desc, gemm_plan_t **out)
     // Tuning override: STGEMM_FORCE_KERNEL=<family name> replaces the choice
     // for descriptors that family can serve (ignored otherwise).
     if (const char *force = getenv("STGEMM_FORCE_KERNEL")) {
-        // the direct-copy, ping-pong and 128-byte-K variants are built
-        // without the FP8 output kinds
-        // without the FP8 output kinds; MN-major operands only on the
-        // type's 256 x 256 arrangement and the 128 x 128 tile
-        const bool tuning_only_ok = !is_fp8(d.d_type);
+        // MN-major operands only on the type's 256 x 256 arrangement and the
+        // 128 x 128 tile
         for (int f = 0; f < KF_COUNT; ++f) {
-            const bool tuning_only = f == KF_TILED_DMA4 || f == KF_TILED_DMA5 ||
-                                     f == KF_PINGPONG4 || f == KF_PINGPONG5 || f == KF_TILED_256W8L;
             const bool layout_ok = layout == 0 || f == fam256 || f == KF_TILED_128;
             if (strcmp(force, family_name(f)) == 0 &&
-                (f == KF_GENERIC ||
-                 (tiled && is_tiled(f) && (f != KF_TILED_256W8L || long_k) &&
-                  (!tuning_only || tuning_only_ok) && layout_ok) ||
+                (f == KF_GENERIC || (tiled && is_tiled(f) && layout_ok) ||
                  (skinny && f == KF_SKINNY)))
                 fam = f;
         }
@@ -580,6 +613,48 @@ gemm_status_t gemm_plan_describe(const gemm_plan_t *plan, char *buf, size_t len)
         return fail(GEMM_ERR_INVALID_VALUE, "len is 0");
     snprintf(buf, len, "%s", plan->name);
     return ok();
+}
+
+// Byte range [lo, hi) of a matrix of `rows` rows of `cols` elements of
+// `eb` bytes, `ld` elements apart.
+struct Span {
+    uintptr_t lo = 0, hi = 0;
+};
+static Span span(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t eb)
+{
+    Span s;
+    if (!p || rows <= 0 || cols <= 0)
+        return s;
+    s.lo = (uintptr_t)p;
+    s.hi = s.lo + (uintptr_t)(((rows - 1) * ld + cols) * eb);
+    return s;
+}
+static bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// D must not share bytes with any input, except that D may be C itself
+// (in-place accumulate: same address, element size and leading dimension,
+// so every element is read before it is written by the same thread).
+// `inputs` are the operand ranges of the call.
+static gemm_status_t check_d_overlap(const gemm_desc_t &d, const void *C, const void *bias,
+                                     const void *D, std::initializer_list<Span> inputs)
+{
+    const int db = elem_bytes(d.d_type);
+    const Span sd = span(D, d.M, d.N, d.ldd, db);
+    if (d.has_c) {
+        const int cb = (d.c_type == GEMM_F16 || d.c_type == GEMM_BF16) ? 2 : 4;
+        const Span sc = span(C, d.M, d.N, d.ldc, cb);
+        const bool in_place = C == D && cb == db && d.ldc == d.ldd;
+        if (overlap(sc, sd) && !in_place)
+            return fail(GEMM_ERR_UNSUPPORTED,
+                        "D overlaps C: only D == C with the same element size and leading "
+                        "dimension (in-place accumulate) is supported");
+    }
+    if (d.has_bias && overlap(span(bias, 1, d.N, d.N, 4), sd))
+        return fail(GEMM_ERR_UNSUPPORTED, "D overlaps bias");
+    for (const Span &x : inputs)
+        if (overlap(x, sd))
+            return fail(GEMM_ERR_UNSUPPORTED, "D overlaps an input operand");
+    return GEMM_OK;
 }
 
 static gemm_status_t check_epilogue_ptrs(const gemm_desc_t &d, const void *C, const void *bias,
@@ -646,6 +721,14 @@ gemm_status_t gemm_run(const gemm_plan_t *plan, const void *A, const void *B, co
     const int eb = elem_bytes(d.a_type);
     if (d.K > 0 && (!aligned(A, eb) || !aligned(B, eb)))
         return fail(GEMM_ERR_MISALIGNED, "A or B not aligned to its element size");
+    {
+        const bool ar = d.a_layout == GEMM_ROW_MAJOR, bc = d.b_layout == GEMM_COL_MAJOR;
+        st = check_d_overlap(d, C, bias, D,
+                             {span(A, ar ? d.M : d.K, ar ? d.K : d.M, d.lda, eb),
+                              span(B, bc ? d.N : d.K, bc ? d.K : d.N, d.ldb, eb)});
+        if (st != GEMM_OK)
+            return st;
+    }
 
     GemmArgs g;
     g.A = A;
@@ -761,6 +844,15 @@ gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, con
     const int eb = elem_bytes(d.a_type);
     if (d.K > 0 && (!aligned(values, eb) || !aligned(meta, 4) || !aligned(B, eb)))
         return fail(GEMM_ERR_MISALIGNED, "values, meta or B not aligned to its element size");
+    {
+        const bool bc = d.b_layout == GEMM_COL_MAJOR;
+        st = check_d_overlap(d, C, bias, D,
+                             {span(values, d.M, d.K / 2, d.K / 2, eb),
+                              span(meta, d.M, (d.K + 31) / 32, (d.K + 31) / 32, 4),
+                              span(B, bc ? d.N : d.K, bc ? d.K : d.N, d.ldb, eb)});
+        if (st != GEMM_OK)
+            return st;
+    }
     SparseArgs a;
     a.values = values;
     a.meta = meta;
@@ -799,6 +891,17 @@ gemm_status_t gemm_mx_run(const gemm_plan_t *plan, const void *A, const uint8_t 
     gemm_status_t st = check_epilogue_ptrs(d, C, bias, D);
     if (st != GEMM_OK)
         return st;
+    {
+        // packed rows: ld elements of mx_bits bits each
+        const int64_t ra = d.lda * mx_bits(d.a_type) / 8, rb = d.ldb * mx_bits(d.b_type) / 8;
+        const int64_t ka = d.K * mx_bits(d.a_type) / 8, kb = d.K * mx_bits(d.b_type) / 8;
+        st = check_d_overlap(d, C, bias, D,
+                             {span(A, d.M, ka, ra, 1), span(B, d.N, kb, rb, 1),
+                              span(scale_a, d.M, d.K / 32, d.K / 32, 1),
+                              span(scale_b, d.N, d.K / 32, d.K / 32, 1)});
+        if (st != GEMM_OK)
+            return st;
+    }
     GemmArgs g;
     g.A = A;
     g.B = B;
@@ -841,6 +944,15 @@ gemm_status_t gemm_w4a16_run(const gemm_plan_t *plan, const void *A, const void 
         return st;
     if (d.K > 0 && (!aligned(A, 2) || !aligned(scales, 2)))
         return fail(GEMM_ERR_MISALIGNED, "A or scales not aligned to 2 bytes");
+    {
+        const int64_t groups = d.K / d.block_scale;
+        st = check_d_overlap(d, C, bias, D,
+                             {span(A, d.M, d.K, d.lda, 2), span(B, d.N, d.K / 2, d.ldb / 2, 1),
+                              span(scales, d.N, groups, groups, 2),
+                              span(zeros, d.N, groups, groups, 1)});
+        if (st != GEMM_OK)
+            return st;
+    }
     GemmArgs g;
     g.A = A;
     g.B = B;

@@ -25,17 +25,12 @@ enum KernelFamily {
     KF_GENERIC = 0, // any layout / shape / alignment
     KF_TILED_256,   // 256 x 256 workgroup tile, LDS double buffer
     KF_TILED_128,   // 128 x 128 workgroup tile, LDS double buffer
-    KF_SKINNY,      // M <= 64, bandwidth-oriented
+    KF_SKINNY,      // M <= 16, bandwidth-oriented
     KF_SPARSE_GENERIC,
     KF_SPARSE_TILED,
-    KF_TILED_DMA4, // 256 x 256, direct global -> LDS copies, 4 LDS stages
-    KF_TILED_DMA5, // same with 5 LDS stages (160 KB)
     KF_TILED_256W8,  // 256 x 256, 8 waves (2 per SIMD) as 2 x 4, 128 x 64 per wave
     KF_TILED_256W8T, // 256 x 256, 8 waves as 4 x 2, 64 x 128 per wave
-    KF_PINGPONG4,    // 256 x 256, 8 waves in two out-of-phase groups, 4 LDS stages
-    KF_PINGPONG5,    // same with 5 LDS stages
     KF_SPARSE_DMA8,  // 2:4 A, 256 x 256, 8 waves, direct global -> LDS copies, 3 stages
-    KF_TILED_256W8L, // 256 x 256, 8 waves of 128 x 64, 128-byte K tiles, 2 direct-copy stages
     KF_MX_GENERIC,   // MX block-scaled, any format pair
     KF_MX_TILED,     // MX block-scaled, 256 x 256 4-wave tile, pairs of one width (8 or 4 bits)
     KF_W4_GENERIC,   // W4A16, any shape

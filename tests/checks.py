@@ -128,3 +128,24 @@ def check(D, d_type, D_ref, Y, S, in_type, alpha=1.0):
                 S.reshape(-1)[i])
         return Result(nb == 0, n, float(norm.max()) if n else 0.0, int((~first & second).sum()),
                       nb, det)
+
+
+def check_rows(D, d_type, D_ref, Y, S, in_type, alpha=1.0, rows=512):
+    """check() over an [M,N] output in blocks of `rows` rows (bounded
+    temporaries at full size); one Result for the whole output whose detail
+    names the first bad element's (row, column)."""
+    D = np.asarray(D)
+    M = D.shape[0]
+    tot = Result(True, 0)
+    for r0 in range(0, M, rows):
+        r1 = min(M, r0 + rows)
+        r = check(D[r0:r1], d_type, D_ref[r0:r1], None if Y is None else Y[r0:r1],
+                  None if S is None else S[r0:r1], in_type, alpha)
+        if r.n_bad and tot.ok:
+            tot.detail = "rows %d..%d: %s" % (r0, r1 - 1, r.detail)
+        tot.ok &= r.ok
+        tot.n += r.n
+        tot.max_norm_err = max(tot.max_norm_err, r.max_norm_err)
+        tot.n_second_clause += r.n_second_clause
+        tot.n_bad += r.n_bad
+    return tot

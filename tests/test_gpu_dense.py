@@ -66,11 +66,10 @@ def test_dense_parity(orc, a_type, b_type, algo, shape):
     compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, algo, expect_kernel=algo)
 
 
-@pytest.mark.parametrize("family", ["tiled256", "tiled256dma4", "tiled256dma5", "tiled256w8",
-                                    "tiled256w8t", "pingpong4", "pingpong5"])
+@pytest.mark.parametrize("family", ["tiled256", "tiled256w8", "tiled256w8t"])
 @pytest.mark.parametrize("a_type,b_type", PAIRS)
 @pytest.mark.parametrize("shape", [(600, 520, 256), (256, 256, 64), (300, 700, 448)])
-def test_dense_parity_dma_variants(orc, monkeypatch, family, a_type, b_type, shape):
+def test_dense_parity_256_variants(orc, monkeypatch, family, a_type, b_type, shape):
     """Every 256 x 256 kernel variant, each selected through the
     STGEMM_FORCE_KERNEL tuning override (the automatic choice takes one of
     them per operand type)."""
@@ -79,26 +78,6 @@ def test_dense_parity_dma_variants(orc, monkeypatch, family, a_type, b_type, sha
     A, B, C, _ = make(a_type, b_type, M, N, K, seed=zlib.crc32(repr((family, a_type, shape)).encode()))
     d_type = "s32" if a_type == "s8" else "f32"
     compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, "auto", expect_kernel=family)
-
-
-@pytest.mark.parametrize("a_type,b_type", PAIRS)
-@pytest.mark.parametrize("shape", [(600, 520, 256), (256, 256, 128), (300, 700, 384),
-                                   (520, 264, 1152)])
-def test_dense_parity_long_k_tiles(orc, monkeypatch, a_type, b_type, shape):
-    """The 256 x 256 kernel with 128-byte K tiles (K bytes a multiple of 128;
-    selected through the STGEMM_FORCE_KERNEL tuning override)."""
-    monkeypatch.setenv("STGEMM_FORCE_KERNEL", "tiled256w8l")
-    M, N, K = shape
-    A, B, C, _ = make(a_type, b_type, M, N, K, seed=zlib.crc32(repr(("w8l", a_type, shape)).encode()))
-    d_type = "s32" if a_type == "s8" else "f32"
-    compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, "auto", expect_kernel="tiled256w8l")
-
-
-def test_long_k_tiles_need_whole_128_byte_tiles(monkeypatch):
-    """K bytes not a multiple of 128: the tuning override is ignored."""
-    monkeypatch.setenv("STGEMM_FORCE_KERNEL", "tiled256w8l")
-    assert G.gemm_plan(G.make_desc(512, 512, 256, "bf16", "bf16", "f32")).name.startswith("tiled256w8l")
-    assert not G.gemm_plan(G.make_desc(512, 512, 96, "bf16", "bf16", "f32")).name.startswith("tiled256w8l")
 
 
 @pytest.mark.parametrize("a_type,b_type", PAIRS)
@@ -131,9 +110,9 @@ def test_skinny_is_chosen_for_small_m():
     assert G.gemm_plan(G.make_desc(17, 8192, 8192, "bf16", "bf16", "bf16")).name != "skinny_bf16"
 
 
-@pytest.mark.parametrize("family", ["tiled256dma5"])
+@pytest.mark.parametrize("family", ["tiled256w8"])
 @pytest.mark.parametrize("d_type", ["f16", "bf16"])
-def test_dma_epilogue(orc, monkeypatch, family, d_type):
+def test_forced_family_epilogue(orc, monkeypatch, family, d_type):
     monkeypatch.setenv("STGEMM_FORCE_KERNEL", family)
     M, N, K = 520, 390, 320
     A, B, C, bias = make("e4m3", "e5m2", M, N, K, seed=17, bias=True)
@@ -158,7 +137,7 @@ def test_epilogue_variants(orc, a_type, b_type, d_type, algo, epi):
             alpha=epi.get("alpha", 1.0), relu=epi.get("relu", False))
 
 
-@pytest.mark.parametrize("algo", ["tiled256", "tiled128", "generic", "tiled256dma5", "tiled256w8l"])
+@pytest.mark.parametrize("algo", ["tiled256", "tiled128", "generic", "tiled256w8", "tiled256w8t"])
 @pytest.mark.parametrize("a_type,b_type,d_type", [("bf16", "bf16", "bf16"), ("f16", "f16", "f16"),
                                                   ("e4m3", "e5m2", "f16"),
                                                   ("e4m3", "e5m2", "bf16")])
@@ -221,7 +200,7 @@ def test_padded_leading_dimensions(orc, monkeypatch):
     Cp = rng.uniform(-1, 1, (M, ldc)).astype(np.float32)
     Dr, Y, S = orc.gemm(np.ascontiguousarray(Ap[:, :K]), np.ascontiguousarray(Bp[:, :K]),
                         np.ascontiguousarray(Cp[:, :N]), None, M, N, K, "bf16", "bf16", "bf16")
-    for algo in ["tiled128", "tiled256", "generic", "tiled256dma5", "tiled256w8"]:
+    for algo in ["tiled128", "tiled256", "generic", "tiled256w8", "tiled256w8t"]:
         say("padded", algo)
         monkeypatch.delenv("STGEMM_FORCE_KERNEL", raising=False)
         if algo.startswith("tiled256") and algo != "tiled256":
@@ -258,6 +237,34 @@ def test_in_place_accumulate_d_equals_c(orc):
     D, _ = gpu_gemm(A, B, None, None, M, N, K, "f16", "f16", "f32", c_dev=tC, out=tC)
     Dr, Y, S = orc.gemm(A, B, C, None, M, N, K, "f16", "f16", "f32")
     assert check(D, "f32", Dr, Y, S, "f16").ok
+
+
+def test_overlapping_d_is_rejected():
+    """D may be C itself (same element size and leading dimension); any other
+    overlap of D with C, A, B or bias is refused before a launch."""
+    M, N, K = 64, 64, 64
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    base = buf.data_ptr()
+
+    def run(d_type, D, C=None, A=None, B=None, bias=None, ldc=0):
+        desc = G.make_desc(M, N, K, "bf16", "bf16", d_type, has_c=C is not None,
+                           has_bias=bias is not None, ldc=ldc)
+        plan = G.gemm_plan(desc)
+        try:
+            G.gemm_run(plan, A or base + 600000, B or base + 700000, C, bias, D)
+            torch.cuda.synchronize()
+            return G.GEMM_OK
+        except G.GemmError as e:
+            return e.status
+
+    assert run("f32", base, C=base) == G.GEMM_OK                      # in place
+    assert run("bf16", base, C=base) == G.GEMM_ERR_UNSUPPORTED        # narrower D over C
+    assert run("f32", base, C=base, ldc=N + 4) == G.GEMM_ERR_UNSUPPORTED  # other pitch
+    assert run("f32", base + 256, C=base) == G.GEMM_ERR_UNSUPPORTED   # shifted
+    assert run("f32", base, A=base + 1024) == G.GEMM_ERR_UNSUPPORTED  # D over A
+    assert run("f32", base, B=base + 4096) == G.GEMM_ERR_UNSUPPORTED  # D over B
+    assert run("f32", base, bias=base + 64) == G.GEMM_ERR_UNSUPPORTED  # D over bias
+    assert run("f32", base, C=base + M * N * 4) == G.GEMM_OK          # adjacent, disjoint
 
 
 @pytest.mark.parametrize("algo", ["tiled128", "generic"])

@@ -153,9 +153,10 @@ def test_mn_plan_choices(monkeypatch):
     assert name(8192, 8192, 8192, "s8", "s32", a_layout="col") == "tiled256w8t_s8_acol"
     assert name(520, 512, 512, "s8", "s32", a_layout="col").startswith("generic")  # M % 16
     assert name(512, 512, 96, "e4m3", "f32", b_layout="row").startswith("generic")  # K % 64
-    # tuning families that do not take MN-major operands are not forced
-    monkeypatch.setenv("STGEMM_FORCE_KERNEL", "pingpong4")
-    assert name(512, 512, 512, "bf16", "bf16", b_layout="row").startswith("tiled128")
+    # a 256 x 256 arrangement other than the type's own does not take
+    # MN-major operands: forcing it is ignored
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", "tiled256w8t")
+    assert name(8192, 8192, 8192, "bf16", "bf16", b_layout="row") == "tiled256w8_bf16_brow"
 
 
 NS = 4096

@@ -151,17 +151,6 @@ def test_mx_and_w4_fp8_outputs(orc):
         assert r.ok, r
 
 
-@pytest.mark.parametrize("fam", ["pingpong4", "tiled256dma4", "tiled256w8l"])
-def test_tuning_only_families_refuse_fp8_outputs(monkeypatch, fam):
-    """Those variants are built without the FP8 output kinds: forcing them for
-    an FP8 output keeps the plan's own choice."""
-    monkeypatch.setenv("STGEMM_FORCE_KERNEL", fam)
-    bf = G.gemm_plan(G.make_desc(512, 512, 512, "bf16", "bf16", "bf16", has_c=False))
-    assert bf.name.startswith(fam)
-    f8 = G.gemm_plan(G.make_desc(512, 512, 512, "bf16", "bf16", "e4m3", has_c=False))
-    assert not f8.name.startswith(fam), f8.name
-
-
 @pytest.mark.parametrize("fam,shape", [("tiled256w8", (256, 256, 128)), ("skinny", (16, 256, 256)),
                                        ("generic", (40, 72, 64))],
                          ids=["tiled256w8", "skinny", "generic"])

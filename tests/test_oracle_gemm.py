@@ -223,6 +223,88 @@ def test_entries_match_full(orc):
     assert np.array_equal(Ye, Y[rows, cols]) and np.array_equal(Se, S[rows, cols])
 
 
+def _py_int_dot(A, B, m, n, K, a_col, b_col):
+    """sum_k A[m,k] B[k,n] in Python integers (no numpy arithmetic)."""
+    s = 0
+    for k in range(K):
+        a = int(A[k, m]) if a_col else int(A[m, k])
+        b = int(B[n, k]) if b_col else int(B[k, n])
+        s += a * b
+    return s
+
+
+def _wrap32(x):
+    return (x + 2 ** 31) % 2 ** 32 - 2 ** 31
+
+
+@pytest.mark.parametrize("a_col,b_col", [(False, True), (True, False)])
+@pytest.mark.parametrize("mode", ["wrap", "saturate", "bf16", "f32_epi"])
+def test_entries_s8_match_full_and_integer_sums(orc, a_col, b_col, mode):
+    """The integer branch of gemm_entries (the checker of every sampled s8
+    entry at full size): equal to the full oracle in D, Y and S, and to sums
+    of Python integers, for s32 outputs (wrapping or saturating, the Ampere
+    section's .satfinite-or-wrap rule of "NVIDIA MMA") and for the int8 ->
+    float epilogue.  C near the int32 bounds makes a fifth of the entries
+    leave the int32 range."""
+    rng = np.random.default_rng(11)
+    M, N, K = 23, 37, 320
+    A = rng.integers(-128, 128, size=(K, M) if a_col else (M, K), dtype=np.int8)
+    B = rng.integers(-128, 128, size=(N, K) if b_col else (K, N), dtype=np.int8)
+    kw = dict(a_col_major=a_col, b_col_major=b_col)
+    if mode in ("wrap", "saturate"):
+        C = rng.integers(-2 ** 31, 2 ** 31, size=(M, N), dtype=np.int64)
+        near = np.sign(C) * (2 ** 31 - 1 - rng.integers(0, 2 ** 15, (M, N)))
+        C = np.where(rng.random((M, N)) < 0.5, near, C).astype(np.int32)
+        d_type, bias, alpha, relu = "s32", None, 1.0, False
+        kw["saturate"] = mode == "saturate"
+    else:
+        C = rng.uniform(-1e5, 1e5, size=(M, N)).astype(np.float32)
+        d_type = "bf16" if mode == "bf16" else "f32"
+        bias = rng.uniform(-1e3, 1e3, size=N).astype(np.float32)
+        alpha, relu = 0.75, True
+    D, Y, S = orc.gemm(A, B, C, bias, M, N, K, "s8", "s8", d_type, alpha=alpha, relu=relu, **kw)
+    rows = np.concatenate([np.arange(M), rng.integers(0, M, 200)])
+    cols = np.concatenate([np.arange(M) % N, rng.integers(0, N, 200)])
+    De, Ye, Se = orc.gemm_entries(A, B, C, bias, M, N, K, "s8", "s8", d_type, rows, cols,
+                                  alpha=alpha, relu=relu, **kw)
+    assert np.array_equal(De, D[rows, cols])
+    assert np.array_equal(Ye, Y[rows, cols]) and np.array_equal(Se, S[rows, cols])
+    n_out = 0
+    for i, (m, n) in enumerate(zip(rows, cols)):
+        acc = _py_int_dot(A, B, m, n, K, a_col, b_col)
+        sabs = sum(abs((int(A[k, m]) if a_col else int(A[m, k])) *
+                       (int(B[n, k]) if b_col else int(B[k, n]))) for k in range(K))
+        c = int(C[m, n]) if d_type == "s32" else Fraction(float(C[m, n]))
+        assert Se[i] == float(sabs + abs(c))
+        if d_type == "s32":
+            t = acc + c
+            n_out += not (-2 ** 31 <= t < 2 ** 31)
+            want = max(-2 ** 31, min(2 ** 31 - 1, t)) if mode == "saturate" else _wrap32(t)
+            assert int(De[i]) == want
+        else:
+            # the int32 sum (exact here) through the fp64 epilogue
+            y = Fraction(alpha) * (acc + c) + Fraction(float(bias[n]))
+            y = max(y, Fraction(0))
+            assert Ye[i] == float(y)
+    if d_type == "s32":
+        assert n_out > len(rows) // 10  # the wrap / clamp is exercised
+
+
+def test_entries_s8_wrap_closed_form(orc):
+    """A = B = -128 everywhere: every sum is 16384 K.  At K = 131072 that is
+    2^31, which wraps to -2^31 (saturates to 2^31 - 1); one K group less
+    (K = 131068) stays 2^31 - 65536, in range."""
+    for K, wrap, sat in [(131072, -2 ** 31, 2 ** 31 - 1), (131068, 2 ** 31 - 65536, 2 ** 31 - 65536)]:
+        A = np.full((2, K), -128, np.int8)
+        B = np.full((3, K), -128, np.int8)
+        rows, cols = np.array([0, 1, 1]), np.array([2, 0, 1])
+        for saturate, want in [(False, wrap), (True, sat)]:
+            D, Y, S = orc.gemm_entries(A, B, None, None, 2, 3, K, "s8", "s8", "s32", rows, cols,
+                                       saturate=saturate)
+            assert (D == want).all() and (Y == want).all()
+            assert (S == 16384.0 * K).all()
+
+
 @pytest.mark.parametrize("d_type", ["f32", "f16", "bf16"])
 def test_epilogue_f32_is_exactly_rounded(orc, d_type):
     """The fp32-semantics epilogue: fmaf(alpha, t, bias) is one RNE rounding of
