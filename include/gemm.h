@@ -216,6 +216,20 @@ gemm_status_t gemm_sparse24_sizes(int64_t M, int64_t K, int32_t a_type, size_t *
 gemm_status_t gemm_sparse24_compress(int64_t M, int64_t K, int32_t a_type, const void *A,
                                      void *values, uint32_t *meta, gemm_stream_t stream);
 
+/* gemm_sparse24_compress for callers that cannot allocate device memory
+ * (code that must not call hipMalloc: tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, output, synchronisation and status
+ * codes as gemm_sparse24_compress, and the same sizes are accepted (the
+ * scratch it needs does not grow with M or K), but it allocates nothing:
+ * the error flag gemm_sparse24_compress allocates per call lives instead in
+ * a static device array of 64 ints (256 bytes) that each GPU the library
+ * runs on holds until the process ends.  The flag is cleared by a kernel on
+ * `stream` at the start of every call.  All calls on one GPU share that
+ * array: calls that overlap on one GPU (from several host threads or
+ * streams) race on the flag and may report each other's NOT_SPARSE24. */
+gemm_status_t gemm_sparse24_compress_noalloc(int64_t M, int64_t K, int32_t a_type, const void *A,
+                                             void *values, uint32_t *meta, gemm_stream_t stream);
+
 /* Enqueue D = epilogue(A*B + C) with A given as (values, meta) from
  * gemm_sparse24_compress.  The plan must have sparse_a == 1; its A/B types,
  * accumulator and epilogue follow the dense rules (f16 x f16, bf16 x bf16,

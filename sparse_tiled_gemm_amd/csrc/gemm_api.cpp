@@ -825,6 +825,50 @@ gemm_status_t gemm_sparse24_compress(int64_t M, int64_t K, int32_t a_type, const
     return ok();
 }
 
+gemm_status_t gemm_sparse24_compress_noalloc(int64_t M, int64_t K, int32_t a_type, const void *A,
+                                             void *values, uint32_t *meta, gemm_stream_t stream)
+{
+    size_t vb = 0, mb = 0;
+    gemm_status_t st = gemm_sparse24_sizes(M, K, a_type, &vb, &mb);
+    if (st != GEMM_OK)
+        return st;
+    if (M == 0 || K == 0)
+        return ok();
+    if (!A || !values || !meta)
+        return fail(GEMM_ERR_NULL_POINTER, "A, values or meta is NULL");
+    const int eb = elem_bytes(a_type);
+    if (!aligned(A, 4 * eb) || !aligned(values, 2 * eb) || !aligned(meta, 4))
+        return fail(GEMM_ERR_MISALIGNED,
+                    "A must be aligned to 4 elements, values to 2 elements, meta to 4 bytes");
+    int dev = 0;
+    st = check_device(&dev, nullptr);
+    if (st != GEMM_OK)
+        return st;
+    // the flag is element 0 of the library's static device scratch (looked
+    // up on this device's first call), cleared by a kernel on the stream
+    int *flag = nullptr;
+    hipError_t e = sparse24_scratch(dev, &flag);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    hipStream_t s = (hipStream_t)stream;
+    int host_flag = 0;
+    e = launch_zero_ints(flag, 1, s);
+    if (e == hipSuccess)
+        e = launch_sparse24_compress(eb, eb == 2 ? 0x7FFFu : (a_type == GEMM_S8 ? 0xFFu : 0x7Fu),
+                                     M, K, A, values, meta, flag, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
+        return hip_fail(e, "sparse24 compress (no allocation)");
+    if (host_flag)
+        return fail(GEMM_ERR_NOT_SPARSE24,
+                    "A has a group of 4 with more than two non-zeros (first such row: %d)",
+                    0x7fffffff - host_flag);
+    return ok();
+}
+
 gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, const uint32_t *meta,
                                 const void *B, const void *C, const void *bias, void *D,
                                 gemm_stream_t stream)

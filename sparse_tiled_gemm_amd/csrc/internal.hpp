@@ -63,6 +63,12 @@ hipError_t launch_sparse(int family, int op, const SparseArgs &a, hipStream_t s)
 hipError_t launch_sparse24_compress(int elem_bytes, uint32_t zero_mask, int64_t M, int64_t K,
                                     const void *A, void *values, uint32_t *meta, int *flag,
                                     hipStream_t s);
+// Allocation-free compressor: the device address of this library's static
+// scratch array on device `dev` (current), SPARSE24_SCRATCH_INTS ints, of
+// which the flag uses element 0; and a kernel that zeroes n ints.
+constexpr int SPARSE24_SCRATCH_INTS = 64;
+hipError_t sparse24_scratch(int dev, int **out);
+hipError_t launch_zero_ints(int *p, int n, hipStream_t s);
 
 } // namespace stg
 

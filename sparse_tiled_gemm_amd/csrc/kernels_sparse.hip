@@ -20,6 +20,8 @@
 //   from an index register and skips the dropped half of A - the "twice the
 //   K per instruction" of the page's sparse MMA.
 // k_sparse_dma8: 8 waves, direct global -> LDS copies (the fast path).
+#include <mutex>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -167,6 +169,14 @@ __global__ __launch_bounds__(256) void k_sparse24_compress(int64_t M, int64_t K,
         atomicMax(flag, (int)(0x7fffffff - m));
 }
 
+// Fill n ints at p with 0 (clears the compressor's flag in device scratch
+// without hipMemsetAsync).
+__global__ __launch_bounds__(64) void k_zero_ints(int *p, int n)
+{
+    for (int i = threadIdx.x; i < n; i += 64)
+        p[i] = 0;
+}
+
 hipError_t launch_sparse24_compress(int elem_bytes, uint32_t zero_mask, int64_t M, int64_t K,
                                     const void *A, void *values, uint32_t *meta, int *flag,
                                     hipStream_t s)
@@ -183,6 +193,48 @@ hipError_t launch_sparse24_compress(int elem_bytes, uint32_t zero_mask, int64_t 
                            (const uint8_t *)A, (uint8_t *)values, meta, zero_mask, flag);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+} // namespace stg
+
+// ---------------------------------------------------------------- allocation-free flag
+
+// Device scratch of gemm_sparse24_compress_noalloc: its offending-row flag
+// (element 0; the rest is headroom) lives here instead of in memory
+// allocated per call.  Every GPU the library runs on holds its own copy
+// until the process ends.  Host code never uses the array's name as an
+// address: the device address is looked up once per device with
+// hipGetSymbolAddress (below) and only that pointer reaches kernels.
+static __device__ __align__(256) int scratch[stg::SPARSE24_SCRATCH_INTS];
+
+namespace stg {
+
+namespace {
+std::mutex g_scratch_mu;
+int *g_scratch_ptr[64]; // per device: the address of `scratch` on that device
+} // namespace
+
+hipError_t sparse24_scratch(int dev, int **out)
+{
+    if (dev < 0 || dev >= 64)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // the caller made `dev` current
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[dev] = (int *)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_zero_ints(int *p, int n, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_zero_ints, dim3(1), dim3(64), 0, s, p, n);
     return hipGetLastError();
 }
 

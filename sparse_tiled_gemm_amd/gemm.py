@@ -5,7 +5,7 @@ addresses; PyTorch provides memory and streams only.
 
 The functions carry the C names: gemm_validate_desc, gemm_plan,
 gemm_plan_destroy, gemm_plan_describe, gemm_run, gemm_sparse24_sizes,
-gemm_sparse24_compress, gemm_sparse24_run, gemm_mx_run, gemm_w4a16_run, gemm_status_string,
+gemm_sparse24_compress, gemm_sparse24_compress_noalloc, gemm_sparse24_run, gemm_mx_run, gemm_w4a16_run, gemm_status_string,
 gemm_last_error.  Non-OK statuses raise GemmError (except
 gemm_validate_desc, which returns the status).
 """
@@ -83,6 +83,7 @@ def load():
         "gemm_sparse24_sizes": (st, [i64, i64, i32, ctypes.POINTER(ctypes.c_size_t),
                                      ctypes.POINTER(ctypes.c_size_t)]),
         "gemm_sparse24_compress": (st, [i64, i64, i32, vp, vp, vp, vp]),
+        "gemm_sparse24_compress_noalloc": (st, [i64, i64, i32, vp, vp, vp, vp]),
         "gemm_sparse24_run": (st, [vp, vp, vp, vp, vp, vp, vp, vp]),
         "gemm_status_string": (ctypes.c_char_p, [st]),
         "gemm_last_error": (ctypes.c_char_p, []),
@@ -215,6 +216,11 @@ def gemm_sparse24_sizes(M, K, a_type="f16"):
 def gemm_sparse24_compress(M, K, a_type, A, values, meta, stream=None):
     _check(load().gemm_sparse24_compress(M, K, DTYPES[a_type], _ptr(A), _ptr(values), _ptr(meta),
                                          _stream(stream)))
+
+
+def gemm_sparse24_compress_noalloc(M, K, a_type, A, values, meta, stream=None):
+    _check(load().gemm_sparse24_compress_noalloc(M, K, DTYPES[a_type], _ptr(A), _ptr(values),
+                                                 _ptr(meta), _stream(stream)))
 
 
 def gemm_sparse24_run(plan, values, meta, B, C, bias, D, stream=None):
