@@ -2,7 +2,7 @@
 """Throughput of the gfx950 GEMM library on its synthetic workloads.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-extras] [--no-cpu-baseline]
+                    [--no-extras] [--no-cpu-baseline] [--ceiling]
 
 One step is one call of the library (gemm_run, or gemm_sparse24_run for the
 2:4 workload) over the workload's operands, which are resident in device
@@ -223,6 +223,35 @@ def cpu_baseline(p, rows=4096):
                       "accumulation, same epilogue" % (r - 1, r, N, K, M, N, K)}
 
 
+def ceiling(steps, warmup):
+    """The MFMA-only throughput ceiling (gemm_diag_mfma_loop): one workgroup
+    of 8 waves per compute unit issuing nothing but MFMAs on random register
+    operands; each launch sized to about a millisecond."""
+    import torch
+    from sparse_tiled_gemm_amd import gemm as G
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    res = {}
+    for kind, name, flop, peak in [(0, "bf16", 32768, PEAK["bf16"]), (1, "fp8", 131072, PEAK["fp8"]),
+                                   (2, "s8", 65536, PEAK["s8"])]:
+        per_iter = cus * 8 * 64 * flop
+        iters = max(1, int(0.6 * peak * 1e12 * 1e-3 / per_iter))
+        for _ in range(warmup):
+            G.gemm_diag_mfma_loop(kind, cus, iters, out)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            G.gemm_diag_mfma_loop(kind, cus, iters, out)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        rate = per_iter * iters / (ms * 1e-3) / 1e12
+        res[name] = {"TFLOPS" if kind != 2 else "TOPS": rate, "frac_peak": rate / peak,
+                     "ms_per_launch": ms, "iters": iters, "workgroups": cus}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,6 +265,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (x3), the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="run only the MFMA-only ceiling diagnostic (bf16, fp8, int8) and print "
+                         "its rates as one JSON line")
     ap.add_argument("--force-kernel", default=None,
                     help="kernel family to force (tuning: sets STGEMM_FORCE_KERNEL)")
     args = ap.parse_args()
@@ -253,6 +285,13 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": a.numel() * 4, "copies": 3}))
+        return
+    if args.ceiling:
+        import torch
+        torch.cuda.set_device(0)
+        from sparse_tiled_gemm_amd import gemm as G
+        G.load()
+        print(json.dumps({"mfma_only_ceiling": ceiling(args.steps, args.warmup)}))
         return
     if args.force_kernel:
         os.environ["STGEMM_FORCE_KERNEL"] = args.force_kernel

@@ -11,6 +11,7 @@
 #include <mutex>
 #include <new>
 
+#include "gemm_diag.h"
 #include "internal.hpp"
 
 using namespace stg;
@@ -1014,6 +1015,23 @@ gemm_status_t gemm_w4a16_run(const gemm_plan_t *plan, const void *A, const void 
     if ((fam == KF_W4_TILED || fam == KF_W4_SKINNY) && (!aligned(A, 16) || !aligned(B, 16)))
         fam = plan->fallback;
     hipError_t e = launch_w4(fam, plan->op, g, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "kernel launch");
+    return ok();
+}
+
+gemm_status_t gemm_diag_mfma_loop(int32_t kind, int32_t blocks, int64_t iters, float *out,
+                                  gemm_stream_t stream)
+{
+    if (!out)
+        return fail(GEMM_ERR_NULL_POINTER, "out is NULL");
+    if (kind < 0 || kind > 2 || blocks < 1 || blocks > (1 << 20) || iters < 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "kind 0..2, blocks 1..2^20, iters >= 0");
+    int dev = 0;
+    gemm_status_t st = check_device(&dev, nullptr);
+    if (st != GEMM_OK)
+        return st;
+    hipError_t e = launch_mfma_loop(kind, blocks, iters, out, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "kernel launch");
     return ok();

@@ -85,6 +85,7 @@ def load():
         "gemm_sparse24_compress": (st, [i64, i64, i32, vp, vp, vp, vp]),
         "gemm_sparse24_compress_noalloc": (st, [i64, i64, i32, vp, vp, vp, vp]),
         "gemm_sparse24_run": (st, [vp, vp, vp, vp, vp, vp, vp, vp]),
+        "gemm_diag_mfma_loop": (st, [i32, i32, i64, vp, vp]),
         "gemm_status_string": (ctypes.c_char_p, [st]),
         "gemm_last_error": (ctypes.c_char_p, []),
     }
@@ -236,3 +237,9 @@ def gemm_mx_run(plan, A, scale_a, B, scale_b, C, bias, D, stream=None):
 def gemm_w4a16_run(plan, A, B, scales, zeros, C, bias, D, stream=None):
     _check(load().gemm_w4a16_run(plan.handle, _ptr(A), _ptr(B), _ptr(scales), _ptr(zeros),
                                  _ptr(C), _ptr(bias), _ptr(D), _stream(stream)))
+
+
+def gemm_diag_mfma_loop(kind, blocks, iters, out, stream=None):
+    """Diagnostic MFMA-only loop (include/gemm_diag.h); kind 0 bf16, 1 fp8,
+    2 int8; out: a device float tensor of blocks * 512 elements."""
+    _check(load().gemm_diag_mfma_loop(kind, blocks, iters, _ptr(out), _stream(stream)))

@@ -16,6 +16,7 @@
 #include <cstring>
 
 #include "gemm.h"
+#include "gemm_diag.h"
 #include "internal.hpp"
 
 // ------------------------------------------------------------ HIP stubs
@@ -123,6 +124,12 @@ hipError_t launch_sparse24_compress(int eb, uint32_t, int64_t M, int64_t K, cons
 hipError_t sparse24_scratch(int, int **out)
 {
     *out = g_flag_store;
+    return hipSuccess;
+}
+hipError_t launch_mfma_loop(int kind, int blocks, int64_t iters, float *out, hipStream_t)
+{
+    EXPECT(kind >= 0 && kind <= 2 && blocks >= 1 && iters >= 0 && out);
+    ++g_launches;
     return hipSuccess;
 }
 hipError_t launch_zero_ints(int *p, int n, hipStream_t)
@@ -240,6 +247,10 @@ int main(int argc, char **argv)
     g_flag_store[0] = 0x7fffffff - 5;
     EXPECT(gemm_sparse24_compress_noalloc(64, 64, GEMM_F16, fake(1), fake(2),
                                           (uint32_t *)fake(3), nullptr) == GEMM_OK);
+    EXPECT(gemm_diag_mfma_loop(0, 256, 100, (float *)fake(1), nullptr) == GEMM_OK);
+    EXPECT(gemm_diag_mfma_loop(3, 256, 100, (float *)fake(1), nullptr) == GEMM_ERR_INVALID_VALUE);
+    EXPECT(gemm_diag_mfma_loop(1, 0, 100, (float *)fake(1), nullptr) == GEMM_ERR_INVALID_VALUE);
+    EXPECT(gemm_diag_mfma_loop(2, 8, 1, nullptr, nullptr) == GEMM_ERR_NULL_POINTER);
     for (int s = -2; s < 10; ++s)
         EXPECT(gemm_status_string((gemm_status_t)s) != nullptr);
 

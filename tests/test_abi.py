@@ -26,6 +26,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), n
     assert "gemm_sparse24_run" in names and "gemm_plan" in names
+    assert "gemm_diag_mfma_loop" in names and "gemm_sparse24_compress_noalloc" in names
 
 
 def test_status_strings():
