@@ -77,8 +77,10 @@ typedef enum {
     GEMM_F6_E2M3 = 8, /* bias 1, max 7.5, no inf/NaN; 4 elements in 3 bytes */
     GEMM_F6_E3M2 = 9, /* bias 3, max 28, no inf/NaN; 4 elements in 3 bytes */
     GEMM_F4_E2M1 = 10, /* bias 1, max 6, no inf/NaN; 2 elements per byte */
-    GEMM_U4 = 11       /* W4A16 weight codes 0..15, two per byte along K (the
+    GEMM_U4 = 11,      /* W4A16 weight codes 0..15, two per byte along K (the
                           even element in the low nibble); B only */
+    GEMM_U8 = 12       /* uint8 0..255: A and / or B of an integer GEMM, paired
+                          with S8 or U8 */
 } gemm_dtype_t;
 
 typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout_t;
@@ -109,18 +111,22 @@ typedef enum {
  *   differ): c_type F32, F16 or BF16 (a 16-bit C is widened exactly to fp32;
  *   it takes the element-wise epilogue), d_type F32 / F16 / BF16 / F8_E4M3 /
  *   F8_E5M2, any epilogue.
- *   a = b = S8: either c_type S32, d_type S32, alpha == 1, no bias, no
- *   activation; or (dequantising epilogue) c_type F32 / F16 / BF16, d_type F32 / F16 /
- *   BF16 / F8_E4M3 / F8_E5M2, any epilogue, where the int32 sum is first
- *   rounded to fp32 (to nearest even).  The int32 sum wraps modulo 2^32 in
- *   both.  With saturate = 1 (int32 output only, K < 131072, where the sum of
- *   products cannot leave the int32 range) D = clamp(acc + C) to
- *   [-2^31, 2^31 - 1] instead ("NVIDIA MMA", section "Ampere: FP16/BF16 and
- *   integer MMA baseline": integer MMA saturates with .satfinite, else
- *   wraps).
+ *   a, b in {S8, U8} (any pairing: the INT8 rows of the instruction tables
+ *   on "NVIDIA MMA", section "Ampere: FP16/BF16 and integer MMA baseline",
+ *   take signed or unsigned A and B): either c_type S32, d_type S32,
+ *   alpha == 1, no bias, no activation; or (dequantising epilogue) c_type
+ *   F32 / F16 / BF16, d_type F32 / F16 / BF16 / F8_E4M3 / F8_E5M2, any
+ *   epilogue, where the int32 sum is first rounded to fp32 (to nearest
+ *   even).  The int32 sum wraps modulo 2^32 in both.  With saturate = 1
+ *   (int32 output only, and K small enough that the sum of products cannot
+ *   leave the int32 range: K * max|a| * max|b| < 2^31, i.e. K < 131072 for
+ *   s8 x s8, 65794 for u8 x s8 or s8 x u8, 33026 for u8 x u8) D = clamp(acc +
+ *   C) to [-2^31, 2^31 - 1] instead (same section: integer MMA saturates with
+ *   .satfinite, else wraps).  The fast kernels take U8 with A row-major and
+ *   B column-major; other layouts of a U8 operand run the generic kernel.
  *   sparse_a = 1: any of the pairs above, A row-major and packed,
  *   K % 4 == 0; used with gemm_sparse24_run (A is then given in compressed
- *   form).
+ *   form).  A U8 A of a 2:4 product runs the generic kernel.
  *   block_scale = 32 (MX): a, b any of F8_E4M3, F8_E5M2, F6_E2M3, F6_E3M2,
  *   F4_E2M1 (they may differ), A row-major, B column-major, K % 32 == 0,
  *   rows of whole bytes (lda, ldb in elements); c_type F32, any float
@@ -198,7 +204,7 @@ gemm_status_t gemm_run(const gemm_plan_t *plan, const void *A, const void *B, co
                        const void *bias, void *D, gemm_stream_t stream);
 
 /* Bytes of the compressed form of an M x K A of type a_type (f16, bf16,
- * fp8 E4M3/E5M2 or s8; K % 4 == 0): values are M x K/2 elements of a_type;
+ * fp8 E4M3/E5M2, s8 or u8; K % 4 == 0): values are M x K/2 elements of a_type;
  * metadata is M x ceil(K/32) uint32 whatever the type.  The sparse rows of
  * the instruction tables on "NVIDIA MMA" (sections "Ampere: FP16/BF16 and
  * integer MMA baseline" and "Ada: mma.sync adds FP8") give these types a
@@ -215,7 +221,7 @@ gemm_status_t gemm_sparse24_sizes(int64_t M, int64_t K, int32_t a_type, size_t *
  *   and the nibble (i0 | i1 << 2) at bits 4(g%8)..4(g%8)+3 of
  *   meta[m*ceil(K/32) + g/8]; unused high nibbles are 0.
  * The zeros are +0 and -0 of the float types and 0 of s8 (whose 0x80 is
- * -128); NaN and infinity count as non-zero.  Positions ascend, as the
+ * -128) and of u8; NaN and infinity count as non-zero.  Positions ascend, as the
  * ordered-metadata form on "NVIDIA MMA" (section "Ampere: FP16/BF16 and
  * integer MMA baseline") requires; the bit packing is this library's own.
  * Synchronises `stream` (a one-time weight preprocessing step) and returns

@@ -115,6 +115,7 @@ struct OpF8 {
 struct OpS8 {
     static constexpr int ELEM = 1, LANE_BYTES = 16, KB = 32, BITS = 8;
     static constexpr bool INT = true, MX = false, SPLIT = false, W4 = false;
+    static constexpr bool AU = false, BU = false; // unsigned A / B (OpI8)
     typedef i16_t acc_t;
     __device__ static inline acc_t mma(const uint32_t *a, const uint32_t *b, acc_t c)
     {
@@ -123,6 +124,76 @@ struct OpS8 {
         return __builtin_amdgcn_mfma_i32_32x32x32_i8(va, vb, c, 0, 0, 0);
     }
 };
+
+// 8-bit integer operands of either signedness (the INT8 rows of "NVIDIA
+// MMA", section "Ampere: FP16/BF16 and integer MMA baseline", take signed or
+// unsigned A and B).  gfx950's int8 MFMA is signed only, so an unsigned
+// operand x (0..255) enters it as x - 128 (its bits XOR 0x80) and the exact
+// sum is restored afterwards: with a = a' + 128 AU and b = b' + 128 BU,
+//   sum_k a b = sum_k a' b' + 128 BU sum_k a'[m,k] + 128 AU sum_k b'[k,n]
+//               + 16384 AU BU K,
+// every term taken modulo 2^32 like the int32 accumulator itself, so the
+// result is bit-exact (u8_correct).
+template <bool A_U, bool B_U>
+struct OpI8 : OpS8 {
+    static constexpr bool AU = A_U, BU = B_U;
+};
+template <class OP>
+constexpr bool au_v()
+{
+    if constexpr (requires { OP::AU; })
+        return OP::AU;
+    else
+        return false;
+}
+template <class OP>
+constexpr bool bu_v()
+{
+    if constexpr (requires { OP::BU; })
+        return OP::BU;
+    else
+        return false;
+}
+// XOR mask that turns four packed u8 into the s8 values x - 128
+constexpr uint32_t U8_FLIP = 0x80808080u;
+
+// Sum of the four signed bytes of w, added to acc.
+__device__ STG_AI inline int sum4_s8(uint32_t w, int acc)
+{
+    return __builtin_amdgcn_sdot4((int)w, 0x01010101, acc, false);
+}
+
+// The offset terms of OpI8 for a wave's FM x FN grid of 32x32 int32
+// accumulators.  rs[i]: this lane's partial sum of the signed (shifted) A
+// values of row lane % 32 of fragment row i over its half of K (the two
+// lane halves hold the two halves); cs[j]: the same for column lane % 32 of
+// B's fragment column j.  K: the number of K positions summed.
+template <bool AU, bool BU, int FM, int FN>
+__device__ STG_AI inline void u8_correct(i16_t (&acc)[FM][FN], const int (&rs)[FM],
+                                         const int (&cs)[FN], int64_t K, int lane)
+{
+    if constexpr (AU || BU) {
+        const uint32_t kc = AU && BU ? (uint32_t)((uint64_t)K * 16384u) : 0u;
+        uint32_t cfull[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            cfull[j] = AU ? (uint32_t)(cs[j] + __shfl_xor(cs[j], 32)) * 128u : 0u;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int rfull = BU ? rs[i] + __shfl_xor(rs[i], 32) : 0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                // accumulator register r of this lane is row R of the fragment,
+                // whose full sum lane R holds
+                const int R = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const uint32_t rr = BU ? (uint32_t)__shfl(rfull, R) * 128u : 0u;
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j][r] = (int)((uint32_t)acc[i][j][r] + rr + cfull[j] + kc);
+            }
+        }
+    }
+}
 
 // MX block-scaled product of OCP MX element formats (AF / BF: 0 = E4M3, 1 =
 // E5M2, 2 = E2M3, 3 = E3M2, 4 = E2M1, the selectors of the gfx950

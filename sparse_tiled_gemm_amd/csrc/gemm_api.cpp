@@ -74,10 +74,13 @@ int elem_bytes(int t)
     case GEMM_BF16: return 2;
     case GEMM_F8_E4M3:
     case GEMM_F8_E5M2:
-    case GEMM_S8: return 1;
+    case GEMM_S8:
+    case GEMM_U8: return 1;
     default: return 4;
     }
 }
+bool is_int8(int t) { return t == GEMM_S8 || t == GEMM_U8; }
+bool is_unsigned_op(int op) { return op == OPK_U8S8 || op == OPK_S8U8 || op == OPK_U8U8; }
 
 int op_kind(int a, int b)
 {
@@ -85,8 +88,9 @@ int op_kind(int a, int b)
         return OPK_F16;
     if (a == GEMM_BF16 && b == GEMM_BF16)
         return OPK_BF16;
-    if (a == GEMM_S8 && b == GEMM_S8)
-        return OPK_S8;
+    if (is_int8(a) && is_int8(b))
+        return a == GEMM_S8 ? (b == GEMM_S8 ? OPK_S8 : OPK_S8U8)
+                            : (b == GEMM_S8 ? OPK_U8S8 : OPK_U8U8);
     if (is_fp8(a) && is_fp8(b)) {
         const bool a5 = a == GEMM_F8_E5M2, b5 = b == GEMM_F8_E5M2;
         return a5 ? (b5 ? OPK_F8_E5E5 : OPK_F8_E5E4) : (b5 ? OPK_F8_E4E5 : OPK_F8_E4E4);
@@ -96,8 +100,8 @@ int op_kind(int a, int b)
 
 const char *op_name(int op)
 {
-    static const char *names[] = {"f16", "bf16", "e4m3xe4m3", "e4m3xe5m2", "e5m2xe4m3",
-                                  "e5m2xe5m2", "s8"};
+    static const char *names[] = {"f16",       "bf16", "e4m3xe4m3", "e4m3xe5m2", "e5m2xe4m3",
+                                  "e5m2xe5m2", "s8",   "u8xs8",     "s8xu8",     "u8xu8"};
     return (op >= 0 && op < OPK_COUNT) ? names[op] : "?";
 }
 
@@ -258,7 +262,7 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
     if (d.M < 0 || d.N < 0 || d.K < 0)
         return fail(GEMM_ERR_INVALID_VALUE, "negative size M=%lld N=%lld K=%lld",
                     (long long)d.M, (long long)d.N, (long long)d.K);
-    auto dtype_ok = [](int t) { return t >= GEMM_F16 && t <= GEMM_U4; };
+    auto dtype_ok = [](int t) { return t >= GEMM_F16 && t <= GEMM_U8; };
     if (!dtype_ok(d.a_type) || !dtype_ok(d.b_type) || !dtype_ok(d.d_type) ||
         !(d.c_type == 0 || dtype_ok(d.c_type)))
         return fail(GEMM_ERR_INVALID_VALUE, "unknown dtype code");
@@ -267,13 +271,18 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
         return fail(GEMM_ERR_INVALID_VALUE, "unknown layout code");
     if (d.act != GEMM_ACT_NONE && d.act != GEMM_ACT_RELU)
         return fail(GEMM_ERR_INVALID_VALUE, "unknown activation code");
-    // saturation: int32 outputs, with K small enough that the int32 MFMA sum
-    // itself cannot overflow (|sum| <= K 2^14 < 2^31), so that clamping acc + C
-    // is the exact saturated result
+    // saturation: int32 outputs, with K small enough that the sum of
+    // products itself cannot leave the int32 range (K max|a| max|b| < 2^31),
+    // so that the wrapped sum is the exact one and clamping acc + C is the
+    // exact saturated result
     if (d.saturate != 0 && d.saturate != 1)
         return fail(GEMM_ERR_INVALID_VALUE, "saturate must be 0 or 1");
-    if (d.saturate && (d.d_type != GEMM_S32 || d.K >= 131072))
-        return fail(GEMM_ERR_UNSUPPORTED, "saturation applies to int32 outputs with K < 131072");
+    if (d.saturate) {
+        const int64_t ma = d.a_type == GEMM_U8 ? 255 : 128, mb = d.b_type == GEMM_U8 ? 255 : 128;
+        if (d.d_type != GEMM_S32 || smul(d.K, ma * mb) >= ((int64_t)1 << 31))
+            return fail(GEMM_ERR_UNSUPPORTED, "saturation applies to int32 outputs with "
+                                              "K * max|a| * max|b| < 2^31");
+    }
     if ((d.has_c != 0 && d.has_c != 1) || (d.has_bias != 0 && d.has_bias != 1) ||
         (d.sparse_a != 0 && d.sparse_a != 1))
         return fail(GEMM_ERR_INVALID_VALUE, "has_c / has_bias / sparse_a must be 0 or 1");
@@ -341,14 +350,15 @@ gemm_status_t gemm_validate_desc(const gemm_desc_t *desc)
             return fail(GEMM_ERR_UNSUPPORTED, "float output must be f32, f16, bf16 or fp8");
         return ok();
     }
-    if (d.a_type > GEMM_S32 || d.b_type > GEMM_S32)
+    auto narrow_mx = [](int t) { return t == GEMM_F6_E2M3 || t == GEMM_F6_E3M2 || t == GEMM_F4_E2M1; };
+    if (narrow_mx(d.a_type) || narrow_mx(d.b_type))
         return fail(GEMM_ERR_UNSUPPORTED, "6- and 4-bit float formats need block_scale = 32");
     if (d.d_type > GEMM_S32 || d.c_type > GEMM_S32)
         return fail(GEMM_ERR_UNSUPPORTED, "unsupported C or D type");
 
-    if (d.a_type == GEMM_S8 || d.b_type == GEMM_S8) {
-        if (d.a_type != GEMM_S8 || d.b_type != GEMM_S8)
-            return fail(GEMM_ERR_UNSUPPORTED, "s8 must be paired with s8");
+    if (is_int8(d.a_type) || is_int8(d.b_type)) {
+        if (!is_int8(d.a_type) || !is_int8(d.b_type))
+            return fail(GEMM_ERR_UNSUPPORTED, "8-bit integers (s8, u8) pair with 8-bit integers");
         if (d.d_type == GEMM_S32) {
             if (!(d.c_type == GEMM_S32 || (d.c_type == 0 && !d.has_c)))
                 return fail(GEMM_ERR_UNSUPPORTED, "s32 output takes an s32 C");
@@ -524,14 +534,19 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
                           (d.ldb * eb) % 16 == 0 && d.K * eb / 2 * 256 < lim &&
                           d.ldb * eb * 256 < lim;
         // the 8-wave kernel with direct copies measured fastest (2:4 f16,
-        // 8192^3); it takes K in whole metadata groups of 256 logical K
-        const bool dma8 = fast && d.K % 256 == 0;
+        // 8192^3); it takes K in whole metadata groups of 256 logical K.
+        // Unsigned B: that kernel only (its fragments are offset after the
+        // LDS reads); unsigned A: the generic kernel (the SMFMAC skips the
+        // dropped positions, so the offset correction would depend on the
+        // positions of every row)
+        const bool dma8 = fast && d.K % 256 == 0 && d.a_type != GEMM_U8;
+        const bool fast_any = fast && (!is_unsigned_op(p->op) || dma8);
         const int tiled_fam = dma8 ? KF_SPARSE_DMA8 : KF_SPARSE_TILED;
         int fam = -1;
         switch (d.algo) {
-        case GEMM_ALGO_AUTO: fam = fast ? tiled_fam : KF_SPARSE_GENERIC; break;
+        case GEMM_ALGO_AUTO: fam = fast_any ? tiled_fam : KF_SPARSE_GENERIC; break;
         case GEMM_ALGO_TILED:
-        case GEMM_ALGO_TILED_256: fam = fast ? tiled_fam : -1; break;
+        case GEMM_ALGO_TILED_256: fam = fast_any ? tiled_fam : -1; break;
         case GEMM_ALGO_GENERIC: fam = KF_SPARSE_GENERIC; break;
         default: fam = -1;
         }
@@ -542,7 +557,9 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
         if (const char *force = getenv("STGEMM_FORCE_KERNEL")) { // tuning override
             for (int f : {KF_SPARSE_TILED, KF_SPARSE_DMA8, KF_SPARSE_GENERIC})
                 if (strcmp(force, family_name(f)) == 0 &&
-                    (f == KF_SPARSE_GENERIC || (fast && (f != KF_SPARSE_DMA8 || dma8))))
+                    (f == KF_SPARSE_GENERIC ||
+                     (fast_any && (f != KF_SPARSE_DMA8 || dma8) &&
+                      (f != KF_SPARSE_TILED || !is_unsigned_op(p->op)))))
                     fam = f;
         }
         p->family = fam;
@@ -552,9 +569,12 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
         return ok();
     }
 
-    const bool tiled = tiled_ok(d);
     const int layout = (d.a_layout == GEMM_COL_MAJOR ? 1 : 0) | (d.b_layout == GEMM_ROW_MAJOR ? 2 : 0);
-    const bool skinny = skinny_ok(d);
+    // an unsigned 8-bit operand: the K-contiguous tiled kernels and the
+    // generic one (the MN-major and skinny paths take signed operands only)
+    const bool uns = is_unsigned_op(p->op);
+    const bool tiled = tiled_ok(d) && (!uns || layout == 0);
+    const bool skinny = skinny_ok(d) && !uns;
     int fam = -1;
     const int64_t big_tiles = ceil_div(d.M, 256) * ceil_div(d.N, 256);
     // 256 x 256 tiles: the fastest variant measured per operand type on
@@ -562,7 +582,7 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
     // 64 x 128; fp8: 4 waves of 128 x 128, whose 8-wave forms run short of
     // registers)
     const int op = op_kind(d.a_type, d.b_type);
-    const int fam256 = op == OPK_S8 ? KF_TILED_256W8T
+    const int fam256 = (op == OPK_S8 || uns) ? KF_TILED_256W8T
                        : (op == OPK_F16 || op == OPK_BF16) ? KF_TILED_256W8 : KF_TILED_256;
     const int auto_tiled = big_tiles >= di.num_cu ? fam256 : KF_TILED_128;
     switch (d.algo) {
@@ -585,8 +605,10 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
         // 128 x 128 tile
         for (int f = 0; f < KF_COUNT; ++f) {
             const bool layout_ok = layout == 0 || f == fam256 || f == KF_TILED_128;
+            // unsigned 8-bit operands are built on the 128 tile and w8t only
+            const bool uns_ok = !uns || f == KF_TILED_128 || f == KF_TILED_256W8T;
             if (strcmp(force, family_name(f)) == 0 &&
-                (f == KF_GENERIC || (tiled && is_tiled(f) && layout_ok) ||
+                (f == KF_GENERIC || (tiled && is_tiled(f) && layout_ok && uns_ok) ||
                  (skinny && f == KF_SKINNY)))
                 fam = f;
         }
@@ -771,8 +793,8 @@ gemm_status_t gemm_sparse24_sizes(int64_t M, int64_t K, int32_t a_type, size_t *
         return fail(GEMM_ERR_NULL_POINTER, "output pointer is NULL");
     if (M < 0 || K < 0)
         return fail(GEMM_ERR_INVALID_VALUE, "negative size");
-    if (a_type != GEMM_F16 && a_type != GEMM_BF16 && a_type != GEMM_S8 && !is_fp8(a_type))
-        return fail(GEMM_ERR_UNSUPPORTED, "2:4 compression takes f16, bf16, fp8 or s8");
+    if (a_type != GEMM_F16 && a_type != GEMM_BF16 && !is_int8(a_type) && !is_fp8(a_type))
+        return fail(GEMM_ERR_UNSUPPORTED, "2:4 compression takes f16, bf16, fp8, s8 or u8");
     if (K % 4)
         return fail(GEMM_ERR_UNSUPPORTED, "K must be a multiple of 4");
     *values_bytes = (size_t)M * (size_t)(K / 2) * (size_t)elem_bytes(a_type);
@@ -808,7 +830,7 @@ gemm_status_t gemm_sparse24_compress(int64_t M, int64_t K, int32_t a_type, const
     int host_flag = 0;
     e = hipMemsetAsync(flag, 0, sizeof(int), s);
     if (e == hipSuccess)
-        e = launch_sparse24_compress(eb, eb == 2 ? 0x7FFFu : (a_type == GEMM_S8 ? 0xFFu : 0x7Fu),
+        e = launch_sparse24_compress(eb, eb == 2 ? 0x7FFFu : (is_int8(a_type) ? 0xFFu : 0x7Fu),
                                      M, K, A, values, meta, flag, s);
     if (e == hipSuccess)
         e = hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, s);
@@ -855,7 +877,7 @@ gemm_status_t gemm_sparse24_compress_noalloc(int64_t M, int64_t K, int32_t a_typ
     int host_flag = 0;
     e = launch_zero_ints(flag, 1, s);
     if (e == hipSuccess)
-        e = launch_sparse24_compress(eb, eb == 2 ? 0x7FFFu : (a_type == GEMM_S8 ? 0xFFu : 0x7Fu),
+        e = launch_sparse24_compress(eb, eb == 2 ? 0x7FFFu : (is_int8(a_type) ? 0xFFu : 0x7Fu),
                                      M, K, A, values, meta, flag, s);
     if (e == hipSuccess)
         e = hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, s);

@@ -17,6 +17,9 @@ enum OpKind {
     OPK_F8_E5E4,
     OPK_F8_E5E5,
     OPK_S8,
+    OPK_U8S8, // u8 A x s8 B (int8 MFMA on A - 128, corrected in the epilogue)
+    OPK_S8U8,
+    OPK_U8U8,
     OPK_COUNT
 };
 

@@ -52,15 +52,39 @@ __global__ __launch_bounds__(256) void k_generic(GemmArgs g)
         return; // whole wave idle
     const int64_t am = m0 + (lane & 31), bn = n0 + (lane & 31);
     const bool a_ok = am < g.e.M, b_ok = bn < g.e.N;
+    constexpr bool AU = au_v<OP>(), BU = bu_v<OP>();
+    int rs[1] = {0}, cs[1] = {0}; // unsigned operands: sums of the shifted values
     typename OP::acc_t acc = {};
     for (int64_t k0 = 0; k0 < g.K; k0 += KI) {
         uint32_t a[OP::LANE_BYTES / 4], b[OP::LANE_BYTES / 4];
         const int64_t kb = k0 + (lane >> 5) * LE;
         load_frag_strided<OP::ELEM, LE>(a, g.A, a_ok, am * g.a_rs, g.a_cs, kb, g.K);
         load_frag_strided<OP::ELEM, LE>(b, g.B, b_ok, bn * g.b_cs, g.b_rs, kb, g.K);
+        if constexpr (AU || BU) {
+            // an unsigned value x enters the MFMA as x - 128; bytes past K
+            // stay 0 (they must add nothing), the rows past the edge are
+            // never stored
+#pragma unroll
+            for (int w = 0; w < OP::LANE_BYTES / 4; ++w) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    m |= (kb + 4 * w + q < g.K ? 0x80u : 0u) << (8 * q);
+                if constexpr (AU)
+                    a[w] ^= m;
+                if constexpr (BU)
+                    b[w] ^= m;
+                if constexpr (BU)
+                    rs[0] = sum4_s8(a[w], rs[0]);
+                if constexpr (AU)
+                    cs[0] = sum4_s8(b[w], cs[0]);
+            }
+        }
         acc = OP::mma(a, b, acc);
     }
     typename OP::acc_t grid[1][1] = {{acc}};
+    if constexpr (AU || BU)
+        u8_correct<AU, BU>(grid, rs, cs, g.K, lane);
     epilogue_grid<OP, 1, 1>(g.e, grid, m0, n0, lane);
 }
 
@@ -237,6 +261,9 @@ static dense_launch_fn generic_table(int op)
     case OPK_F8_E5E4: return launch_generic_t<OpF8<1, 0>>;
     case OPK_F8_E5E5: return launch_generic_t<OpF8<1, 1>>;
     case OPK_S8: return launch_generic_t<OpS8>;
+    case OPK_U8S8: return launch_generic_t<OpI8<true, false>>;
+    case OPK_S8U8: return launch_generic_t<OpI8<false, true>>;
+    case OPK_U8U8: return launch_generic_t<OpI8<true, true>>;
     default: return nullptr;
     }
 }
@@ -252,8 +279,19 @@ static dense_launch_fn tiled_table_t(int op)
     case OPK_F8_E5E4: return launch_tiled_t<OpF8<1, 0>, BM, BN, GM, GN, WPC>;
     case OPK_F8_E5E5: return launch_tiled_t<OpF8<1, 1>, BM, BN, GM, GN, WPC>;
     case OPK_S8: return launch_tiled_t<OpS8, BM, BN, GM, GN, WPC>;
-    default: return nullptr;
+    default: break;
     }
+    // unsigned 8-bit operands: on the tiles the plan uses for int8 (the
+    // 128 x 128 tile and the 8-wave 64 x 128-per-wave 256 x 256 one)
+    if constexpr (BM == 128 || GM == 4) {
+        switch (op) {
+        case OPK_U8S8: return launch_tiled_t<OpI8<true, false>, BM, BN, GM, GN, WPC>;
+        case OPK_S8U8: return launch_tiled_t<OpI8<false, true>, BM, BN, GM, GN, WPC>;
+        case OPK_U8U8: return launch_tiled_t<OpI8<true, true>, BM, BN, GM, GN, WPC>;
+        default: break;
+        }
+    }
+    return nullptr;
 }
 
 template <class OP>

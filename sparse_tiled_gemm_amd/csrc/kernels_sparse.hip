@@ -94,6 +94,19 @@ struct SpS8 : SpOpBase<OpS8> {
     }
 };
 
+// 8-bit integers of either signedness (OpI8): the signed SMFMAC on the
+// shifted values x - 128 of an unsigned operand, corrected afterwards (the
+// SMFMAC kernel takes an unsigned B only; an unsigned A runs the generic
+// kernel, where the dropped positions are explicit zeros)
+template <bool AU, bool BU>
+struct SpI8 : SpOpBase<OpI8<AU, BU>> {
+    typedef i16_t acc_t;
+    __device__ static STG_AI acc_t smfmac(const uint32_t *a, const uint32_t *b, int idx, acc_t c)
+    {
+        return SpS8::smfmac(a, b, idx, c);
+    }
+};
+
 // AFMT / BFMT: 0 = E4M3, 1 = E5M2 (the selectors of OpF8)
 template <int AFMT, int BFMT>
 struct SpF8 : SpOpBase<OpF8<AFMT, BFMT>> {
@@ -257,6 +270,8 @@ __global__ __launch_bounds__(256) void k_sparse_generic(SparseArgs a)
     const bool a_ok = am < a.e.M, b_ok = bn < a.e.N;
     const int64_t K = a.K, W = (K + 31) / 32;
     const uint8_t *vals = (const uint8_t *)a.values;
+    constexpr bool AU = au_v<D>(), BU = bu_v<D>();
+    int rs[1] = {0}, cs[1] = {0}; // unsigned operands: sums of the shifted values
     typename D::acc_t acc = {};
     for (int64_t k0 = 0; k0 < K; k0 += KI) {
         const int64_t kb = k0 + (lane >> 5) * LE; // this lane's LE K positions = NG groups
@@ -284,9 +299,31 @@ __global__ __launch_bounds__(256) void k_sparse_generic(SparseArgs a)
             }
         }
         load_frag_strided<EB, LE>(bw, a.B, b_ok, bn * a.b_cs, a.b_rs, kb, K);
+        if constexpr (AU || BU) {
+            // unsigned values x enter the MFMA as x - 128 (the dropped
+            // positions of A are zeros of u8 like any other); bytes past K
+            // stay 0
+#pragma unroll
+            for (int w = 0; w < LE * EB / 4; ++w) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    m |= (kb + 4 * w + q < K ? 0x80u : 0u) << (8 * q);
+                if constexpr (AU)
+                    aw[w] ^= m;
+                if constexpr (BU)
+                    bw[w] ^= m;
+                if constexpr (BU)
+                    rs[0] = sum4_s8(aw[w], rs[0]);
+                if constexpr (AU)
+                    cs[0] = sum4_s8(bw[w], cs[0]);
+            }
+        }
         acc = D::mma(aw, bw, acc);
     }
     typename D::acc_t grid[1][1] = {{acc}};
+    if constexpr (AU || BU)
+        u8_correct<AU, BU>(grid, rs, cs, K, lane);
     epilogue_grid<D, 1, 1>(a.e, grid, m0, n0, lane);
 }
 
@@ -471,6 +508,12 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
 {
     constexpr int EB = SP::ELEM;
     constexpr int BM = 256, BN = 256, BK = 2 * SP::KI; // BK: logical K per tile
+    // unsigned B (SpI8<false, true>): its fragments are shifted to x - 128
+    // after the LDS reads and the rows' sums of A's kept values restore the
+    // exact product; an unsigned A cannot be restored per row here (the
+    // SMFMAC skips the dropped positions), so it never reaches this kernel
+    constexpr bool BU = bu_v<typename SP::Dense>();
+    static_assert(!au_v<typename SP::Dense>(), "unsigned A runs the generic 2:4 kernel");
     constexpr int NSTAGE = 3, MG = 256 / BK;         // LDS stages; tiles per metadata slot
     constexpr int AVB = BK * EB / 2, AMB = BK / 8, BB = BK * EB; // bytes per row per tile
     constexpr int WM = 128, WN = 64, FM = WM / 32, FN = WN / 32, GN = BN / WN;
@@ -557,28 +600,14 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
 
     uint32_t af[2][FM][4], bf[2][FN][8];
     uint2 mw[FM]; // this lane's metadata words of both K steps of a fragment row
-    // fragment reads of K step S of tile t from stage `st` (step 0 also
-    // reads both steps' metadata)
-    auto lread = [&](auto set, const uint8_t *st, int t) STG_AI {
+    // fragment reads of K step S of tile t from stage `st`
+    auto lread = [&](auto set, const uint8_t *st) STG_AI {
         constexpr int S = decltype(set)::value;
-        // row r, tile t of the group: block r / 32, chunk (t % MG) * AMB / 16,
-        // row r % 32 of the chunk, byte (t % MG) * AMB % 16 of the row's 16
-        const int tb = (t % MG) * AMB;
-        const uint8_t *meta = lds + OFF_META + ((t / MG) & 1) * (BM * MROW) + (tb >> 4) * 512 +
-                              (tb & 15);
         const int ca = 2 * S + half; // value chunk: byte S*32 + half*16
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int r = arow + 32 * i;
             *(u4_t *)af[S][i] = *(const u4_t *)(st + r * AVB + ((ca ^ sa) << 4));
-            if constexpr (S == 0) {
-                // two 4-byte reads, which the compiler merges into one: with
-                // an 8-byte read written as such it first waits for every
-                // pending direct copy into LDS
-                const int mo = (r >> 5) * 1024 + (r & 31) * 16;
-                mw[i].x = *(const uint32_t *)(meta + mo + 4 * SP::word_of_step(0, half));
-                mw[i].y = *(const uint32_t *)(meta + mo + 4 * SP::word_of_step(1, half));
-            }
         }
         const int cb = 4 * S + half; // B chunks 4S + half and 4S + half + 2
 #pragma unroll
@@ -589,6 +618,34 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
                 *(const u4_t *)(st + OFF_B + r * BB + (((cb + 2) ^ sb[j]) << 4));
         }
     };
+    // this lane's metadata words of both K steps of tile t, one tile ahead
+    // of their use: the SMFMAC's index operand must be in a register before
+    // the tile's first instruction, and LDS reads complete in order, so a
+    // metadata read issued behind the tile's fragment reads would hold the
+    // first SMFMAC until all of them returned.  The ring slot of tile t + 1
+    // is complete when tile t runs: group g is requested at the first tile
+    // of group g - 1 and waited for at that tile's end, and a group has at
+    // least two tiles, so its first tile's metadata is read at the earliest
+    // during the second tile of group g - 1.  The slot it overwrites held
+    // group g - 2, whose last read came a tile before that group ended.
+    auto mread = [&](int t, uint2 (&dst)[FM]) STG_AI {
+        // row r, tile t of the group: block r / 32, chunk (t % MG) * AMB / 16,
+        // row r % 32 of the chunk, byte (t % MG) * AMB % 16 of the row's 16
+        const int tb = (t % MG) * AMB;
+        const uint8_t *meta = lds + OFF_META + ((t / MG) & 1) * (BM * MROW) + (tb >> 4) * 512 +
+                              (tb & 15);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int r = arow + 32 * i;
+            // two 4-byte reads, which the compiler merges into one: with
+            // an 8-byte read written as such it first waits for every
+            // pending direct copy into LDS
+            const int mo = (r >> 5) * 1024 + (r & 31) * 16;
+            dst[i].x = *(const uint32_t *)(meta + mo + 4 * SP::word_of_step(0, half));
+            dst[i].y = *(const uint32_t *)(meta + mo + 4 * SP::word_of_step(1, half));
+        }
+    };
+    uint2 mwn[FM]; // the next tile's metadata words
 
     typename SP::acc_t acc[FM][FN];
 #pragma unroll
@@ -596,8 +653,21 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             acc[i][j] = typename SP::acc_t{};
+    int usum_a[FM] = {}, usum_b[FN] = {}; // unsigned B: row sums of A's kept values
     auto mma = [&](auto set) STG_AI {
         constexpr int S = decltype(set)::value;
+        if constexpr (BU) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int w = 0; w < 8; ++w)
+                    bf[S][j][w] ^= U8_FLIP;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    usum_a[i] = sum4_s8(af[S][i][w], usum_a[i]);
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int idx = SP::index_of(S == 0 ? mw[i].x : mw[i].y, half);
@@ -608,11 +678,13 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
     };
 
     // one tile: the first step's fragment reads, then the SMFMACs with the
-    // second step's reads spread over the first step's SMFMACs and the
-    // copies of a future tile spread over all of them
+    // second step's reads and the next tile's metadata reads spread over the
+    // first step's SMFMACs and the copies of a future tile spread over all of
+    // them
     constexpr int NM = FM * FN;
-    // DS reads of steps 0 and 1 (the two metadata words of a row merge into one)
-    constexpr int NR0 = 2 * FM + 2 * FN, NR1 = FM + 2 * FN;
+    // DS reads of step 0, and of step 1 plus the next tile's metadata (the
+    // two metadata words of a row merge into one read)
+    constexpr int NR0 = FM + 2 * FN, NR1 = FM + 2 * FN + FM;
     auto schedule = [&]() STG_AI {
         __builtin_amdgcn_sched_group_barrier(0x100, NR0, 0); // step 0 DS reads
         [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
@@ -644,6 +716,7 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
         dma_tile(p, p);
     STG_WAIT_VMCNT((NSTAGE - 2) * NI);
     lds_barrier();
+    mread(0, mw);
 
     int st = 0; // LDS stage of tile t
     for (int t = 0; t < KT; ++t) {
@@ -655,22 +728,26 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
             dma_meta(t + MG);
         STG_COMPILER_FENCE();
         dma_tile(st == 0 ? NSTAGE - 1 : st - 1, t + NSTAGE - 1);
-        lread(I0{}, cur, t);
-        lread(I1{}, cur, t);
+        lread(I0{}, cur);
+        lread(I1{}, cur);
+        mread(t + 1, mwn); // past the last tile: read, never used
         mma(I0{});
         mma(I1{});
         schedule();
         __builtin_amdgcn_sched_barrier(0);
-        // tile t+1 complete (the requests of this tile may be in flight: the
-        // copies of tile t+2, and the metadata group requested at its start)
-        if (meta_now)
-            STG_WAIT_VMCNT((NSTAGE - 2) * NI + 1);
-        else
-            STG_WAIT_VMCNT((NSTAGE - 2) * NI);
+        // tile t+1 and the metadata group requested at this tile's start
+        // complete (only this tile's copies of tile t+2 may be in flight:
+        // the metadata request precedes them and copies complete in order)
+        STG_WAIT_VMCNT((NSTAGE - 2) * NI);
         lds_barrier();
         st = st == NSTAGE - 1 ? 0 : st + 1;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            mw[i] = mwn[i];
     }
     STG_WAIT_VMCNT(0); // drain the requests past the last tile before the LDS is reused
+    if constexpr (BU)
+        u8_correct<false, true>(acc, usum_a, usum_b, K, lane);
     __syncthreads();
 
     epilogue_grid_lds<typename SP::Dense, FM, FN>(a.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
@@ -687,15 +764,21 @@ static hipError_t launch_sparse_op(int family, const SparseArgs &a, hipStream_t 
     }
     constexpr int BM = 256, BN = 256;
     const int tiles_m = (int)((a.e.M + BM - 1) / BM), tiles_n = (int)((a.e.N + BN - 1) / BN);
-    if (family == KF_SPARSE_DMA8) {
-        hipLaunchKernelGGL(k_sparse_dma8<SP>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, s,
-                           a, tiles_m, tiles_n);
-        return hipGetLastError();
-    }
-    if (family == KF_SPARSE_TILED) {
-        hipLaunchKernelGGL((k_sparse_tiled<SP, BM, BN>), dim3((unsigned)(tiles_m * tiles_n)),
-                           dim3(256), 0, s, a, tiles_m, tiles_n);
-        return hipGetLastError();
+    constexpr bool AU = au_v<typename SP::Dense>(), BU = bu_v<typename SP::Dense>();
+    if constexpr (!AU) { // unsigned A: generic only (the plan never asks otherwise)
+        if (family == KF_SPARSE_DMA8) {
+            hipLaunchKernelGGL(k_sparse_dma8<SP>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0,
+                               s, a, tiles_m, tiles_n);
+            return hipGetLastError();
+        }
+        if constexpr (!BU) {
+            if (family == KF_SPARSE_TILED) {
+                hipLaunchKernelGGL((k_sparse_tiled<SP, BM, BN>),
+                                   dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, s, a,
+                                   tiles_m, tiles_n);
+                return hipGetLastError();
+            }
+        }
     }
     return hipErrorInvalidValue;
 }
@@ -706,6 +789,9 @@ hipError_t launch_sparse(int family, int op, const SparseArgs &a, hipStream_t s)
     case OPK_F16: return launch_sparse_op<SpF16>(family, a, s);
     case OPK_BF16: return launch_sparse_op<SpBF16>(family, a, s);
     case OPK_S8: return launch_sparse_op<SpS8>(family, a, s);
+    case OPK_U8S8: return launch_sparse_op<SpI8<true, false>>(family, a, s);
+    case OPK_S8U8: return launch_sparse_op<SpI8<false, true>>(family, a, s);
+    case OPK_U8U8: return launch_sparse_op<SpI8<true, true>>(family, a, s);
     case OPK_F8_E4E4: return launch_sparse_op<SpF8<0, 0>>(family, a, s);
     case OPK_F8_E4E5: return launch_sparse_op<SpF8<0, 1>>(family, a, s);
     case OPK_F8_E5E4: return launch_sparse_op<SpF8<1, 0>>(family, a, s);

@@ -34,6 +34,10 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
     // fall on distinct bank groups, and every offset inside a step is an
     // immediate.
     constexpr bool AMN = a_mn_v<OP>(), BMN = b_mn_v<OP>();
+    // unsigned 8-bit operands (OpI8): staged into LDS as x - 128, corrected
+    // before the epilogue from per-lane operand sums
+    constexpr bool AU = au_v<OP>(), BU = bu_v<OP>();
+    static_assert(!(AU || BU) || !(AMN || BMN), "unsigned operands: K-contiguous layouts");
     static_assert(!(AMN || BMN) || ((OP::BITS == 16 || OP::BITS == 8) && !OP::MX && !OP::W4),
                   "MN-major: 16- and 8-bit types");
     constexpr int EB = AMN || BMN ? OP::BITS / 8 : 2; // bytes per element (MN-major)
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         constexpr int S = decltype(set)::value;
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
-            *(u4_t *)(stage_base + la0 + a_pass(i)) = ga[S][i];
+            *(u4_t *)(stage_base + la0 + a_pass(i)) = AU ? ga[S][i] ^ U8_FLIP : ga[S][i];
         if constexpr (W4) {
             // 32 codes -> 32 16-bit values: row t of the B tile, four chunks
             constexpr bool BF = std::is_same<OP, OpW4<OpBF16>>::value;
@@ -171,7 +175,7 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         } else {
 #pragma unroll
             for (int i = 0; i < B_LD; ++i)
-                *(u4_t *)(stage_base + lb0 + b_pass(i)) = gb[S][i];
+                *(u4_t *)(stage_base + lb0 + b_pass(i)) = BU ? gb[S][i] ^ U8_FLIP : gb[S][i];
         }
     };
 
@@ -288,6 +292,7 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             acc[i][j] = typename OP::acc_t{};
+    int usum_a[FM] = {}, usum_b[FN] = {}; // unsigned operands: see mma
     // fragment set F; for MX also the tile's parity P and step S
     auto mma = [&](auto set, auto pset, auto step) STG_AI {
         constexpr int S = decltype(set)::value;
@@ -306,6 +311,21 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = OP::mma(fa[S][i], fb[S][j], acc[i][j]);
+            // unsigned operands: this lane's sums of the other operand's
+            // shifted values (rows of A when B is unsigned, columns of B when
+            // A is unsigned)
+            if constexpr (BU)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int w = 0; w < FW; ++w)
+                        usum_a[i] = sum4_s8(fa[S][i][w], usum_a[i]);
+            if constexpr (AU)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int w = 0; w < FW; ++w)
+                        usum_b[j] = sum4_s8(fb[S][j][w], usum_b[j]);
         }
     };
 
@@ -416,6 +436,8 @@ __global__ __launch_bounds__(64 * GM * GN, WG_PER_CU) void k_tiled(GemmArgs g, i
         if (t < KT)
             iter(I0{}, t);
 
+    if constexpr (AU || BU)
+        u8_correct<AU, BU>(acc, usum_a, usum_b, g.K, lane);
     __syncthreads(); // every wave is done with the LDS stages
     epilogue_grid_lds<OP, FM, FN>(g.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
                                   (uint32_t *)lds + wave * 32 * (WN + 4));

@@ -27,13 +27,13 @@ GEMM_ERR_HIP = 7
 
 # gemm_dtype_t
 DTYPES = {"f16": 1, "bf16": 2, "e4m3": 3, "e5m2": 4, "s8": 5, "f32": 6, "s32": 7,
-          "e2m3": 8, "e3m2": 9, "e2m1": 10, "u4": 11}
+          "e2m3": 8, "e3m2": 9, "e2m1": 10, "u4": 11, "u8": 12}
 ROW_MAJOR, COL_MAJOR = 0, 1
 ACT_NONE, ACT_RELU = 0, 1
 # gemm_algo_t
 ALGO = {"auto": 0, "tiled": 1, "generic": 2, "skinny": 3, "tiled128": 4, "tiled256": 5}
 
-ELEM_BYTES = {"f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1, "s8": 1, "f32": 4, "s32": 4}
+ELEM_BYTES = {"f16": 2, "bf16": 2, "e4m3": 1, "e5m2": 1, "s8": 1, "u8": 1, "f32": 4, "s32": 4}
 
 
 class GemmError(RuntimeError):
@@ -138,7 +138,7 @@ def make_desc(M, N, K, a_type, b_type, d_type, *, c_type=None, has_c=True, has_b
               alpha=1.0, act="none", a_layout="row", b_layout="col", lda=0, ldb=0, ldc=0,
               ldd=0, sparse_a=False, algo="auto", block_scale=0, saturate=False):
     """Build a gemm_desc_t from readable arguments (type names as in DTYPES)."""
-    integer = a_type == "s8" and d_type == "s32"
+    integer = a_type in ("s8", "u8") and d_type == "s32"
     if c_type is None:
         c_type = "s32" if integer else "f32"
     d = gemm_desc_t()

@@ -14,9 +14,13 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    inc = os.path.dirname(HEADER)
+    for h in sorted(os.listdir(inc)):
+        text = open(os.path.join(inc, h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -60,6 +64,28 @@ def _ok(**kw):
     (dict(a_type="s8", b_type="s8", d_type="f32"), G.GEMM_OK),          # int8 -> float
     (dict(a_type="s8", b_type="s8", d_type="e4m3", alpha=0.5, act="relu"), G.GEMM_OK),
     (dict(a_type="s8", b_type="s8", d_type="bf16", c_type="s32"), G.GEMM_ERR_UNSUPPORTED),
+    # unsigned 8-bit A and / or B (with s8 or u8 only); saturation's K limit
+    # is K * max|a| * max|b| < 2^31
+    (dict(a_type="u8", b_type="s8", d_type="s32"), G.GEMM_OK),
+    (dict(a_type="s8", b_type="u8", d_type="s32"), G.GEMM_OK),
+    (dict(a_type="u8", b_type="u8", d_type="s32"), G.GEMM_OK),
+    (dict(a_type="u8", b_type="u8", d_type="bf16", alpha=0.25, act="relu"), G.GEMM_OK),
+    (dict(a_type="u8", b_type="bf16", d_type="f32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="e4m3", b_type="u8", d_type="f32"), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="u8", b_type="u8", d_type="s32", alpha=2.0), G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="u8", b_type="u8", d_type="s32", saturate=True, K=33024), G.GEMM_OK),
+    (dict(a_type="u8", b_type="u8", d_type="s32", saturate=True, K=33028),
+     G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="u8", b_type="s8", d_type="s32", saturate=True, K=65792), G.GEMM_OK),
+    (dict(a_type="s8", b_type="u8", d_type="s32", saturate=True, K=65796),
+     G.GEMM_ERR_UNSUPPORTED),
+    (dict(a_type="s8", b_type="s8", d_type="s32", saturate=True, K=131068), G.GEMM_OK),
+    (dict(a_type="s8", b_type="s8", d_type="s32", saturate=True, K=131072),
+     G.GEMM_ERR_UNSUPPORTED),
+    (dict(sparse_a=True, a_type="u8", b_type="s8", d_type="s32"), G.GEMM_OK),
+    (dict(sparse_a=True, a_type="s8", b_type="u8", d_type="f32"), G.GEMM_OK),
+    (dict(sparse_a=True, a_type="u8", b_type="u8", d_type="s32"), G.GEMM_OK),
+    (dict(a_type="u8", b_type="u8", block_scale=32), G.GEMM_ERR_UNSUPPORTED),
     (dict(a_type="bf16", b_type="bf16", d_type="e5m2"), G.GEMM_OK),      # fp8 output
     (dict(a_type="e4m3", b_type="e5m2", d_type="e4m3", has_c=False), G.GEMM_OK),
     (dict(d_type="s32"), G.GEMM_ERR_UNSUPPORTED),
@@ -130,7 +156,7 @@ def test_sparse24_sizes():
     assert e.value.status == G.GEMM_ERR_UNSUPPORTED
     # values are elements of A's type; the metadata does not depend on it
     assert G.gemm_sparse24_sizes(4, 8, "bf16") == (4 * 4 * 2, 4 * 4)
-    for t in ("s8", "e4m3", "e5m2"):
+    for t in ("s8", "u8", "e4m3", "e5m2"):
         assert G.gemm_sparse24_sizes(4, 40, t) == (4 * 20, 4 * 2 * 4)
     with pytest.raises(G.GemmError) as e:
         G.gemm_sparse24_sizes(4, 8, "f32")
