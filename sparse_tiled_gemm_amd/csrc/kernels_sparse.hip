@@ -618,16 +618,14 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
                 *(const u4_t *)(st + OFF_B + r * BB + (((cb + 2) ^ sb[j]) << 4));
         }
     };
-    // this lane's metadata words of both K steps of tile t, one tile ahead
-    // of their use: the SMFMAC's index operand must be in a register before
-    // the tile's first instruction, and LDS reads complete in order, so a
-    // metadata read issued behind the tile's fragment reads would hold the
-    // first SMFMAC until all of them returned.  The ring slot of tile t + 1
-    // is complete when tile t runs: group g is requested at the first tile
-    // of group g - 1 and waited for at that tile's end, and a group has at
-    // least two tiles, so its first tile's metadata is read at the earliest
-    // during the second tile of group g - 1.  The slot it overwrites held
-    // group g - 2, whose last read came a tile before that group ended.
+    // this lane's metadata words of both K steps of tile t, read in phase B
+    // of tile t - 1 (the SMFMAC's index operand must be in a register before
+    // the tile's first instruction).  Group g is requested in phase B of the
+    // first tile of group g - 1 and is complete and visible from the next
+    // tile's barrier on; a group has at least two tiles, so its first
+    // tile's metadata is read at the earliest in phase B of the second tile
+    // of group g - 1.  The slot the request overwrites held group g - 2,
+    // whose last read completed before the barrier of the requesting tile.
     auto mread = [&](int t, uint2 (&dst)[FM]) STG_AI {
         // row r, tile t of the group: block r / 32, chunk (t % MG) * AMB / 16,
         // row r % 32 of the chunk, byte (t % MG) * AMB % 16 of the row's 16
@@ -677,70 +675,73 @@ __global__ __launch_bounds__(512, 1) void k_sparse_dma8(SparseArgs a, int tiles_
         }
     };
 
-    // one tile: the first step's fragment reads, then the SMFMACs with the
-    // second step's reads and the next tile's metadata reads spread over the
-    // first step's SMFMACs and the copies of a future tile spread over all of
-    // them
-    constexpr int NM = FM * FN;
-    // DS reads of step 0, and of step 1 plus the next tile's metadata (the
-    // two metadata words of a row merge into one read)
-    constexpr int NR0 = FM + 2 * FN, NR1 = FM + 2 * FN + FM;
-    auto schedule = [&]() STG_AI {
-        __builtin_amdgcn_sched_group_barrier(0x100, NR0, 0); // step 0 DS reads
+    // Each tile runs in two phases around one barrier.  Phase A: step 0's
+    // SMFMACs (their fragments were read during the previous phase B) with
+    // step 1's fragment reads spread among them; then the wait for tile
+    // t+1's copies and the barrier.  Phase B: tile t+1's metadata and step-0
+    // fragments read, tile t's stage refilled with tile t+NSTAGE (every
+    // wave's reads of it completed before the barrier), then step 1's
+    // SMFMACs.  So no SMFMAC waits for an LDS read issued in its own phase,
+    // and the copies of a tile have a tile and a half to land.
+    constexpr int NM = FM * FN, NR = FM + 2 * FN; // SMFMACs and DS reads per step
+    auto schedule_a = [&]() STG_AI {
         [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
             (
                 [&]() STG_AI {
-                    constexpr int nr = Q < NM ? spread(Q, NR1, NM) : 0;
-                    constexpr int nl = spread(Q, NI, 2 * NM);
+                    constexpr int nr = spread(Q, NR, NM);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
                     if constexpr (nr > 0)
                         __builtin_amdgcn_sched_group_barrier(0x100, nr, 0); // DS read
-                    if constexpr (nl > 0)
-                        __builtin_amdgcn_sched_group_barrier(0x020, nl, 0); // VMEM read
                 }(),
                 ...);
-        }(std::make_integer_sequence<int, 2 * NM>{});
+        }(std::make_integer_sequence<int, NM>{});
     };
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
 
-    // prologue: metadata group 0, tiles 0 and 1 requested; wait for group 0
-    // and tile 0 (tile 1's copies may be in flight)
-    // (the compiler fences keep the copies in program order: the waits below
-    // count requests in that order)
+    // prologue: metadata group 0 and tiles 0 .. NSTAGE-1 requested; wait for
+    // group 0 and tile 0, then read tile 0's metadata and step-0 fragments
+    // (the compiler fences keep the copies in program order: the waits
+    // below count requests in that order)
     dma_meta(0);
     STG_COMPILER_FENCE();
 #pragma unroll
-    for (int p = 0; p < NSTAGE - 1; ++p)
+    for (int p = 0; p < NSTAGE; ++p)
         dma_tile(p, p);
-    STG_WAIT_VMCNT((NSTAGE - 2) * NI);
+    STG_WAIT_VMCNT((NSTAGE - 1) * NI);
     lds_barrier();
     mread(0, mw);
+    lread(I0{}, lds);
 
     int st = 0; // LDS stage of tile t
     for (int t = 0; t < KT; ++t) {
-        const uint8_t *cur = lds + st * STAGE;
-        // at the first tile of a group: the next group's metadata, into the
-        // slot whose tiles ended with the barrier before this tile
-        const bool meta_now = (t % MG) == 0;
-        if (meta_now)
+        const int sn = st == NSTAGE - 1 ? 0 : st + 1;
+        // phase A
+        lread(I1{}, lds + st * STAGE);
+        mma(I0{});
+        schedule_a();
+        __builtin_amdgcn_sched_barrier(0);
+        // tile t+1 complete: only the requests of the previous phase B (its
+        // metadata request, issued first, included) are counted as in flight
+        STG_WAIT_VMCNT(NI);
+        lds_barrier();
+        // phase B.  The reads come before the copies: an LDS read issued
+        // after a direct copy into the metadata ring makes the compiler wait
+        // for every copy in flight (vmcnt(0)), which would serialise the
+        // copy pipeline.  Past the last tile the reads are never used.
+        mread(t + 1, mwn);
+        lread(I0{}, lds + sn * STAGE);
+        STG_COMPILER_FENCE();
+        // at the first tile of a group: the group after next's metadata,
+        // into the slot whose last reads completed before this barrier
+        if ((t % MG) == 0)
             dma_meta(t + MG);
         STG_COMPILER_FENCE();
-        dma_tile(st == 0 ? NSTAGE - 1 : st - 1, t + NSTAGE - 1);
-        lread(I0{}, cur);
-        lread(I1{}, cur);
-        mread(t + 1, mwn); // past the last tile: read, never used
-        mma(I0{});
+        dma_tile(st, t + NSTAGE);
         mma(I1{});
-        schedule();
         __builtin_amdgcn_sched_barrier(0);
-        // tile t+1 and the metadata group requested at this tile's start
-        // complete (only this tile's copies of tile t+2 may be in flight:
-        // the metadata request precedes them and copies complete in order)
-        STG_WAIT_VMCNT((NSTAGE - 2) * NI);
-        lds_barrier();
-        st = st == NSTAGE - 1 ? 0 : st + 1;
+        st = sn;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             mw[i] = mwn[i];
