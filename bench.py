@@ -42,6 +42,7 @@ def _workloads():
         "bf16_8192": (lambda: inputs.dense_bf16(8192, 8192, 8192), "bf16"),
         "bf16_skinny_16x8192x8192": (lambda: inputs.dense_bf16(16, 8192, 8192), "bf16"),
         "bf16_8192_acol_brow": (lambda: _mn_major(inputs.dense_bf16(8192, 8192, 8192)), "bf16"),
+        "bf16_8192_c_bf16": (lambda: _c16(inputs.dense_bf16(8192, 8192, 8192), "bf16"), "bf16"),
         "fp8_8192_acol_brow": (lambda: _mn_major(inputs.dense_fp8(8192, 8192, 8192)), "fp8"),
         "s8_8192_acol_brow": (lambda: _mn_major(inputs.dense_s8(8192, 8192, 8192)), "s8"),
         "s8_8192": (lambda: inputs.dense_s8(8192, 8192, 8192), "s8"),
@@ -66,6 +67,15 @@ def _mn_major(p):
     p["A"] = np.ascontiguousarray(p["A"].T)
     p["B"] = np.ascontiguousarray(p["B"].T)
     p["a_col"], p["b_col"] = True, False
+    return p
+
+
+def _c16(p, c_type):
+    """The same problem with C given as fp16 or bf16 (its fp32 values
+    rounded to nearest even)."""
+    from sparse_tiled_gemm_amd import inputs
+    p["C"] = (inputs.to_bf16 if c_type == "bf16" else inputs.to_f16)(p["C"])
+    p["c_type"] = c_type
     return p
 
 
@@ -94,7 +104,7 @@ def algorithmic_bytes(p, sparse=False):
     else:
         a = M * K * eb[p["a_type"]]
     b = N * K * eb[p["b_type"]]
-    c = M * N * 4 if p["C"] is not None else 0
+    c = M * N * (2 if p.get("c_type") in ("f16", "bf16") else 4) if p["C"] is not None else 0
     bias = N * 4 if p["bias"] is not None else 0
     d = M * N * eb[p["d_type"]]
     return a + b + c + bias + d
@@ -109,8 +119,8 @@ def run_workload(name, steps, warmup, rotate_b=1):
     M, N, K = p["M"], p["N"], p["K"]
     sparse = p.get("A_logical") is not None
     mx, w4 = bool(p.get("mx")), bool(p.get("w4"))
-    desc = G.make_desc(M, N, K, p["a_type"], p["b_type"], p["d_type"], has_c=p["C"] is not None,
-                       has_bias=p["bias"] is not None, alpha=p["alpha"],
+    desc = G.make_desc(M, N, K, p["a_type"], p["b_type"], p["d_type"], c_type=p.get("c_type"),
+                       has_c=p["C"] is not None, has_bias=p["bias"] is not None, alpha=p["alpha"],
                        act="relu" if p["relu"] else "none", sparse_a=sparse,
                        block_scale=32 if mx else (p["gs"] if w4 else 0),
                        a_layout="col" if p.get("a_col") else "row",

@@ -739,6 +739,22 @@ __device__ STG_AI inline void epi_store4(__amdgpu_buffer_rsrc_t rd, int voff, in
 // acc + C, four elements: fp32 addition, or int32 addition modulo 2^32
 // (saturating to the int32 range when `sat`)
 __device__ STG_AI inline f4_t add_c(f4_t v, f4_t c) { return v + c; }
+// Four C values as fp32: c_kind 0 = fp32 in all four words; 1 = fp16 and
+// 2 = bf16, packed two per word in words 0 and 1 (element q in the low half
+// of word q / 2 for even q); both widen exactly.
+__device__ STG_AI inline f4_t widen_c(u4_t c, int c_kind)
+{
+    if (c_kind == 0)
+        return __builtin_bit_cast(f4_t, c);
+    f4_t r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t h = (c[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+        r[q] = c_kind == 1 ? (float)__builtin_bit_cast(_Float16, (uint16_t)h)
+                           : __builtin_bit_cast(float, h << 16);
+    }
+    return r;
+}
 __device__ STG_AI inline i4_t add_c(i4_t v, i4_t c, int sat)
 {
     if (sat)
@@ -790,15 +806,18 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
     // the host enables e.vec only when 257 rows of C and of D span less
     // than 2^31 bytes, so every offset below fits in 32 bits (the resources
     // are empty when unused)
+    // C elements: 4 bytes (fp32, int32) or 2 (fp16, bf16: a float output
+    // only), read 4 per lane as one 16- or 8-byte load and widened exactly
+    const int CB = e.c_kind == 0 ? 4 : 2;
     const int ldd_b = (int)(e.ldd * DB);
-    const int ldc_b = has_c ? (int)(e.ldc * 4) : 0;
+    const int ldc_b = has_c ? (int)(e.ldc * CB) : 0;
     const __amdgpu_buffer_rsrc_t rd =
         epi_rsrc((uint8_t *)e.D + m0 * e.ldd * DB, fast ? (e.M - m0) * e.ldd * DB : 0);
     const __amdgpu_buffer_rsrc_t rc =
-        epi_rsrc(has_c ? (const uint8_t *)e.C + m0 * e.ldc * 4 : (const uint8_t *)e.D,
-                 fast && has_c ? (e.M - m0) * e.ldc * 4 : 0);
+        epi_rsrc(has_c ? (const uint8_t *)e.C + m0 * e.ldc * CB : (const uint8_t *)e.D,
+                 fast && has_c ? (e.M - m0) * e.ldc * CB : 0);
     const int vd = rl * ldd_b + (int)(col * DB);
-    const int vc = rl * ldc_b + (int)(col * 4);
+    const int vc = rl * ldc_b + (int)(col * CB);
     f4_t bv{};
     if constexpr (!IOUT) {
         if (fast && e.bias)
@@ -815,10 +834,19 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
         u4_t cv[NP];
         if (fast && has_c) {
 #pragma unroll
-            for (int p = 0; p < NP; ++p)
-                cv[p] = __builtin_bit_cast(
-                    u4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, vc, (32 * i + p * RPP) * ldc_b,
-                                                               EPI_CPOL));
+            for (int p = 0; p < NP; ++p) {
+                if (IOUT || e.c_kind == 0) {
+                    cv[p] = __builtin_bit_cast(
+                        u4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                  rc, vc, (32 * i + p * RPP) * ldc_b, EPI_CPOL));
+                } else {
+                    typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+                    const u2_t h = __builtin_bit_cast(
+                        u2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                  rc, vc, (32 * i + p * RPP) * ldc_b, EPI_CPOL));
+                    cv[p] = u4_t{h.x, h.y, 0u, 0u};
+                }
+            }
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j)
@@ -845,7 +873,7 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, w), rd, vd, soff,
                                                            EPI_CPOL);
                 } else {
-                    const f4_t f = has_c ? add_c(v, __builtin_bit_cast(f4_t, cv[p])) : v;
+                    const f4_t f = has_c ? add_c(v, widen_c(cv[p], e.c_kind)) : v;
                     epi_store4<KIND>(rd, vd, soff, epi_affine(e, f, bv));
                 }
             }

@@ -714,9 +714,11 @@ static EpiArgs make_epi(const gemm_desc_t &d, const void *C, const void *bias, v
     // the vector epilogue addresses a block's C and D rows with 32-bit
     // offsets: 257 rows of each must span less than 2^31 bytes
     const int64_t lim = 0x7fffffff / 257;
-    // a 16-bit C (float outputs) is read element by element
+    // C is read 4 elements per lane: 16 bytes of fp32 / int32 or 8 of
+    // fp16 / bf16 (float outputs only)
     e.c_kind = !d.has_c ? 0 : (d.c_type == GEMM_F16 ? 1 : (d.c_type == GEMM_BF16 ? 2 : 0));
-    e.vec = (!d.has_c || (e.c_kind == 0 && aligned(C, 16) && d.ldc % 4 == 0 && d.ldc * 4 < lim)) &&
+    const int cb = e.c_kind == 0 ? 4 : 2;
+    e.vec = (!d.has_c || (aligned(C, 4 * cb) && d.ldc % 4 == 0 && d.ldc * cb < lim)) &&
             (!d.has_bias || aligned(bias, 16)) && aligned(D, 4 * db) && d.ldd % 4 == 0 &&
             d.ldd * db < lim;
     return e;

@@ -263,3 +263,42 @@ def test_16bit_c_validation():
     with pytest.raises(G.GemmError):  # block-scaled GEMM keeps an fp32 C
         G.gemm_plan(G.make_desc(256, 256, 512, "e4m3", "e4m3", "bf16", c_type="bf16",
                                 block_scale=32))
+
+
+@pytest.mark.parametrize("c_type", ["f16", "bf16"])
+@pytest.mark.parametrize("ldc_pad,c_shift", [(0, 0), (4, 0), (2, 0), (0, 1)],
+                         ids=["packed", "ldc+4", "ldc+2", "misaligned"])
+def test_16bit_c_bit_exact(orc, c_type, ldc_pad, c_shift):
+    """A 16-bit C through the 256 x 256 kernel's epilogue, bit for bit: D =
+    the fp32 epilogue of (the kernel's own fp32 accumulator + C widened).
+    8-byte-aligned C rows take the vector path (4 C elements per lane in one
+    load); an odd pitch or a C not 8-byte aligned takes the element path."""
+    M, N, K = 520, 392, 256
+    p = _dense("bf16", M, N, K)
+    conv = inputs.to_f16 if c_type == "f16" else inputs.to_bf16
+    ldc = N + ldc_pad
+    C = conv(np.random.default_rng(31).uniform(-8, 8, size=(M, ldc)))
+    bias = _bias(N)
+    tA, tB = to_dev(p["A"]), to_dev(p["B"])
+    # the fp32 accumulator, no C
+    dT = G.make_desc(M, N, K, "bf16", "bf16", "f32", has_c=False, algo="tiled256")
+    T = torch.empty(M * N * 4, dtype=torch.uint8, device="cuda")
+    G.gemm_run(G.gemm_plan(dT), tA, tB, None, None, T)
+    buf = torch.zeros(M * ldc * 2 + 16, dtype=torch.uint8, device="cuda")
+    off = 2 * c_shift
+    buf[off:off + M * ldc * 2] = to_dev(C.reshape(-1).view(np.uint8))
+    for d_type in ["bf16", "f32"]:
+        desc = G.make_desc(M, N, K, "bf16", "bf16", d_type, c_type=c_type, has_c=True, ldc=ldc,
+                           has_bias=True, alpha=0.75, act="relu", algo="tiled256")
+        plan = G.gemm_plan(desc)
+        D = torch.empty(M * N * G.ELEM_BYTES[d_type], dtype=torch.uint8, device="cuda")
+        G.gemm_run(plan, tA, tB, buf[off:], to_dev(bias), D)
+        torch.cuda.synchronize()
+        Tc = (T.cpu().numpy().view(np.float32).reshape(M, N) +
+              orc.decode(c_type, C[:, :N]).astype(np.float32))
+        ref = orc.epilogue_f32(Tc, 0.75, bias, True, d_type)
+        out = D.cpu().numpy().view(ref.dtype).reshape(M, N)
+        mism = int((out.view(np.uint32 if d_type == "f32" else np.uint16) !=
+                    ref.view(np.uint32 if d_type == "f32" else np.uint16)).sum())
+        say("c16 exact", plan.name, c_type, d_type, ldc_pad, c_shift, "mismatches", mism)
+        assert mism == 0
