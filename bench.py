@@ -242,8 +242,13 @@ def ceiling(steps, warmup):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
     res = {}
+    # kind k (32x32 form) and k + 3 (16x16 form) do the same work per
+    # iteration: 64 instructions of `flop` each per wave
     for kind, name, flop, peak in [(0, "bf16", 32768, PEAK["bf16"]), (1, "fp8", 131072, PEAK["fp8"]),
-                                   (2, "s8", 65536, PEAK["s8"])]:
+                                   (2, "s8", 65536, PEAK["s8"]),
+                                   (3, "bf16_16x16", 32768, PEAK["bf16"]),
+                                   (4, "fp8_16x16", 131072, PEAK["fp8"]),
+                                   (5, "s8_16x16", 65536, PEAK["s8"])]:
         per_iter = cus * 8 * 64 * flop
         iters = max(1, int(0.6 * peak * 1e12 * 1e-3 / per_iter))
         for _ in range(warmup):
@@ -257,7 +262,7 @@ def ceiling(steps, warmup):
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / steps
         rate = per_iter * iters / (ms * 1e-3) / 1e12
-        res[name] = {"TFLOPS" if kind != 2 else "TOPS": rate, "frac_peak": rate / peak,
+        res[name] = {"TOPS" if name.startswith("s8") else "TFLOPS": rate, "frac_peak": rate / peak,
                      "ms_per_launch": ms, "iters": iters, "workgroups": cus}
     return res
 
@@ -276,7 +281,8 @@ def main():
                     help="run only a plain 1 GiB device copy (x3), the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--ceiling", action="store_true",
-                    help="run only the MFMA-only ceiling diagnostic (bf16, fp8, int8) and print "
+                    help="run only the MFMA-only ceiling diagnostic (bf16, fp8, int8; 32x32 and "
+                         "16x16 forms) and print "
                          "its rates as one JSON line")
     ap.add_argument("--force-kernel", default=None,
                     help="kernel family to force (tuning: sets STGEMM_FORCE_KERNEL)")

@@ -1049,8 +1049,8 @@ gemm_status_t gemm_diag_mfma_loop(int32_t kind, int32_t blocks, int64_t iters, f
 {
     if (!out)
         return fail(GEMM_ERR_NULL_POINTER, "out is NULL");
-    if (kind < 0 || kind > 2 || blocks < 1 || blocks > (1 << 20) || iters < 0)
-        return fail(GEMM_ERR_INVALID_VALUE, "kind 0..2, blocks 1..2^20, iters >= 0");
+    if (kind < 0 || kind > 5 || blocks < 1 || blocks > (1 << 20) || iters < 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "kind 0..5, blocks 1..2^20, iters >= 0");
     int dev = 0;
     gemm_status_t st = check_device(&dev, nullptr);
     if (st != GEMM_OK)

@@ -70,8 +70,9 @@ hipError_t launch_sparse24_compress(int elem_bytes, uint32_t zero_mask, int64_t 
 // scratch array on device `dev` (current), SPARSE24_SCRATCH_INTS ints, of
 // which the flag uses element 0; and a kernel that zeroes n ints.
 constexpr int SPARSE24_SCRATCH_INTS = 64;
-// Diagnostic MFMA-only loop (kernels_diag.hip): kind 0 bf16, 1 fp8, 2 int8;
-// `blocks` workgroups of 512 threads, 64 MFMAs per wave per iteration.
+// Diagnostic MFMA-only loop (kernels_diag.hip): kind 0 bf16, 1 fp8, 2 int8
+// (32x32 forms), 3..5 the same types' 16x16 forms; `blocks` workgroups of
+// 512 threads.
 hipError_t launch_mfma_loop(int kind, int blocks, int64_t iters, float *out, hipStream_t s);
 hipError_t sparse24_scratch(int dev, int **out);
 hipError_t launch_zero_ints(int *p, int n, hipStream_t s);

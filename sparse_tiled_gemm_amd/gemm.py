@@ -241,5 +241,6 @@ def gemm_w4a16_run(plan, A, B, scales, zeros, C, bias, D, stream=None):
 
 def gemm_diag_mfma_loop(kind, blocks, iters, out, stream=None):
     """Diagnostic MFMA-only loop (include/gemm_diag.h); kind 0 bf16, 1 fp8,
-    2 int8; out: a device float tensor of blocks * 512 elements."""
+    2 int8 (32x32 forms), 3..5 the same types' 16x16 forms; out: a device
+    float tensor of blocks * 512 elements."""
     _check(load().gemm_diag_mfma_loop(kind, blocks, iters, _ptr(out), _stream(stream)))

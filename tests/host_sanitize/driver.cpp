@@ -128,7 +128,7 @@ hipError_t sparse24_scratch(int, int **out)
 }
 hipError_t launch_mfma_loop(int kind, int blocks, int64_t iters, float *out, hipStream_t)
 {
-    EXPECT(kind >= 0 && kind <= 2 && blocks >= 1 && iters >= 0 && out);
+    EXPECT(kind >= 0 && kind <= 5 && blocks >= 1 && iters >= 0 && out);
     ++g_launches;
     return hipSuccess;
 }
@@ -248,7 +248,8 @@ int main(int argc, char **argv)
     EXPECT(gemm_sparse24_compress_noalloc(64, 64, GEMM_F16, fake(1), fake(2),
                                           (uint32_t *)fake(3), nullptr) == GEMM_OK);
     EXPECT(gemm_diag_mfma_loop(0, 256, 100, (float *)fake(1), nullptr) == GEMM_OK);
-    EXPECT(gemm_diag_mfma_loop(3, 256, 100, (float *)fake(1), nullptr) == GEMM_ERR_INVALID_VALUE);
+    EXPECT(gemm_diag_mfma_loop(5, 256, 100, (float *)fake(1), nullptr) == GEMM_OK);
+    EXPECT(gemm_diag_mfma_loop(6, 256, 100, (float *)fake(1), nullptr) == GEMM_ERR_INVALID_VALUE);
     EXPECT(gemm_diag_mfma_loop(1, 0, 100, (float *)fake(1), nullptr) == GEMM_ERR_INVALID_VALUE);
     EXPECT(gemm_diag_mfma_loop(2, 8, 1, nullptr, nullptr) == GEMM_ERR_NULL_POINTER);
     for (int s = -2; s < 10; ++s)
