@@ -273,7 +273,15 @@ gemm_status_t gemm_sparse24_run(const gemm_plan_t *plan, const void *values, con
  *   A scale of 0xFF (NaN) gives an unspecified result.
  * Device pointers; the fast kernel (pairs of one width: both 8-bit or both
  * E2M1, K % 512 == 0, rows of whole 16 bytes) needs A, B and the scales
- * 16-byte aligned, else the generic kernel runs. */
+ * 16-byte aligned, else the generic kernel runs.  With a 6-bit operand
+ * (partner 6- or 8-bit, K % 512 == 0, 6-bit rows of whole 4 bytes, 8-bit
+ * rows of whole 16) the fast path first rewrites each 6-bit operand into a
+ * temporary of M*K (A) or N*K (B) bytes, taken on `stream` from a memory
+ * pool the library keeps per device (its blocks stay reserved for later
+ * calls until the process ends) and released on `stream` after the
+ * product; it needs 6-bit operands 4-byte aligned, 8-bit ones and the
+ * scales 16-byte aligned, else the generic kernel runs.  A failure to get
+ * the temporary is returned as GEMM_ERR_HIP. */
 gemm_status_t gemm_mx_run(const gemm_plan_t *plan, const void *A, const uint8_t *scale_a,
                           const void *B, const uint8_t *scale_b, const void *C, const void *bias,
                           void *D, gemm_stream_t stream);

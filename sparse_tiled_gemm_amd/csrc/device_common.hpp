@@ -198,8 +198,9 @@ __device__ STG_AI inline void u8_correct(i16_t (&acc)[FM][FN], const int (&rs)[F
 // MX block-scaled product of OCP MX element formats (AF / BF: 0 = E4M3, 1 =
 // E5M2, 2 = E2M3, 3 = E3M2, 4 = E2M1, the selectors of the gfx950
 // v_mfma_scale_f32_32x32x64_f8f6f4) with one E8M0 scale per 32 K of every A
-// row and B column.  The tiled kernel takes pairs of one width: both 8-bit or
-// both 4-bit (BITS).  Lane layouts (measured with single-instruction probes):
+// row and B column.  The tiled kernel takes pairs of one width: both 8-bit,
+// both 4-bit, or both 6-bit in the padded layout below (BITS is the stored
+// width).  Lane layouts (measured with single-instruction probes):
 //  - 8-bit operands: lane l (h = l / 32) gives bytes 0..15 = K 16h .. 16h+15
 //    and bytes 16..31 = K 32+16h .. 32+16h+15 of row / column l % 32 (so
 //    K block b of the instruction is bytes 16b .. 16b+15 of both lane
@@ -209,10 +210,18 @@ __device__ STG_AI inline void u8_correct(i16_t (&acc)[FM][FN], const int (&rs)[F
 //    bit 0 up (4-bit: the even element in the low nibble);
 //  - the scale VGPR of lane half b holds (in the byte the instruction's
 //    op_sel picks) the scale of the lane's row / column over K block b.
-template <int AF, int BF>
+// PAD6: both operands 6-bit, stored padded to the 8-bit geometry - each
+// 32-K block's 24 packed bytes followed by 8 unused bytes, and the 64-byte
+// K groups in the 8-bit chunk order (chunk h: bytes 0..15 of block h, chunk
+// 2 + h: bytes 16..23 of block h and the padding), so that after the 8-bit
+// chunk swap a lane half reads its block's 24 bytes as words 0..5 (the
+// instruction reads six registers of a 6-bit operand).
+template <int AF, int BF, bool PAD6 = false>
 struct OpMX {
-    static constexpr int BITS = AF <= 1 ? 8 : (AF == 4 ? 4 : 6);
-    static_assert((BF <= 1 ? 8 : (BF == 4 ? 4 : 6)) == BITS, "one width for A and B");
+    static constexpr int FBITS = AF <= 1 ? 8 : (AF == 4 ? 4 : 6);
+    static_assert((BF <= 1 ? 8 : (BF == 4 ? 4 : 6)) == FBITS, "one width for A and B");
+    static_assert(!PAD6 || FBITS == 6, "padding: 6-bit formats");
+    static constexpr int BITS = PAD6 ? 8 : FBITS; // storage bits per K
     static constexpr int ELEM = 1; // (unused: MX addressing is by BITS)
     static constexpr int LANE_BYTES = 32 * BITS / 8; // one 32-K block per lane
     static constexpr int KB = 2 * LANE_BYTES;        // row bytes per instruction (64 K)

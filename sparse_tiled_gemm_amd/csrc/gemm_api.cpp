@@ -214,6 +214,7 @@ const char *family_name(int f)
     case KF_W4_GENERIC: return "w4_generic";
     case KF_W4_TILED: return "w4_tiled";
     case KF_W4_SKINNY: return "w4_skinny";
+    case KF_MX_TILED6: return "mx_tiled6";
     default: return "?";
     }
 }
@@ -497,11 +498,19 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
         const bool fast = ab == bb && ab != 6 && d.K % 512 == 0 && rowa % 16 == 0 &&
                           rowb % 16 == 0 && rowa * 256 < lim && rowb * 256 < lim &&
                           (d.K / 32) * 256 < lim;
+        // 6-bit operands (with a 6- or 8-bit partner): expanded into K-byte
+        // rows of 8-bit codes (packed 6-bit rows read 4 bytes at a time),
+        // then the 8-bit kernel
+        const bool fast6 = (ab == 6 || bb == 6) && ab != 4 && bb != 4 && d.K % 512 == 0 &&
+                           rowa % (ab == 6 ? 4 : 16) == 0 && rowb % (bb == 6 ? 4 : 16) == 0 &&
+                           d.K * 256 < lim && rowa * 256 < lim && rowb * 256 < lim &&
+                           (d.K / 32) * 256 < lim;
+        const int tiled_fam = fast ? KF_MX_TILED : (fast6 ? KF_MX_TILED6 : -1);
         int fam = -1;
         switch (d.algo) {
-        case GEMM_ALGO_AUTO: fam = fast ? KF_MX_TILED : KF_MX_GENERIC; break;
+        case GEMM_ALGO_AUTO: fam = tiled_fam >= 0 ? tiled_fam : KF_MX_GENERIC; break;
         case GEMM_ALGO_TILED:
-        case GEMM_ALGO_TILED_256: fam = fast ? KF_MX_TILED : -1; break;
+        case GEMM_ALGO_TILED_256: fam = tiled_fam; break;
         case GEMM_ALGO_GENERIC: fam = KF_MX_GENERIC; break;
         default: fam = -1;
         }
@@ -514,6 +523,8 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
                 fam = KF_MX_GENERIC;
             if (strcmp(force, family_name(KF_MX_TILED)) == 0 && fast)
                 fam = KF_MX_TILED;
+            if (strcmp(force, family_name(KF_MX_TILED6)) == 0 && fast6)
+                fam = KF_MX_TILED6;
         }
         p->op = mx_sel(d.a_type) * 8 + mx_sel(d.b_type);
         p->family = fam;
@@ -988,6 +999,13 @@ gemm_status_t gemm_mx_run(const gemm_plan_t *plan, const void *A, const uint8_t 
     int fam = plan->family;
     if (fam == KF_MX_TILED &&
         (!aligned(A, 16) || !aligned(B, 16) || !aligned(scale_a, 16) || !aligned(scale_b, 16)))
+        fam = plan->fallback;
+    // the expansion reads a 6-bit operand 4 bytes at a time; an 8-bit one
+    // goes to the tiled kernel as it is
+    if (fam == KF_MX_TILED6 &&
+        (!aligned(A, mx_bits(d.a_type) == 6 ? 4 : 16) ||
+         !aligned(B, mx_bits(d.b_type) == 6 ? 4 : 16) || !aligned(scale_a, 16) ||
+         !aligned(scale_b, 16)))
         fam = plan->fallback;
     hipError_t e = launch_mx(fam, plan->op / 8, plan->op % 8, g, (hipStream_t)stream);
     if (e != hipSuccess)

@@ -39,6 +39,7 @@ enum KernelFamily {
     KF_W4_GENERIC,   // W4A16, any shape
     KF_W4_TILED,     // W4A16, 256 x 256 4-wave tile, B dequantised into LDS
     KF_W4_SKINNY,    // W4A16, M <= 16, B streamed and dequantised in registers
+    KF_MX_TILED6,    // MX with 6-bit operands: expanded to 8-bit codes, then KF_MX_TILED's kernel
     KF_COUNT
 };
 
@@ -53,6 +54,8 @@ hipError_t launch_dense_mn(int family, int op, int layout, const GemmArgs &g, hi
 // (0 E4M3, 1 E5M2, 2 E2M3, 3 E3M2, 4 E2M1); g.sa / g.sb hold the scales.
 hipError_t launch_mx(int family, int afmt, int bfmt, const GemmArgs &g, hipStream_t s);
 hipError_t launch_mx_tiled(int afmt, int bfmt, const GemmArgs &g, hipStream_t s);
+// both operands 6-bit, in the padded 8-bit geometry of OpMX<.., .., true>
+hipError_t launch_mx_tiled_pad6(int afmt, int bfmt, const GemmArgs &g, hipStream_t s);
 // W4A16: op is OPK_F16 or OPK_BF16 (the activations' type); g.ws / g.wz /
 // g.wgs hold the weight groups' scales and zero points.
 hipError_t launch_w4(int family, int op, const GemmArgs &g, hipStream_t s);

@@ -367,6 +367,18 @@ hipError_t launch_mx_tiled(int afmt, int bfmt, const GemmArgs &g, hipStream_t s)
     }
 }
 
+// Both operands 6-bit (E2M3 / E3M2), stored in OpMX's padded layout.
+hipError_t launch_mx_tiled_pad6(int afmt, int bfmt, const GemmArgs &g, hipStream_t s)
+{
+    switch (afmt * 8 + bfmt) {
+    case 2 * 8 + 2: return launch_mx_tiled_t<OpMX<2, 2, true>>(g, s);
+    case 2 * 8 + 3: return launch_mx_tiled_t<OpMX<2, 3, true>>(g, s);
+    case 3 * 8 + 2: return launch_mx_tiled_t<OpMX<3, 2, true>>(g, s);
+    case 3 * 8 + 3: return launch_mx_tiled_t<OpMX<3, 3, true>>(g, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_dense(int family, int op, int layout, const GemmArgs &g, hipStream_t s)
 {
     dense_launch_fn fn = nullptr;

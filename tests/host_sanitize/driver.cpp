@@ -88,7 +88,7 @@ hipError_t launch_dense(int family, int op, int layout, const GemmArgs &g, hipSt
 hipError_t launch_dense_mn(int, int, int, const GemmArgs &, hipStream_t) { return hipSuccess; }
 hipError_t launch_mx(int family, int afmt, int bfmt, const GemmArgs &g, hipStream_t)
 {
-    EXPECT(family == KF_MX_GENERIC || family == KF_MX_TILED);
+    EXPECT(family == KF_MX_GENERIC || family == KF_MX_TILED || family == KF_MX_TILED6);
     EXPECT(afmt >= 0 && afmt < 5 && bfmt >= 0 && bfmt < 5 && g.K % 32 == 0);
     check_epi(g.e);
     ++g_launches;

@@ -198,7 +198,7 @@ def test_full_sparse24_types_8192(orc, t):
                                          ("mxfp6", "e2m3", 10)])
 def test_full_mx_8192(orc, name, a, seed):
     """MX block-scaled GEMM at 8192^3 -> bf16 through the plan bench.py times
-    (the tiled kernel for MXFP8 and MXFP4, the generic one for MXFP6):
+    (the tiled kernel; for MXFP6 after the expansion to 8-bit codes):
     sampled entries against the oracle, and column sums over every output."""
     say("workload", name, "8192^3 -> bf16")
     M = N = K = 8192
@@ -211,7 +211,7 @@ def test_full_mx_8192(orc, name, a, seed):
     torch.cuda.synchronize()
     D = D.cpu().numpy().view(np.uint16).reshape(M, N)
     say("  ran", plan.name)
-    assert plan.name.startswith("mx_generic" if a == "e2m3" else "mx_tiled")
+    assert plan.name.startswith("mx_tiled6" if a == "e2m3" else "mx_tiled")
     rows, cols = _samples(M, N, seed)
     Dr, Y, S = orc.mx_gemm_entries(p["A"], p["SA"], p["B"], p["SB"], None, None, M, N, K, a, a,
                                    "bf16", rows, cols)

@@ -1,7 +1,8 @@
 """GPU parity of the MX block-scaled path ("NVIDIA MMA", section "Blackwell:
 FP4/FP6 and block-scaled MMA"): every pair of element formats through the
-generic kernel, the tiled kernel for pairs of one width, ragged shapes,
-padded rows, the run-time fallback, and the fused epilogue bit for bit -
+generic kernel, the tiled kernel for pairs of one width, the 6-bit pairs
+through the expansion to 8-bit codes and the tiled kernel, ragged shapes,
+padded rows, the run-time fallbacks, and the fused epilogue bit for bit -
 all against the oracle's block-scaled GEMM on the same packed bytes."""
 import numpy as np
 import pytest
@@ -17,6 +18,9 @@ pytestmark = pytest.mark.gpu
 FMTS = ["e4m3", "e5m2", "e2m3", "e3m2", "e2m1"]
 TILED_PAIRS = [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2"),
                ("e2m1", "e2m1")]
+# pairs with a 6-bit operand and a 6- or 8-bit partner
+TILED6_PAIRS = [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2"), ("e3m2", "e2m3"),
+                ("e2m3", "e4m3"), ("e5m2", "e3m2")]
 
 
 def _problem(a, b, M, N, K, seed=40):
@@ -83,6 +87,46 @@ def test_mx_tiled(orc, pair):
         assert r.ok, r
 
 
+@pytest.mark.parametrize("pair", TILED6_PAIRS, ids=["x".join(q) for q in TILED6_PAIRS])
+def test_mx_tiled6(orc, pair):
+    """Every 6-bit code (subnormals, both zeros, the largest) reaches the
+    product: uniform codes rather than quantised normals."""
+    for (M, N, K) in [(600, 520, 512), (130, 300, 1536), (17, 700, 512)]:
+        p = _problem(pair[0], pair[1], M, N, K, seed=45)
+        rng = np.random.default_rng(M + N)
+        for side, rows in (("A", M), ("B", N)):
+            f = p[side.lower() + "_type"]
+            if inputs.MX_BITS[f] == 6:
+                p[side] = inputs.mx_pack(rng.integers(0, 64, (rows, K)), f)
+        C, _ = _extras(M, N, 5)
+        say("mx tiled6", pair, (M, N, K))
+        D, name = gpu_mx(p, C=C)
+        assert name.startswith("mx_tiled6"), name
+        r = _vs_oracle(orc, p, D, C=C)
+        say("  ", r)
+        assert r.ok, r
+
+
+def test_mx_tiled6_repeated_calls(orc):
+    """Back-to-back calls of different sizes on one stream reuse the
+    expansion's temporaries; each result stays right."""
+    outs = []
+    for (M, N, K, seed) in [(512, 512, 2048, 46), (300, 200, 512, 47), (512, 512, 2048, 48)]:
+        p = _problem("e3m2", "e2m3", M, N, K, seed=seed)
+        M, N, K = p["M"], p["N"], p["K"]
+        desc = G.make_desc(M, N, K, "e3m2", "e2m3", "f32", has_c=False, block_scale=32)
+        plan = G.gemm_plan(desc)
+        D = empty_out(M, N, "f32")
+        G.gemm_mx_run(plan, to_dev(p["A"]), to_dev(p["SA"]), to_dev(p["B"]), to_dev(p["SB"]),
+                      None, None, D)
+        outs.append((p, D, plan.name))
+    torch.cuda.synchronize()
+    for p, D, name in outs:
+        assert name.startswith("mx_tiled6"), name
+        r = _vs_oracle(orc, p, D.cpu().numpy().view(np.float32).reshape(p["M"], p["N"]))
+        assert r.ok, r
+
+
 @pytest.mark.parametrize("pair", [("e4m3", "e4m3"), ("e2m1", "e2m1"), ("e2m3", "e3m2")],
                          ids=["mxfp8", "mxfp4", "mxfp6"])
 @pytest.mark.parametrize("d_type", ["bf16", "f16"])
@@ -106,7 +150,8 @@ def _pad_rows(packed, extra_bytes):
     return np.concatenate([packed, np.zeros((rows, extra_bytes), np.uint8)], axis=1)
 
 
-@pytest.mark.parametrize("fmt,pad_elems", [("e2m1", 32), ("e4m3", 16), ("e2m3", 4)])
+@pytest.mark.parametrize("fmt,pad_elems", [("e2m1", 32), ("e4m3", 16), ("e2m3", 4),
+                                           ("e2m3", 16), ("e2m3", 32), ("e3m2", 8)])
 def test_mx_padded_rows(orc, fmt, pad_elems):
     M, N, K = 200, 150, 512
     p = _problem(fmt, fmt, M, N, K, seed=43)
@@ -115,18 +160,28 @@ def test_mx_padded_rows(orc, fmt, pad_elems):
     B = _pad_rows(p["B"], pad_elems * bits // 8)
     D, name = gpu_mx(p, lda=K + pad_elems, ldb=K + pad_elems, A=A, B=B)
     say("  padded", fmt, name)
-    assert name.startswith("mx_tiled" if (fmt != "e2m3" and pad_elems * bits % 128 == 0)
-                           else "mx_generic"), name
+    if bits == 6:   # the expansion reads 4-byte words: rows of a multiple of 4 bytes
+        want = "mx_tiled6" if pad_elems * bits % 32 == 0 else "mx_generic"
+    else:
+        want = "mx_tiled" if pad_elems * bits % 128 == 0 else "mx_generic"
+    assert name.startswith(want), name
     r = _vs_oracle(orc, p, D)
     assert r.ok, r
 
 
-def test_mx_misaligned_a_falls_back(orc):
+@pytest.mark.parametrize("pair,off", [(("e4m3", "e5m2"), 8), (("e2m3", "e3m2"), 2),
+                                      (("e4m3", "e3m2"), 4), (("e2m3", "e3m2"), 4),
+                                      (("e2m3", "e3m2"), 8)])
+def test_mx_misaligned_a_falls_back(orc, pair, off):
+    """A off the alignment the tiled path reads it with (16 bytes for 8-bit
+    codes, 4 for packed 6-bit ones): the run takes the generic kernel.  A
+    6-bit pair 4- but not 8-byte aligned takes the 8-bit code expansion
+    instead of the padded regrouping; 8-byte aligned, the regrouping."""
     M, N, K = 160, 96, 512
-    p = _problem("e4m3", "e5m2", M, N, K, seed=44)
+    p = _problem(pair[0], pair[1], M, N, K, seed=44)
     buf = torch.zeros(p["A"].size + 64, dtype=torch.uint8, device="cuda")
-    buf[8:8 + p["A"].size] = to_dev(p["A"]).view(-1)
-    D, name = gpu_mx(p, a_dev=buf[8:])
+    buf[off:off + p["A"].size] = to_dev(p["A"]).view(-1)
+    D, name = gpu_mx(p, a_dev=buf[off:])
     assert name.startswith("mx_tiled")  # the plan; the run used the generic kernel
     r = _vs_oracle(orc, p, D)
     assert r.ok, r
@@ -141,7 +196,11 @@ def test_mx_plan_choice():
     assert name("e4m3", "e4m3", 96).startswith("mx_generic")    # K % 512
     assert name("e2m1", "e2m1", 256).startswith("mx_generic")
     assert name("e2m1", "e4m3", 512).startswith("mx_generic")   # two widths
-    assert name("e2m3", "e2m3", 512).startswith("mx_generic")   # 6-bit
+    assert name("e2m3", "e2m3", 512).startswith("mx_tiled6")
+    assert name("e3m2", "e4m3", 1024).startswith("mx_tiled6")
+    assert name("e5m2", "e2m3", 512).startswith("mx_tiled6")
+    assert name("e2m3", "e2m1", 512).startswith("mx_generic")   # 6-bit with 4-bit
+    assert name("e2m3", "e3m2", 256).startswith("mx_generic")   # K % 512
     with pytest.raises(G.GemmError):
         G.gemm_plan(G.make_desc(512, 512, 96, "e4m3", "e4m3", "f32", has_c=False,
                                 block_scale=32, algo="tiled"))
