@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libstgemm.so")
 SOURCES = ["gemm_api.cpp", "kernels_dense.hip", "kernels_sparse.hip", "kernels_mx.hip",
-           "kernels_w4.hip", "kernels_mn.hip", "kernels_diag.hip"]
+           "kernels_w4.hip", "kernels_mn.hip", "kernels_diag.hip", "kernels_k16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -774,8 +774,9 @@ __device__ STG_AI inline i4_t add_c(i4_t v, i4_t c, int sat)
     return v;
 }
 
-// Epilogue of a wave's (32 FM) x (32 FN) accumulator block at (m0, n0)
-// (the same in every lane),
+// Epilogue of a wave's (FB FM) x (FB FN) accumulator block at (m0, n0)
+// (the same in every lane; FB = 32 for the 32x32 MFMA forms, 16 for the
+// 16x16 forms, whose accumulators hold 4 values per lane),
 // staged through `lds_wave` (32 * (32 FN + 4) words of LDS owned by this
 // wave): for each 32-row slab, the fragments are written to LDS in row-major
 // order, then read back four consecutive columns per lane, so C and bias are
@@ -794,7 +795,10 @@ template <class OP, int FM, int FN, int KIND>
 __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_t (&acc)[FM][FN],
                                       int64_t m0, int64_t n0, int lane, uint32_t *lds_wave)
 {
-    constexpr int COLS = 32 * FN, PITCH = COLS + 4, LPR = COLS / 4; // lanes per row
+    constexpr bool M16 = sizeof(typename OP::acc_t) == 16; // 16x16 fragments
+    constexpr int FB = M16 ? 16 : 32;                      // fragment rows / columns
+    constexpr int NSLAB = FM * FB / 32;                    // 32-row slabs
+    constexpr int COLS = FB * FN, PITCH = COLS + 4, LPR = COLS / 4; // lanes per row
     constexpr int RPP = 64 / LPR;                                    // rows per pass
     constexpr int NP = 32 / RPP;                                     // passes per slab
     constexpr bool IOUT = KIND == OUT_S32;
@@ -833,7 +837,7 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
             bv = *(const f4_t *)(e.bias + col);
     }
 
-    // one slab per fragment row i, expanded at compile time so that the
+    // one slab per 32 rows (slab i), expanded at compile time so that the
     // accumulator indices are constants however large the body
     auto slab = [&](auto ic) STG_AI {
         constexpr int i = decltype(ic)::value;
@@ -857,19 +861,36 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
                 }
             }
         }
+        // (32x32: register r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
+        // column l % 32; 16x16: row 4 (l / 16) + r, column l % 16, and a slab
+        // holds fragment rows 2 i and 2 i + 1)
+        auto put = [&](int row, int col, auto x) STG_AI {
+            if constexpr (IOUT || !OP::INT)
+                lds_wave[row * PITCH + col] = __builtin_bit_cast(uint32_t, x);
+            else
+                lds_wave[row * PITCH + col] = __builtin_bit_cast(uint32_t, (float)x);
+        };
+        if constexpr (M16) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                // copy the element out first: a bit_cast applied to a
-                // vector-element expression would read element 0
-                const auto x = acc[i][j][r];
-                if constexpr (IOUT || !OP::INT)
-                    lds_wave[row * PITCH + j * 32 + (lane & 31)] = __builtin_bit_cast(uint32_t, x);
-                else
-                    lds_wave[row * PITCH + j * 32 + (lane & 31)] = __builtin_bit_cast(uint32_t, (float)x);
-            }
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const auto x = acc[2 * i + h][j][r];
+                        put(16 * h + 4 * (lane >> 4) + r, j * 16 + (lane & 15), x);
+                    }
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    // copy the element out first: a bit_cast applied to a
+                    // vector-element expression would read element 0
+                    const auto x = acc[i][j][r];
+                    put(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), j * 32 + (lane & 31), x);
+                }
+        }
         wave_lds_sync(); // the slab is in LDS
         if (fast) {
 #pragma unroll
@@ -904,7 +925,7 @@ __device__ STG_AI inline void epilogue_slabs(const EpiArgs &e, typename OP::acc_
     };
     [&]<int... I>(std::integer_sequence<int, I...>) STG_AI {
         (slab(std::integral_constant<int, I>{}), ...);
-    }(std::make_integer_sequence<int, FM>{});
+    }(std::make_integer_sequence<int, NSLAB>{});
 }
 
 

@@ -208,6 +208,8 @@ const char *family_name(int f)
     case KF_SPARSE_TILED: return "sparse24_tiled";
     case KF_SPARSE_DMA8: return "sparse24_dma8";
     case KF_TILED_256W8: return "tiled256w8";
+    case KF_TILED_256W8K16: return "tiled256w8k16";
+    case KF_TILED_256W8TK16: return "tiled256w8tk16";
     case KF_TILED_256W8T: return "tiled256w8t";
     case KF_MX_GENERIC: return "mx_generic";
     case KF_MX_TILED: return "mx_tiled";
@@ -231,7 +233,8 @@ bool skinny_ok(const gemm_desc_t &d)
 
 bool is_tiled(int f)
 {
-    return f == KF_TILED_256 || f == KF_TILED_128 || f == KF_TILED_256W8 || f == KF_TILED_256W8T;
+    return f == KF_TILED_256 || f == KF_TILED_128 || f == KF_TILED_256W8 || f == KF_TILED_256W8T ||
+           f == KF_TILED_256W8K16 || f == KF_TILED_256W8TK16;
 }
 
 } // namespace
@@ -589,11 +592,15 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
     int fam = -1;
     const int64_t big_tiles = ceil_div(d.M, 256) * ceil_div(d.N, 256);
     // 256 x 256 tiles: the fastest variant measured per operand type on
-    // MI355X at 8192^3 (16-bit: 8 waves of 128 x 64; int8: 8 waves of
-    // 64 x 128; fp8: 4 waves of 128 x 128, whose 8-wave forms run short of
+    // MI355X at 8192^3 (K-contiguous 16-bit and signed int8: 8 waves of
+    // 64 x 128 on the 16x16 MFMA forms; MN-major 16-bit: 8 waves of 128 x 64,
+    // MN-major or unsigned int8: 8 waves of 64 x 128, both on the 32x32
+    // forms; fp8: 4 waves of 128 x 128, whose 8-wave forms run short of
     // registers)
     const int op = op_kind(d.a_type, d.b_type);
-    const int fam256 = (op == OPK_S8 || uns) ? KF_TILED_256W8T
+    const bool k16 = layout == 0 && !uns && (op == OPK_F16 || op == OPK_BF16 || op == OPK_S8);
+    const int fam256 = k16 ? KF_TILED_256W8TK16
+                       : (op == OPK_S8 || uns) ? KF_TILED_256W8T
                        : (op == OPK_F16 || op == OPK_BF16) ? KF_TILED_256W8 : KF_TILED_256;
     const int auto_tiled = big_tiles >= di.num_cu ? fam256 : KF_TILED_128;
     switch (d.algo) {
@@ -618,6 +625,10 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
             const bool layout_ok = layout == 0 || f == fam256 || f == KF_TILED_128;
             // unsigned 8-bit operands are built on the 128 tile and w8t only
             const bool uns_ok = !uns || f == KF_TILED_128 || f == KF_TILED_256W8T;
+            // the 16x16-form kernel: 16-bit and int8 inputs, K-contiguous
+            if ((f == KF_TILED_256W8K16 || f == KF_TILED_256W8TK16) &&
+                (layout != 0 || (op != OPK_F16 && op != OPK_BF16 && op != OPK_S8)))
+                continue;
             if (strcmp(force, family_name(f)) == 0 &&
                 (f == KF_GENERIC || (tiled && is_tiled(f) && layout_ok && uns_ok) ||
                  (skinny && f == KF_SKINNY)))

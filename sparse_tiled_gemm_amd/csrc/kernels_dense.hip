@@ -390,6 +390,8 @@ hipError_t launch_dense(int family, int op, int layout, const GemmArgs &g, hipSt
     case KF_TILED_128: fn = tiled_table_t<128, 128>(op); break;
     case KF_SKINNY: fn = skinny_table(op); break;
     case KF_TILED_256W8: fn = tiled_table_t<256, 256, 2, 4>(op); break;
+    case KF_TILED_256W8K16: return launch_tiled16(op, g, s);
+    case KF_TILED_256W8TK16: return launch_tiled16t(op, g, s);
     case KF_TILED_256W8T: fn = tiled_table_t<256, 256, 4, 2>(op); break;
     default: break;
     }

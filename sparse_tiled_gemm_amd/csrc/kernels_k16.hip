@@ -1,0 +1,237 @@
+// The 256 x 256 LDS-tiled GEMM for 16-bit and int8 inputs on the 16x16 MFMA
+// forms (16x16x32 f16 / bf16, 16x16x64 i8)
+// ("Tensor Core 三种调用层次…", section 3: a workgroup tile staged through
+// shared memory, each warp's sub-tile accumulated from fragments; here eight
+// 64-lane waves, 128 x 64 each).
+//
+// The 16x16 forms do the work of the 32x32 ones in the same number of MFMA
+// passes but, under this chip's power limit, sustain a higher clock
+// (MFMA-only loops: 2015 vs 1771 TFLOP/s for bf16, 4118 vs 3488 TOP/s for
+// int8).  Their fragments cover twice the K per instruction, so
+// double-buffering every fragment as the 32x32 kernel does would need 96
+// registers beside the 128 accumulators; instead each K tile (64 bytes of K
+// = one instruction step) runs row block by row block, and A fragment i of
+// the next tile is read as soon as row block i's four MFMAs have been issued
+// (one A buffer), while the four B fragments are double-buffered.
+//
+// Fragment layout (16 bytes per lane): lane l holds row (A) or column (B)
+// l % 16; lane group l / 16 takes 16-byte chunk l / 16 of the tile's 64-byte
+// row, the same K for A and B.  Accumulator register r of lane l is row
+// 4 (l / 16) + r, column l % 16 of its 16 x 16 block.
+//
+// Global -> LDS staging, the LDS layout (64-byte rows, 16-byte chunks at
+// slot c ^ swz64(r)), the three-stage ring and the epilogue are those of
+// k_tiled (tiled_kernel.hpp).
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace stg {
+
+// GM x GN waves (2 x 4: 128 x 64 each, A fragments roll; 4 x 2: 64 x 128
+// each, B fragments roll and A is double-buffered)
+template <class OP, int GM, int GN>
+__global__ __launch_bounds__(512, 1) void k_tiled16(GemmArgs g, int tiles_m, int tiles_n)
+{
+    static_assert(OP::LANE_BYTES == 16, "16 bytes of K per lane and instruction");
+    static_assert(GM * GN == 8, "eight waves");
+    constexpr int NT = 512, BM = 256, BN = 256;
+    constexpr int BKB = 64, CH = BKB / 16, RPP = NT / CH; // 128 rows per load pass
+    constexpr int A_LD = BM / RPP, B_LD = BN / RPP;
+    constexpr int WM = BM / GM, WN = BN / GN;   // 128 x 64 per wave
+    constexpr int FI = WM / 16, FJ = WN / 16;   // 8 x 4 fragments
+    constexpr int NSTAGE = 3;
+    constexpr int A_TILE = BM * BKB, STAGE = (BM + BN) * BKB;
+    constexpr int EPI = GM * GN * 32 * (WN + 4) * 4;
+    constexpr int KLOOP = NSTAGE * STAGE;
+    constexpr int LDS_BYTES = KLOOP > EPI ? KLOOP : EPI;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m_blk = (int64_t)tm * BM, n_blk = (int64_t)tn * BN;
+    const int64_t lda_b = g.a_rs * OP::ELEM, ldb_b = g.b_cs * OP::ELEM;
+    const int64_t kbytes = g.K * OP::ELEM;
+    const int KT = (int)(kbytes / BKB);
+    // bounded by the last byte of the last row: loads past it return zero
+    const __amdgpu_buffer_rsrc_t ra =
+        tile_rsrc((const uint8_t *)g.A + m_blk * lda_b, (g.e.M - m_blk - 1) * lda_b + kbytes);
+    const __amdgpu_buffer_rsrc_t rb =
+        tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b, (g.e.N - n_blk - 1) * ldb_b + kbytes);
+
+    // global -> LDS copy: thread owns chunk `ch` of rows r0 + i RPP
+    const int ch = tid % CH, r0 = tid / CH;
+    const int va0 = r0 * (int)lda_b + ch * 16, vb0 = r0 * (int)ldb_b + ch * 16;
+    const int va_step = RPP * (int)lda_b, vb_step = RPP * (int)ldb_b;
+    const int l0 = r0 * BKB + ((ch ^ swz64(r0)) << 4); // + i RPP BKB (swz64 is RPP-periodic)
+    u4_t ga[2][A_LD], gb[2][B_LD];
+    auto gload = [&](auto set, int kt) STG_AI {
+        constexpr int S = decltype(set)::value;
+        const int soff = kt * BKB;
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i)
+            ga[S][i] = buf_load16(ra, va0 + i * va_step, soff);
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i)
+            gb[S][i] = buf_load16(rb, vb0 + i * vb_step, soff);
+    };
+    auto lstore = [&](auto set, uint8_t *__restrict__ stage_base) STG_AI {
+        constexpr int S = decltype(set)::value;
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i)
+            *(u4_t *)(stage_base + l0 + i * RPP * BKB) = ga[S][i];
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i)
+            *(u4_t *)(stage_base + A_TILE + l0 + i * RPP * BKB) = gb[S][i];
+    };
+
+    // fragments: A block i is rows wm WM + 16 i + l % 16, B block j rows
+    // wn WN + 16 j + l % 16 of the B tile, chunk l / 16 (swz64(r + 16 i) ==
+    // swz64(r))
+    const int wm = wave / GN, wn = wave % GN;
+    const int arow = wm * WM + (lane & 15), brow = wn * WN + (lane & 15), grp = lane >> 4;
+    const int a_off = arow * BKB + ((grp ^ swz64(arow)) << 4);
+    const int b_off = A_TILE + brow * BKB + ((grp ^ swz64(brow)) << 4);
+    // the operand with more fragments rolls (one buffer), the other is
+    // double-buffered; FR / FD fragments, R = rolling, D = double
+    constexpr bool ROLLB = FJ > FI;
+    constexpr int FR = ROLLB ? FJ : FI, FD = ROLLB ? FI : FJ;
+    const int r_off = ROLLB ? b_off : a_off, d_off = ROLLB ? a_off : b_off;
+    u4_t fr[FR], fd[2][FD];
+    auto read_r = [&](const uint8_t *stage_base, int i) STG_AI {
+        fr[i] = *(const u4_t *)(stage_base + r_off + i * 16 * BKB);
+    };
+    auto read_d = [&](auto set, const uint8_t *stage_base, int j) STG_AI {
+        constexpr int S = decltype(set)::value;
+        fd[S][j] = *(const u4_t *)(stage_base + d_off + j * 16 * BKB);
+    };
+
+    typename OP::acc_t acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+            acc[i][j] = typename OP::acc_t{};
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // prologue: tiles 0 and 1 in stages 0 and 1, tile 2 in register set 0,
+    // tile 0's fragments in registers (the last A fragment is read at the
+    // start of each tile)
+    gload(I0{}, 0);
+    gload(I1{}, 1);
+    lstore(I0{}, lds);
+    lstore(I1{}, lds + STAGE);
+    gload(I0{}, 2);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i + 1 < FR; ++i)
+        read_r(lds, i);
+#pragma unroll
+    for (int j = 0; j < FD; ++j)
+        read_d(I0{}, lds, j);
+
+    // One K tile t (parity P): tile t+3 into register set P^1; rolling
+    // fragment FR-1 of tile t; block i of the rolling operand times the FD
+    // double-buffered fragments, then rolling fragment i of tile t+1 (i <
+    // FR-1; the double-buffered fragments of tile t+1 with the first FD
+    // blocks); register set P (tile t+2) into its stage.  The last rolling
+    // fragment of a tile is read at the tile's start rather than after the
+    // previous tile's last MFMAs, so no fragment read is still in flight at
+    // the barrier.  Instruction order: DS reads after each block's MFMAs,
+    // global loads at MFMAs 0, 8, 16, 24 and LDS stores at 4, 12, 20, 28.
+    constexpr int NM = FI * FJ, NR = FR + FD, NL = A_LD + B_LD, NW = A_LD + B_LD;
+    auto schedule = [&]() STG_AI {
+        [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
+            (
+                [&]() STG_AI {
+                    constexpr int nr = spread(Q, NR, NM);
+                    constexpr int nl = spread((Q + NM / NL - 1) % NM, NL, NM);
+                    constexpr int nw = spread((Q + NM / NW - 5) % NM, NW, NM);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                    if constexpr (nr > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x100, nr, 0); // DS read
+                    if constexpr (nl > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x020, nl, 0); // VMEM read
+                    if constexpr (nw > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x200, nw, 0); // DS write
+                }(),
+                ...);
+        }(std::make_integer_sequence<int, NM>{});
+    };
+
+    int st = 0; // LDS stage of tile t
+    auto iter = [&](auto par, int t) STG_AI {
+        constexpr int P = decltype(par)::value;
+        const int st1 = st == NSTAGE - 1 ? 0 : st + 1;
+        const int st2 = st1 == NSTAGE - 1 ? 0 : st1 + 1;
+        auto body = [&](const uint8_t *__restrict__ cur, const uint8_t *__restrict__ nxt,
+                        uint8_t *__restrict__ wr) STG_AI {
+            gload(std::integral_constant<int, P ^ 1>{}, t + 3);
+            read_r(cur, FR - 1);
+#pragma unroll
+            for (int i = 0; i < FR; ++i) {
+#pragma unroll
+                for (int j = 0; j < FD; ++j) {
+                    if constexpr (ROLLB)
+                        acc[j][i] = OP::mma((const uint32_t *)&fd[P][j], (const uint32_t *)&fr[i],
+                                            acc[j][i]);
+                    else
+                        acc[i][j] = OP::mma((const uint32_t *)&fr[i], (const uint32_t *)&fd[P][j],
+                                            acc[i][j]);
+                }
+                if (i + 1 < FR)
+                    read_r(nxt, i);
+                if (i < FD)
+                    read_d(std::integral_constant<int, P ^ 1>{}, nxt, i);
+            }
+            lstore(std::integral_constant<int, P>{}, wr);
+            schedule();
+        };
+        body(lds + st * STAGE, lds + st1 * STAGE, lds + st2 * STAGE);
+        __syncthreads();
+        st = st1;
+    };
+
+    int t = 0;
+    for (; t + 1 < KT; t += 2) {
+        iter(I0{}, t);
+        iter(I1{}, t + 1);
+    }
+    if (t < KT)
+        iter(I0{}, t);
+
+    __syncthreads(); // every wave is done with the LDS stages
+    epilogue_grid_lds<OP, FI, FJ>(g.e, acc, m_blk + wm * WM, n_blk + wn * WN, lane,
+                                  (uint32_t *)lds + wave * 32 * (WN + 4));
+}
+
+template <int GM, int GN>
+static hipError_t launch_t16(int op, const GemmArgs &g, hipStream_t s)
+{
+    const int tiles_m = (int)((g.e.M + 255) / 256), tiles_n = (int)((g.e.N + 255) / 256);
+    const dim3 grid((unsigned)(tiles_m * tiles_n));
+    if (op == OPK_F16)
+        hipLaunchKernelGGL((k_tiled16<Op16F16, GM, GN>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+    else if (op == OPK_BF16)
+        hipLaunchKernelGGL((k_tiled16<Op16BF16, GM, GN>), grid, dim3(512), 0, s, g, tiles_m,
+                           tiles_n);
+    else if (op == OPK_S8)
+        hipLaunchKernelGGL((k_tiled16<Op16S8, GM, GN>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_tiled16(int op, const GemmArgs &g, hipStream_t s)
+{
+    return launch_t16<2, 4>(op, g, s);
+}
+hipError_t launch_tiled16t(int op, const GemmArgs &g, hipStream_t s)
+{
+    return launch_t16<4, 2>(op, g, s);
+}
+
+} // namespace stg

@@ -226,7 +226,7 @@ int main(int argc, char **argv)
     EXPECT(gemm_plan(&d, &p) == GEMM_OK);
     char name[64];
     gemm_plan_describe(p, name, sizeof name);
-    EXPECT(strcmp(name, "tiled256w8_bf16") == 0);
+    EXPECT(strcmp(name, "tiled256w8tk16_bf16") == 0);
     gemm_plan_destroy(p);
     EXPECT(gemm_validate_desc(nullptr) == GEMM_ERR_NULL_POINTER);
     EXPECT(gemm_plan(&d, nullptr) == GEMM_ERR_NULL_POINTER);

@@ -80,6 +80,57 @@ def test_dense_parity_256_variants(orc, monkeypatch, family, a_type, b_type, sha
     compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, "auto", expect_kernel=family)
 
 
+# the 16x16-form kernels: 16-bit and int8 inputs, K-contiguous
+K16_FAMILIES = ["tiled256w8k16", "tiled256w8tk16"]
+K16_PAIRS = [("f16", "f16"), ("bf16", "bf16"), ("s8", "s8")]
+
+
+@pytest.mark.parametrize("family", K16_FAMILIES)
+@pytest.mark.parametrize("a_type,b_type", K16_PAIRS)
+@pytest.mark.parametrize("shape", [(600, 520, 256), (256, 256, 64), (300, 700, 448),
+                                   (1000, 777, 576), (17, 300, 128)])
+def test_dense_parity_k16(orc, monkeypatch, family, a_type, b_type, shape):
+    """Both arrangements of the 16x16-form kernel (forced), ragged M and N,
+    K from one tile up."""
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", family)
+    M, N, K = shape
+    A, B, C, _ = make(a_type, b_type, M, N, K, seed=zlib.crc32(repr((family, a_type, shape)).encode()))
+    d_type = "s32" if a_type == "s8" else "f32"
+    compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, "auto", expect_kernel=family)
+
+
+@pytest.mark.parametrize("family", K16_FAMILIES)
+@pytest.mark.parametrize("a_type,d_type", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f16")])
+def test_epilogue_bit_exact_k16(orc, monkeypatch, family, a_type, d_type):
+    """The fused epilogue of the 16x16-form kernels against the oracle's fp32
+    epilogue on the same kernel's fp32 output, bit for bit."""
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", family)
+    M, N, K = 384, 320, 256
+    A, B, C, bias = make(a_type, a_type, M, N, K, seed=12, bias=True)
+    T, n1 = gpu_gemm(A, B, C, None, M, N, K, a_type, a_type, "f32")
+    D, n2 = gpu_gemm(A, B, C, bias, M, N, K, a_type, a_type, d_type, alpha=0.3, relu=True)
+    assert n1.startswith(family) and n2.startswith(family), (n1, n2)
+    ref = orc.epilogue_f32(T, 0.3, bias, True, d_type)
+    mism = int((D != ref).sum())
+    say("epilogue", family, a_type, d_type, "mismatches", mism)
+    assert mism == 0
+
+
+def test_k16_is_the_automatic_choice():
+    """K-contiguous f16 / bf16 / s8 at 256 x 256 scale take the 16x16-form
+    kernel; MN-major, unsigned and fp8 operands keep their kernels."""
+    def name(t, d, **kw):
+        return G.gemm_plan(G.make_desc(8192, 8192, 8192, t, t, d, **kw)).name
+    assert name("bf16", "bf16") == "tiled256w8tk16_bf16"
+    assert name("f16", "f32") == "tiled256w8tk16_f16"
+    assert name("s8", "s32") == "tiled256w8tk16_s8"
+    assert name("bf16", "bf16", a_layout="col") == "tiled256w8_bf16_acol"
+    assert name("s8", "s32", b_layout="row") == "tiled256w8t_s8_brow"
+    assert name("u8", "s32").startswith("tiled256w8t")
+    assert G.gemm_plan(G.make_desc(8192, 8192, 8192, "e4m3", "e5m2", "f16")).name.startswith(
+        "tiled256_")
+
+
 @pytest.mark.parametrize("a_type,b_type", PAIRS)
 @pytest.mark.parametrize("shape", [(16, 1024, 2048), (1, 300, 512), (7, 96, 1024), (16, 33, 256),
                                    (12, 8192, 768)])
@@ -200,7 +251,8 @@ def test_padded_leading_dimensions(orc, monkeypatch):
     Cp = rng.uniform(-1, 1, (M, ldc)).astype(np.float32)
     Dr, Y, S = orc.gemm(np.ascontiguousarray(Ap[:, :K]), np.ascontiguousarray(Bp[:, :K]),
                         np.ascontiguousarray(Cp[:, :N]), None, M, N, K, "bf16", "bf16", "bf16")
-    for algo in ["tiled128", "tiled256", "generic", "tiled256w8", "tiled256w8t"]:
+    for algo in ["tiled128", "tiled256", "generic", "tiled256w8", "tiled256w8t",
+                 "tiled256w8k16", "tiled256w8tk16"]:
         say("padded", algo)
         monkeypatch.delenv("STGEMM_FORCE_KERNEL", raising=False)
         if algo.startswith("tiled256") and algo != "tiled256":

@@ -42,6 +42,8 @@ def _fused_vs_f32(orc, run, d_type, alpha, bias, relu):
 
 # (family forced, a_type, shape): the float kernels with an fp8 output
 DENSE_FAMILIES = [("tiled256w8", "bf16", (300, 520, 256)), ("tiled256", "e4m3", (384, 264, 512)),
+                  ("tiled256w8tk16", "bf16", (300, 520, 256)),
+                  ("tiled256w8k16", "f16", (264, 300, 192)),
                   ("tiled128", "f16", (130, 200, 128)), ("generic", "bf16", (67, 45, 96)),
                   ("skinny", "bf16", (16, 300, 1024))]
 
@@ -74,6 +76,7 @@ def test_dense_fp8_output(orc, monkeypatch, fam, a_type, shape, d_type):
 
 
 S8_FAMILIES = [("tiled256w8t", (300, 520, 256)), ("tiled128", (130, 200, 128)),
+               ("tiled256w8tk16", (300, 520, 256)), ("tiled256w8k16", (264, 300, 192)),
                ("generic", (67, 45, 96)), ("skinny", (16, 300, 1024))]
 
 
@@ -192,7 +195,9 @@ def test_fp8_output_specials(orc, monkeypatch, fam, shape, d_type, relu):
 # then the same epilogue
 C16_FAMILIES = [("tiled256w8", "bf16", (300, 264, 256)), ("tiled128", "f16", (130, 200, 128)),
                 ("generic", "bf16", (67, 45, 96)), ("skinny", "f16", (16, 300, 1024)),
-                ("tiled256", "e4m3", (264, 300, 256)), ("tiled256w8t", "s8", (264, 300, 256))]
+                ("tiled256", "e4m3", (264, 300, 256)), ("tiled256w8t", "s8", (264, 300, 256)),
+                ("tiled256w8tk16", "bf16", (300, 264, 256)), ("tiled256w8tk16", "s8", (264, 300, 256)),
+                ("tiled256w8k16", "f16", (264, 300, 128))]
 
 
 @pytest.mark.parametrize("fam,a_type,shape", C16_FAMILIES, ids=[f[0] + "_" + f[1] for f in C16_FAMILIES])

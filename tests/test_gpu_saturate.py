@@ -42,8 +42,11 @@ def _check(orc, D, A, B, C, M, N, K, saturate, a_col=False, b_col=True):
 @pytest.mark.parametrize("fam,shape", [("tiled256w8t", (520, 300, 256)),
                                        ("tiled128", (200, 136, 128)),
                                        ("generic", (70, 90, 100)),
-                                       ("skinny", (16, 264, 512))],
-                         ids=["tiled256w8t", "tiled128", "generic", "skinny"])
+                                       ("skinny", (16, 264, 512)),
+                                       ("tiled256w8tk16", (520, 300, 256)),
+                                       ("tiled256w8k16", (300, 520, 192))],
+                         ids=["tiled256w8t", "tiled128", "generic", "skinny", "tiled256w8tk16",
+                              "tiled256w8k16"])
 @pytest.mark.parametrize("saturate", [True, False], ids=["sat", "wrap"])
 def test_dense_s32_saturation(orc, monkeypatch, fam, shape, saturate):
     monkeypatch.setenv("STGEMM_FORCE_KERNEL", fam)
