@@ -140,14 +140,30 @@ __global__ __launch_bounds__(512, 1) void k_tiled16(GemmArgs g, int tiles_m, int
     // blocks); register set P (tile t+2) into its stage.  The last rolling
     // fragment of a tile is read at the tile's start rather than after the
     // previous tile's last MFMAs, so no fragment read is still in flight at
-    // the barrier.  Instruction order: DS reads after each block's MFMAs,
-    // global loads at MFMAs 0, 8, 16, 24 and LDS stores at 4, 12, 20, 28.
-    constexpr int NM = FI * FJ, NR = FR + FD, NL = A_LD + B_LD, NW = A_LD + B_LD;
+    // the barrier.  Instruction order (MFMA q of the tile's FR x FD, block
+    // q / FD): the current tile's last rolling fragment after MFMA 0, the
+    // next tile's rolling fragment b after block b's last MFMA (b < FR-1, so
+    // the last one still has a block of MFMAs to complete under), its
+    // double-buffered fragments after MFMAs 1, 5, 9, 13; global loads at
+    // MFMAs 0, 8, 16, 24 and LDS stores at 4, 12, 20, 28.
+    constexpr int NM = FI * FJ, NL = A_LD + B_LD, NW = A_LD + B_LD;
+    auto nread = [](int q) constexpr {
+        return (q == 0 ? 1 : 0) + (q % FD == FD - 1 && q / FD < FR - 1 ? 1 : 0) +
+               (q % FD == 1 && q / FD < FD ? 1 : 0);
+    };
+    static_assert(
+        [&]() constexpr {
+            int n = 0;
+            for (int q = 0; q < NM; ++q)
+                n += nread(q);
+            return n;
+        }() == FR + FD,
+        "every fragment read has a slot");
     auto schedule = [&]() STG_AI {
         [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
             (
                 [&]() STG_AI {
-                    constexpr int nr = spread(Q, NR, NM);
+                    constexpr int nr = nread(Q);
                     constexpr int nl = spread((Q + NM / NL - 1) % NM, NL, NM);
                     constexpr int nw = spread((Q + NM / NW - 5) % NM, NW, NM);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
