@@ -215,6 +215,7 @@ const char *family_name(int f)
     case KF_MX_TILED: return "mx_tiled";
     case KF_W4_GENERIC: return "w4_generic";
     case KF_W4_TILED: return "w4_tiled";
+    case KF_W4_TILED16: return "w4_tiled16";
     case KF_W4_SKINNY: return "w4_skinny";
     case KF_MX_TILED6: return "mx_tiled6";
     default: return "?";
@@ -465,10 +466,11 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
                             rowb * 32 < lim;
         int fam = -1;
         switch (d.algo) {
-        case GEMM_ALGO_AUTO: fam = skinny ? KF_W4_SKINNY : fast ? KF_W4_TILED : KF_W4_GENERIC; break;
+        // (the 16x16-form kernel measured 1144 vs 1185 us at 8192^3, groups of 128)
+        case GEMM_ALGO_AUTO: fam = skinny ? KF_W4_SKINNY : fast ? KF_W4_TILED16 : KF_W4_GENERIC; break;
         case GEMM_ALGO_SKINNY: fam = skinny ? KF_W4_SKINNY : -1; break;
         case GEMM_ALGO_TILED:
-        case GEMM_ALGO_TILED_256: fam = fast ? KF_W4_TILED : -1; break;
+        case GEMM_ALGO_TILED_256: fam = fast ? KF_W4_TILED16 : -1; break;
         case GEMM_ALGO_GENERIC: fam = KF_W4_GENERIC; break;
         default: fam = -1;
         }
@@ -481,6 +483,8 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
                 fam = KF_W4_GENERIC;
             if (strcmp(force, family_name(KF_W4_TILED)) == 0 && fast)
                 fam = KF_W4_TILED;
+            if (strcmp(force, family_name(KF_W4_TILED16)) == 0 && fast)
+                fam = KF_W4_TILED16;
             if (strcmp(force, family_name(KF_W4_SKINNY)) == 0 && skinny)
                 fam = KF_W4_SKINNY;
         }
@@ -1065,7 +1069,8 @@ gemm_status_t gemm_w4a16_run(const gemm_plan_t *plan, const void *A, const void 
     g.wz = zeros;
     g.wgs = d.block_scale;
     int fam = plan->family;
-    if ((fam == KF_W4_TILED || fam == KF_W4_SKINNY) && (!aligned(A, 16) || !aligned(B, 16)))
+    if ((fam == KF_W4_TILED || fam == KF_W4_TILED16 || fam == KF_W4_SKINNY) &&
+        (!aligned(A, 16) || !aligned(B, 16)))
         fam = plan->fallback;
     hipError_t e = launch_w4(fam, plan->op, g, (hipStream_t)stream);
     if (e != hipSuccess)

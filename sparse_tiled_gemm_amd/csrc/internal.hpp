@@ -42,6 +42,7 @@ enum KernelFamily {
     KF_MX_TILED6,    // MX with 6-bit operands: expanded to 8-bit codes, then KF_MX_TILED's kernel
     KF_TILED_256W8K16,  // 16-bit / int8 inputs, 256 x 256, 8 waves of 128 x 64 on the 16x16 MFMA forms
     KF_TILED_256W8TK16, // the same, 8 waves of 64 x 128
+    KF_W4_TILED16,      // W4A16 on the 16x16-form kernel, 8 waves of 128 x 64
     KF_COUNT
 };
 
@@ -51,6 +52,7 @@ hipError_t launch_dense(int family, int op, int layout, const GemmArgs &g, hipSt
 // KF_TILED_256W8K16 (kernels_k16.hip): op OPK_F16, OPK_BF16 or OPK_S8, K-contiguous
 hipError_t launch_tiled16(int op, const GemmArgs &g, hipStream_t s);
 hipError_t launch_tiled16t(int op, const GemmArgs &g, hipStream_t s); // KF_TILED_256W8TK16
+hipError_t launch_w4_tiled16(int op, const GemmArgs &g, hipStream_t s); // KF_W4_TILED16
 // MN-major layouts (layout 1..3) on the tiled families that take them: the
 // 128 x 128 tile, and the 256 x 256 arrangement of each input type
 // (tiled256w8 16-bit, tiled256 fp8, tiled256w8t int8)

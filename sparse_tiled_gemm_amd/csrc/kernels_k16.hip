@@ -22,6 +22,12 @@
 // Global -> LDS staging, the LDS layout (64-byte rows, 16-byte chunks at
 // slot c ^ swz64(r)), the three-stage ring and the epilogue are those of
 // k_tiled (tiled_kernel.hpp).
+//
+// W4A16 (OpW4<Op16F16 / Op16BF16>): B holds 4-bit weight codes (16 bytes per
+// column per 32-K tile); threads 2c and 2c + 1 load 8 code bytes each of
+// column c with the group's scale and zero point and write the 16 values,
+// dequantised as in k_tiled (w4_dequant8), as chunks 2h and 2h + 1 of the
+// column's row of the B tile.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -51,39 +57,75 @@ __global__ __launch_bounds__(512, 1) void k_tiled16(GemmArgs g, int tiles_m, int
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int64_t m_blk = (int64_t)tm * BM, n_blk = (int64_t)tn * BN;
-    const int64_t lda_b = g.a_rs * OP::ELEM, ldb_b = g.b_cs * OP::ELEM;
-    const int64_t kbytes = g.K * OP::ELEM;
+    constexpr bool W4 = OP::W4;
+    constexpr bool BF = std::is_base_of<Op16BF16, OP>::value;
+    const int64_t lda_b = g.a_rs * OP::ELEM, ldb_b = W4 ? g.b_cs / 2 : g.b_cs * OP::ELEM;
+    const int64_t kbytes = g.K * OP::ELEM, kbytes_b = W4 ? g.K / 2 : kbytes;
     const int KT = (int)(kbytes / BKB);
     // bounded by the last byte of the last row: loads past it return zero
     const __amdgpu_buffer_rsrc_t ra =
         tile_rsrc((const uint8_t *)g.A + m_blk * lda_b, (g.e.M - m_blk - 1) * lda_b + kbytes);
     const __amdgpu_buffer_rsrc_t rb =
-        tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b, (g.e.N - n_blk - 1) * ldb_b + kbytes);
+        tile_rsrc((const uint8_t *)g.B + n_blk * ldb_b, (g.e.N - n_blk - 1) * ldb_b + kbytes_b);
+    // W4A16 group scales and zero points of the tile's columns (zero points
+    // absent: a zero-length resource, whose loads return 0, and z = 8)
+    const int64_t wgr = W4 ? g.K / g.wgs : 0; // groups per column
+    const __amdgpu_buffer_rsrc_t rws =
+        tile_rsrc((const uint8_t *)g.ws + n_blk * wgr * 2, W4 ? (g.e.N - n_blk) * wgr * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rwz = tile_rsrc(g.wz ? g.wz + n_blk * wgr : (const uint8_t *)g.B,
+                                                 W4 && g.wz ? (g.e.N - n_blk) * wgr : 0);
+    const bool has_wz = g.wz != nullptr;
+    const int wcol = tid >> 1, whalf = tid & 1; // W4A16: column and half of the codes
 
     // global -> LDS copy: thread owns chunk `ch` of rows r0 + i RPP
     const int ch = tid % CH, r0 = tid / CH;
     const int va0 = r0 * (int)lda_b + ch * 16, vb0 = r0 * (int)ldb_b + ch * 16;
     const int va_step = RPP * (int)lda_b, vb_step = RPP * (int)ldb_b;
     const int l0 = r0 * BKB + ((ch ^ swz64(r0)) << 4); // + i RPP BKB (swz64 is RPP-periodic)
-    u4_t ga[2][A_LD], gb[2][B_LD];
+    u4_t ga[2][A_LD], gb[2][W4 ? 1 : B_LD];
+    uint32_t gw[2][2], wsb[2], wzb[2]; // W4A16: 8 code bytes, scale bits, zero point
     auto gload = [&](auto set, int kt) STG_AI {
         constexpr int S = decltype(set)::value;
         const int soff = kt * BKB;
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
             ga[S][i] = buf_load16(ra, va0 + i * va_step, soff);
+        if constexpr (W4) {
+            typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+            const u2_t c = __builtin_bit_cast(
+                u2_t, __builtin_amdgcn_raw_buffer_load_b64(rb, wcol * (int)ldb_b + 8 * whalf,
+                                                           kt * (BKB / 4), 0));
+            gw[S][0] = c.x;
+            gw[S][1] = c.y;
+            const int grp = (int)((int64_t)kt * (BKB / 2) / g.wgs);
+            wsb[S] = __builtin_amdgcn_raw_buffer_load_b16(rws, (wcol * (int)wgr + grp) * 2, 0, 0);
+            wzb[S] = __builtin_amdgcn_raw_buffer_load_b8(rwz, wcol * (int)wgr + grp, 0, 0);
+        } else {
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i)
-            gb[S][i] = buf_load16(rb, vb0 + i * vb_step, soff);
+            for (int i = 0; i < B_LD; ++i)
+                gb[S][i] = buf_load16(rb, vb0 + i * vb_step, soff);
+        }
     };
     auto lstore = [&](auto set, uint8_t *__restrict__ stage_base) STG_AI {
         constexpr int S = decltype(set)::value;
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
             *(u4_t *)(stage_base + l0 + i * RPP * BKB) = ga[S][i];
+        if constexpr (W4) {
+            const float sc = w4_scale<BF>(wsb[S]);
+            const int z = has_wz ? (int)wzb[S] : 8;
+            uint8_t *brow = stage_base + A_TILE + wcol * BKB;
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i)
-            *(u4_t *)(stage_base + A_TILE + l0 + i * RPP * BKB) = gb[S][i];
+            for (int q = 0; q < 2; ++q) {
+                u4_t v;
+                w4_dequant8<BF>(gw[S][q], z, sc, (uint32_t *)&v);
+                *(u4_t *)(brow + (((2 * whalf + q) ^ swz64(wcol)) << 4)) = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_LD; ++i)
+                *(u4_t *)(stage_base + A_TILE + l0 + i * RPP * BKB) = gb[S][i];
+        }
     };
 
     // fragments: A block i is rows wm WM + 16 i + l % 16, B block j rows
@@ -146,7 +188,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled16(GemmArgs g, int tiles_m, int
     // the last one still has a block of MFMAs to complete under), its
     // double-buffered fragments after MFMAs 1, 5, 9, 13; global loads at
     // MFMAs 0, 8, 16, 24 and LDS stores at 4, 12, 20, 28.
-    constexpr int NM = FI * FJ, NL = A_LD + B_LD, NW = A_LD + B_LD;
+    constexpr int NM = FI * FJ, NL = A_LD + (W4 ? 3 : B_LD), NW = A_LD + B_LD;
     auto nread = [](int q) constexpr {
         return (q == 0 ? 1 : 0) + (q % FD == FD - 1 && q / FD < FR - 1 ? 1 : 0) +
                (q % FD == 1 && q / FD < FD ? 1 : 0);
@@ -248,6 +290,22 @@ hipError_t launch_tiled16(int op, const GemmArgs &g, hipStream_t s)
 hipError_t launch_tiled16t(int op, const GemmArgs &g, hipStream_t s)
 {
     return launch_t16<4, 2>(op, g, s);
+}
+
+// W4A16 on the 2 x 4 arrangement (op: the activations' type)
+hipError_t launch_w4_tiled16(int op, const GemmArgs &g, hipStream_t s)
+{
+    const int tiles_m = (int)((g.e.M + 255) / 256), tiles_n = (int)((g.e.N + 255) / 256);
+    const dim3 grid((unsigned)(tiles_m * tiles_n));
+    if (op == OPK_F16)
+        hipLaunchKernelGGL((k_tiled16<OpW4<Op16F16>, 2, 4>), grid, dim3(512), 0, s, g, tiles_m,
+                           tiles_n);
+    else if (op == OPK_BF16)
+        hipLaunchKernelGGL((k_tiled16<OpW4<Op16BF16>, 2, 4>), grid, dim3(512), 0, s, g, tiles_m,
+                           tiles_n);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 } // namespace stg

@@ -56,6 +56,8 @@ hipError_t launch_w4(int family, int op, const GemmArgs &g, hipStream_t s)
 {
     if (family == KF_W4_TILED)
         return launch_w4_tiled(op, g, s);
+    if (family == KF_W4_TILED16)
+        return launch_w4_tiled16(op, g, s);
     if (family == KF_W4_SKINNY)
         return launch_w4_skinny(op, g, s);
     if (family != KF_W4_GENERIC)

@@ -97,7 +97,7 @@ hipError_t launch_mx(int family, int afmt, int bfmt, const GemmArgs &g, hipStrea
 hipError_t launch_mx_tiled(int, int, const GemmArgs &, hipStream_t) { return hipSuccess; }
 hipError_t launch_w4(int family, int op, const GemmArgs &g, hipStream_t)
 {
-    EXPECT(family >= KF_W4_GENERIC && family <= KF_W4_SKINNY);
+    EXPECT((family >= KF_W4_GENERIC && family <= KF_W4_SKINNY) || family == KF_W4_TILED16);
     EXPECT((op == OPK_F16 || op == OPK_BF16) && g.wgs >= 32 && g.K % g.wgs == 0);
     check_epi(g.e);
     ++g_launches;

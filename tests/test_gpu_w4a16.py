@@ -49,15 +49,22 @@ def _C(M, N, seed=1):
     return np.random.default_rng(seed).uniform(-1, 1, (M, N)).astype(np.float32)
 
 
+# the 4-wave kernel on the 32x32 forms and the 16x16-form kernel, each
+# forced through the tuning override
+W4_TILED = ["w4_tiled", "w4_tiled16"]
+
+
+@pytest.mark.parametrize("family", W4_TILED)
 @pytest.mark.parametrize("a_type", ["bf16", "f16"])
 @pytest.mark.parametrize("gs", [32, 64, 128])
-def test_w4_tiled(orc, a_type, gs):
+def test_w4_tiled(orc, monkeypatch, family, a_type, gs):
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", family)
     for (M, N, K) in [(600, 520, 512), (256, 256, 128), (130, 300, 1024), (17, 700, 256)]:
         p = inputs.w4a16_problem(M, N, K, a_type, gs, workload=60)
         C = _C(M, N)
-        say("w4 tiled", a_type, gs, (M, N, K))
+        say("w4 tiled", family, a_type, gs, (M, N, K))
         D, name = gpu_w4(p, "f32", C=C)
-        assert name.startswith("w4_tiled"), name
+        assert name.startswith(family + "_"), name
         r = _vs_oracle(orc, p, D, "f32", C=C)
         say("  ", r)
         assert r.ok, r
@@ -92,8 +99,11 @@ def test_w4_skinny(orc, a_type, gs):
     assert name.startswith("w4_skinny") and _vs_oracle(orc, p, D, a_type).ok
 
 
-@pytest.mark.parametrize("algo", ["auto", "generic"])
-def test_w4_without_zero_points(orc, algo):
+@pytest.mark.parametrize("algo", ["auto", "generic", "w4_tiled16"])
+def test_w4_without_zero_points(orc, monkeypatch, algo):
+    if algo == "w4_tiled16":
+        monkeypatch.setenv("STGEMM_FORCE_KERNEL", algo)
+        algo = "auto"
     M, N, K = 300, 264, 512
     p = inputs.w4a16_problem(M, N, K, "bf16", 128, workload=62, zeros=False)
     assert p["zeros"] is None
@@ -102,16 +112,18 @@ def test_w4_without_zero_points(orc, algo):
     assert r.ok, r
 
 
+@pytest.mark.parametrize("family", W4_TILED)
 @pytest.mark.parametrize("a_type", ["bf16", "f16"])
 @pytest.mark.parametrize("d_type", ["bf16", "f16"])
-def test_w4_epilogue_bit_exact(orc, a_type, d_type):
+def test_w4_epilogue_bit_exact(orc, monkeypatch, family, a_type, d_type):
+    monkeypatch.setenv("STGEMM_FORCE_KERNEL", family)
     M, N, K = 384, 320, 512
     p = inputs.w4a16_problem(M, N, K, a_type, 64, workload=63)
     C = _C(M, N, 3)
     bias = np.random.default_rng(4).standard_normal(N).astype(np.float32)
     T, n1 = gpu_w4(p, "f32", C=C)
     D, n2 = gpu_w4(p, d_type, C=C, bias=bias, alpha=0.3, relu=True)
-    assert n1 == n2 and n1.startswith("w4_tiled")
+    assert n1 == n2 and n1.startswith(family + "_")
     ref = orc.epilogue_f32(T, 0.3, bias, True, d_type)
     assert int((D != ref).sum()) == 0
     r = _vs_oracle(orc, p, D, d_type, C=C, bias=bias, alpha=0.3, relu=True)
