@@ -19,9 +19,9 @@
 // row, the same K for A and B.  Accumulator register r of lane l is row
 // 4 (l / 16) + r, column l % 16 of its 16 x 16 block.
 //
-// Global -> LDS staging, the LDS layout (64-byte rows, 16-byte chunks at
-// slot c ^ swz64(r)), the three-stage ring and the epilogue are those of
-// k_tiled (tiled_kernel.hpp).
+// Global -> LDS staging, the LDS layout (64-byte rows of 16-byte chunks),
+// the three-stage ring and the epilogue are those of k_tiled
+// (tiled_kernel.hpp), except the chunk slot: c ^ swz16(r).
 //
 // W4A16 (OpW4<Op16F16 / Op16BF16>): B holds 4-bit weight codes (16 bytes per
 // column per 32-K tile); threads 2c and 2c + 1 load 8 code bytes each of
@@ -32,6 +32,15 @@
 #include "internal.hpp"
 
 namespace stg {
+
+// 16-byte chunk slot within a 64-byte LDS row for the 16x16 fragment reads
+// (16 consecutive rows per lane group, the four lane groups on the four
+// chunks): chunk c of row r at slot c ^ swz16(r).  Chosen by measurement on
+// gfx950 (LDS bank-conflict counter on a probe replaying this read
+// pattern): k_tiled's swz64, (r >> 2) & 3, is 2-way conflicted here (half
+// the LDS cycles), r & 3 and several rotations too; (r >> 1) & 3 is
+// conflict-free.  swz16(r + 16 i) == swz16(r).
+__device__ STG_AI inline int swz16(int r) { return (r >> 1) & 3; }
 
 // GM x GN waves (2 x 4: 128 x 64 each, A fragments roll; 4 x 2: 64 x 128
 // each, B fragments roll and A is double-buffered)
@@ -81,7 +90,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled16(GemmArgs g, int tiles_m, int
     const int ch = tid % CH, r0 = tid / CH;
     const int va0 = r0 * (int)lda_b + ch * 16, vb0 = r0 * (int)ldb_b + ch * 16;
     const int va_step = RPP * (int)lda_b, vb_step = RPP * (int)ldb_b;
-    const int l0 = r0 * BKB + ((ch ^ swz64(r0)) << 4); // + i RPP BKB (swz64 is RPP-periodic)
+    const int l0 = r0 * BKB + ((ch ^ swz16(r0)) << 4); // + i RPP BKB (swz16 is RPP-periodic)
     u4_t ga[2][A_LD], gb[2][W4 ? 1 : B_LD];
     uint32_t gw[2][2], wsb[2], wzb[2]; // W4A16: 8 code bytes, scale bits, zero point
     auto gload = [&](auto set, int kt) STG_AI {
@@ -119,7 +128,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled16(GemmArgs g, int tiles_m, int
             for (int q = 0; q < 2; ++q) {
                 u4_t v;
                 w4_dequant8<BF>(gw[S][q], z, sc, (uint32_t *)&v);
-                *(u4_t *)(brow + (((2 * whalf + q) ^ swz64(wcol)) << 4)) = v;
+                *(u4_t *)(brow + (((2 * whalf + q) ^ swz16(wcol)) << 4)) = v;
             }
         } else {
 #pragma unroll
@@ -129,12 +138,11 @@ __global__ __launch_bounds__(512, 1) void k_tiled16(GemmArgs g, int tiles_m, int
     };
 
     // fragments: A block i is rows wm WM + 16 i + l % 16, B block j rows
-    // wn WN + 16 j + l % 16 of the B tile, chunk l / 16 (swz64(r + 16 i) ==
-    // swz64(r))
+    // wn WN + 16 j + l % 16 of the B tile, chunk l / 16
     const int wm = wave / GN, wn = wave % GN;
     const int arow = wm * WM + (lane & 15), brow = wn * WN + (lane & 15), grp = lane >> 4;
-    const int a_off = arow * BKB + ((grp ^ swz64(arow)) << 4);
-    const int b_off = A_TILE + brow * BKB + ((grp ^ swz64(brow)) << 4);
+    const int a_off = arow * BKB + ((grp ^ swz16(arow)) << 4);
+    const int b_off = A_TILE + brow * BKB + ((grp ^ swz16(brow)) << 4);
     // the operand with more fragments rolls (one buffer), the other is
     // double-buffered; FR / FD fragments, R = rolling, D = double
     constexpr bool ROLLB = FJ > FI;
