@@ -108,8 +108,8 @@ typedef enum {
  *
  * Support matrix (everything else is GEMM_ERR_UNSUPPORTED):
  *   a, b in {F16}, {BF16}, or {F8_E4M3, F8_E5M2} (the two fp8 formats may
- *   differ): c_type F32, F16 or BF16 (a 16-bit C is widened exactly to fp32;
- *   it takes the element-wise epilogue), d_type F32 / F16 / BF16 / F8_E4M3 /
+ *   differ): c_type F32, F16 or BF16 (a 16-bit C is widened exactly to fp32
+ *   before the addition), d_type F32 / F16 / BF16 / F8_E4M3 /
  *   F8_E5M2, any epilogue.
  *   a, b in {S8, U8} (any pairing: the INT8 rows of the instruction tables
  *   on "NVIDIA MMA", section "Ampere: FP16/BF16 and integer MMA baseline",
