@@ -596,14 +596,17 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
     int fam = -1;
     const int64_t big_tiles = ceil_div(d.M, 256) * ceil_div(d.N, 256);
     // 256 x 256 tiles: the fastest variant measured per operand type on
-    // MI355X at 8192^3 (K-contiguous 16-bit and signed int8: 8 waves of
-    // 64 x 128 on the 16x16 MFMA forms; MN-major 16-bit: 8 waves of 128 x 64,
-    // MN-major or unsigned int8: 8 waves of 64 x 128, both on the 32x32
-    // forms; fp8: 4 waves of 128 x 128, whose 8-wave forms run short of
-    // registers)
+    // MI355X at 8192^3 (K-contiguous: 16-bit and signed int8 on 8 waves of
+    // 64 x 128 with the 16x16 MFMA forms, fp8 on 8 waves of 128 x 64 with
+    // the 32x32x64 form, both with fragments refreshed in place; MN-major
+    // 16-bit: 8 waves of 128 x 64, MN-major or unsigned int8: 8 waves of
+    // 64 x 128, on the 32x32 forms; MN-major fp8: 4 waves of 128 x 128, whose
+    // double-buffered 8-wave forms run short of registers)
     const int op = op_kind(d.a_type, d.b_type);
     const bool k16 = layout == 0 && !uns && (op == OPK_F16 || op == OPK_BF16 || op == OPK_S8);
+    const bool f8 = op == OPK_F8_E4E4 || op == OPK_F8_E4E5 || op == OPK_F8_E5E4 || op == OPK_F8_E5E5;
     const int fam256 = k16 ? KF_TILED_256W8TK16
+                       : (layout == 0 && f8) ? KF_TILED_256W8K16
                        : (op == OPK_S8 || uns) ? KF_TILED_256W8T
                        : (op == OPK_F16 || op == OPK_BF16) ? KF_TILED_256W8 : KF_TILED_256;
     const int auto_tiled = big_tiles >= di.num_cu ? fam256 : KF_TILED_128;
@@ -629,9 +632,10 @@ static gemm_status_t plan_impl(const gemm_desc_t *desc, gemm_plan_t **out)
             const bool layout_ok = layout == 0 || f == fam256 || f == KF_TILED_128;
             // unsigned 8-bit operands are built on the 128 tile and w8t only
             const bool uns_ok = !uns || f == KF_TILED_128 || f == KF_TILED_256W8T;
-            // the 16x16-form kernel: 16-bit and int8 inputs, K-contiguous
+            // the rolling-fragment kernel: 16-bit and int8 inputs on the
+            // 16x16 forms, fp8 on the 32x32 form; K-contiguous
             if ((f == KF_TILED_256W8K16 || f == KF_TILED_256W8TK16) &&
-                (layout != 0 || (op != OPK_F16 && op != OPK_BF16 && op != OPK_S8)))
+                (layout != 0 || op == OPK_U8S8 || op == OPK_S8U8 || op == OPK_U8U8))
                 continue;
             if (strcmp(force, family_name(f)) == 0 &&
                 (f == KF_GENERIC || (tiled && is_tiled(f) && layout_ok && uns_ok) ||

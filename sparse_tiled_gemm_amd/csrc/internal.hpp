@@ -40,7 +40,8 @@ enum KernelFamily {
     KF_W4_TILED,     // W4A16, 256 x 256 4-wave tile, B dequantised into LDS
     KF_W4_SKINNY,    // W4A16, M <= 16, B streamed and dequantised in registers
     KF_MX_TILED6,    // MX with 6-bit operands: expanded to 8-bit codes, then KF_MX_TILED's kernel
-    KF_TILED_256W8K16,  // 16-bit / int8 inputs, 256 x 256, 8 waves of 128 x 64 on the 16x16 MFMA forms
+    KF_TILED_256W8K16,  // k_tiled16: 256 x 256, 8 waves of 128 x 64, fragments refreshed in
+                        // place (16-bit / int8 on the 16x16 forms, fp8 on 32x32x64)
     KF_TILED_256W8TK16, // the same, 8 waves of 64 x 128
     KF_W4_TILED16,      // W4A16 on the 16x16-form kernel, 8 waves of 128 x 64
     KF_COUNT
@@ -49,7 +50,8 @@ enum KernelFamily {
 // layout: 0 A row-major and B column-major (K contiguous); bit 0 A
 // column-major, bit 1 B row-major (generic, or see launch_dense_mn)
 hipError_t launch_dense(int family, int op, int layout, const GemmArgs &g, hipStream_t s);
-// KF_TILED_256W8K16 (kernels_k16.hip): op OPK_F16, OPK_BF16 or OPK_S8, K-contiguous
+// KF_TILED_256W8K16 (kernels_k16.hip): op OPK_F16, OPK_BF16, OPK_S8 or an fp8
+// pair, K-contiguous
 hipError_t launch_tiled16(int op, const GemmArgs &g, hipStream_t s);
 hipError_t launch_tiled16t(int op, const GemmArgs &g, hipStream_t s); // KF_TILED_256W8TK16
 hipError_t launch_w4_tiled16(int op, const GemmArgs &g, hipStream_t s); // KF_W4_TILED16

@@ -43,17 +43,27 @@ namespace stg {
 __device__ STG_AI inline int swz16(int r) { return (r >> 1) & 3; }
 
 // GM x GN waves (2 x 4: 128 x 64 each, A fragments roll; 4 x 2: 64 x 128
-// each, B fragments roll and A is double-buffered)
+// each, B fragments roll and A is double-buffered).  OP: a 16x16 form (16
+// bytes of K per lane: one 16-byte read per fragment) or the 32x32x64 fp8
+// form OpF8 (32x32 blocks, 32 bytes per lane: two reads, chunks 2 h and
+// 2 h + 1 of the row for lane half h -- a K order the MFMA reads as its own
+// permutation of the tile's 64 K, the same for A and B, so the sum is
+// unchanged -- with k_tiled's slot function swz64, conflict-free for
+// 32-row reads).
 template <class OP, int GM, int GN>
 __global__ __launch_bounds__(512, 1) void k_tiled16(GemmArgs g, int tiles_m, int tiles_n)
 {
-    static_assert(OP::LANE_BYTES == 16, "16 bytes of K per lane and instruction");
+    constexpr bool M16 = sizeof(typename OP::acc_t) == 16; // 16x16 form
+    constexpr int FB = M16 ? 16 : 32;                      // rows / columns per fragment
+    constexpr int NRD = OP::LANE_BYTES / 16;               // 16-byte reads per fragment
+    static_assert((M16 && NRD == 1) || (!M16 && NRD == 2), "one 64-byte K tile per instruction");
     static_assert(GM * GN == 8, "eight waves");
     constexpr int NT = 512, BM = 256, BN = 256;
     constexpr int BKB = 64, CH = BKB / 16, RPP = NT / CH; // 128 rows per load pass
     constexpr int A_LD = BM / RPP, B_LD = BN / RPP;
     constexpr int WM = BM / GM, WN = BN / GN;   // 128 x 64 per wave
-    constexpr int FI = WM / 16, FJ = WN / 16;   // 8 x 4 fragments
+    constexpr int FI = WM / FB, FJ = WN / FB;   // fragments (8 x 4 for 16x16, 2 x 4 ...)
+    auto swz = [](int r) STG_AI { return M16 ? swz16(r) : swz64(r); };
     constexpr int NSTAGE = 3;
     constexpr int A_TILE = BM * BKB, STAGE = (BM + BN) * BKB;
     constexpr int EPI = GM * GN * 32 * (WN + 4) * 4;
@@ -67,6 +77,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled16(GemmArgs g, int tiles_m, int
     tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int64_t m_blk = (int64_t)tm * BM, n_blk = (int64_t)tn * BN;
     constexpr bool W4 = OP::W4;
+    static_assert(!W4 || M16, "W4A16 on the 16x16 forms");
     constexpr bool BF = std::is_base_of<Op16BF16, OP>::value;
     const int64_t lda_b = g.a_rs * OP::ELEM, ldb_b = W4 ? g.b_cs / 2 : g.b_cs * OP::ELEM;
     const int64_t kbytes = g.K * OP::ELEM, kbytes_b = W4 ? g.K / 2 : kbytes;
@@ -90,7 +101,7 @@ __global__ __launch_bounds__(512, 1) void k_tiled16(GemmArgs g, int tiles_m, int
     const int ch = tid % CH, r0 = tid / CH;
     const int va0 = r0 * (int)lda_b + ch * 16, vb0 = r0 * (int)ldb_b + ch * 16;
     const int va_step = RPP * (int)lda_b, vb_step = RPP * (int)ldb_b;
-    const int l0 = r0 * BKB + ((ch ^ swz16(r0)) << 4); // + i RPP BKB (swz16 is RPP-periodic)
+    const int l0 = r0 * BKB + ((ch ^ swz(r0)) << 4); // + i RPP BKB (swz is RPP-periodic)
     u4_t ga[2][A_LD], gb[2][W4 ? 1 : B_LD];
     uint32_t gw[2][2], wsb[2], wzb[2]; // W4A16: 8 code bytes, scale bits, zero point
     auto gload = [&](auto set, int kt) STG_AI {
@@ -137,24 +148,33 @@ __global__ __launch_bounds__(512, 1) void k_tiled16(GemmArgs g, int tiles_m, int
         }
     };
 
-    // fragments: A block i is rows wm WM + 16 i + l % 16, B block j rows
-    // wn WN + 16 j + l % 16 of the B tile, chunk l / 16
+    // fragments: A block i is rows wm WM + FB i + l % FB, B block j rows
+    // wn WN + FB j + l % FB of the B tile; chunks l / 16 (16x16) or
+    // 2 (l / 32) + q, q < 2 (32x32)
     const int wm = wave / GN, wn = wave % GN;
-    const int arow = wm * WM + (lane & 15), brow = wn * WN + (lane & 15), grp = lane >> 4;
-    const int a_off = arow * BKB + ((grp ^ swz16(arow)) << 4);
-    const int b_off = A_TILE + brow * BKB + ((grp ^ swz16(brow)) << 4);
+    const int arow = wm * WM + (lane & (FB - 1)), brow = wn * WN + (lane & (FB - 1));
+    const int grp = M16 ? lane >> 4 : 2 * (lane >> 5);
+    int a_off[NRD], b_off[NRD];
+#pragma unroll
+    for (int q = 0; q < NRD; ++q) {
+        a_off[q] = arow * BKB + (((grp + q) ^ swz(arow)) << 4);
+        b_off[q] = A_TILE + brow * BKB + (((grp + q) ^ swz(brow)) << 4);
+    }
     // the operand with more fragments rolls (one buffer), the other is
     // double-buffered; FR / FD fragments, R = rolling, D = double
     constexpr bool ROLLB = FJ > FI;
     constexpr int FR = ROLLB ? FJ : FI, FD = ROLLB ? FI : FJ;
-    const int r_off = ROLLB ? b_off : a_off, d_off = ROLLB ? a_off : b_off;
-    u4_t fr[FR], fd[2][FD];
+    u4_t fr[FR][NRD], fd[2][FD][NRD];
     auto read_r = [&](const uint8_t *stage_base, int i) STG_AI {
-        fr[i] = *(const u4_t *)(stage_base + r_off + i * 16 * BKB);
+#pragma unroll
+        for (int q = 0; q < NRD; ++q)
+            fr[i][q] = *(const u4_t *)(stage_base + (ROLLB ? b_off[q] : a_off[q]) + i * FB * BKB);
     };
     auto read_d = [&](auto set, const uint8_t *stage_base, int j) STG_AI {
         constexpr int S = decltype(set)::value;
-        fd[S][j] = *(const u4_t *)(stage_base + d_off + j * 16 * BKB);
+#pragma unroll
+        for (int q = 0; q < NRD; ++q)
+            fd[S][j][q] = *(const u4_t *)(stage_base + (ROLLB ? a_off[q] : b_off[q]) + j * FB * BKB);
     };
 
     typename OP::acc_t acc[FI][FJ];
@@ -213,9 +233,9 @@ __global__ __launch_bounds__(512, 1) void k_tiled16(GemmArgs g, int tiles_m, int
         [&]<int... Q>(std::integer_sequence<int, Q...>) STG_AI {
             (
                 [&]() STG_AI {
-                    constexpr int nr = nread(Q);
+                    constexpr int nr = nread(Q) * NRD;
                     constexpr int nl = spread((Q + NM / NL - 1) % NM, NL, NM);
-                    constexpr int nw = spread((Q + NM / NW - 5) % NM, NW, NM);
+                    constexpr int nw = spread(((Q + NM / NW - 5) % NM + NM) % NM, NW, NM);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
                     if constexpr (nr > 0)
                         __builtin_amdgcn_sched_group_barrier(0x100, nr, 0); // DS read
@@ -286,6 +306,14 @@ static hipError_t launch_t16(int op, const GemmArgs &g, hipStream_t s)
                            tiles_n);
     else if (op == OPK_S8)
         hipLaunchKernelGGL((k_tiled16<Op16S8, GM, GN>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+    else if (op == OPK_F8_E4E4)
+        hipLaunchKernelGGL((k_tiled16<OpF8<0, 0>, GM, GN>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+    else if (op == OPK_F8_E4E5)
+        hipLaunchKernelGGL((k_tiled16<OpF8<0, 1>, GM, GN>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+    else if (op == OPK_F8_E5E4)
+        hipLaunchKernelGGL((k_tiled16<OpF8<1, 0>, GM, GN>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
+    else if (op == OPK_F8_E5E5)
+        hipLaunchKernelGGL((k_tiled16<OpF8<1, 1>, GM, GN>), grid, dim3(512), 0, s, g, tiles_m, tiles_n);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -80,9 +80,11 @@ def test_dense_parity_256_variants(orc, monkeypatch, family, a_type, b_type, sha
     compare(orc, A, B, C, None, M, N, K, a_type, b_type, d_type, "auto", expect_kernel=family)
 
 
-# the 16x16-form kernels: 16-bit and int8 inputs, K-contiguous
+# the rolling-fragment kernels (k_tiled16): 16-bit and int8 inputs on the
+# 16x16 forms, fp8 on the 32x32x64 form; K-contiguous
 K16_FAMILIES = ["tiled256w8k16", "tiled256w8tk16"]
-K16_PAIRS = [("f16", "f16"), ("bf16", "bf16"), ("s8", "s8")]
+K16_PAIRS = [("f16", "f16"), ("bf16", "bf16"), ("s8", "s8"), ("e4m3", "e5m2"), ("e5m2", "e4m3"),
+             ("e4m3", "e4m3"), ("e5m2", "e5m2")]
 
 
 @pytest.mark.parametrize("family", K16_FAMILIES)
@@ -100,25 +102,28 @@ def test_dense_parity_k16(orc, monkeypatch, family, a_type, b_type, shape):
 
 
 @pytest.mark.parametrize("family", K16_FAMILIES)
-@pytest.mark.parametrize("a_type,d_type", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f16")])
-def test_epilogue_bit_exact_k16(orc, monkeypatch, family, a_type, d_type):
-    """The fused epilogue of the 16x16-form kernels against the oracle's fp32
-    epilogue on the same kernel's fp32 output, bit for bit."""
+@pytest.mark.parametrize("a_type,b_type,d_type", [("bf16", "bf16", "bf16"), ("f16", "f16", "f16"),
+                                                  ("bf16", "bf16", "f16"),
+                                                  ("e4m3", "e5m2", "f16")])
+def test_epilogue_bit_exact_k16(orc, monkeypatch, family, a_type, b_type, d_type):
+    """The fused epilogue of the rolling-fragment kernels against the
+    oracle's fp32 epilogue on the same kernel's fp32 output, bit for bit."""
     monkeypatch.setenv("STGEMM_FORCE_KERNEL", family)
     M, N, K = 384, 320, 256
-    A, B, C, bias = make(a_type, a_type, M, N, K, seed=12, bias=True)
-    T, n1 = gpu_gemm(A, B, C, None, M, N, K, a_type, a_type, "f32")
-    D, n2 = gpu_gemm(A, B, C, bias, M, N, K, a_type, a_type, d_type, alpha=0.3, relu=True)
+    A, B, C, bias = make(a_type, b_type, M, N, K, seed=12, bias=True)
+    alpha = 0.3 if not a_type.startswith("e") else 0.3 / 256.0
+    T, n1 = gpu_gemm(A, B, C, None, M, N, K, a_type, b_type, "f32")
+    D, n2 = gpu_gemm(A, B, C, bias, M, N, K, a_type, b_type, d_type, alpha=alpha, relu=True)
     assert n1.startswith(family) and n2.startswith(family), (n1, n2)
-    ref = orc.epilogue_f32(T, 0.3, bias, True, d_type)
+    ref = orc.epilogue_f32(T, alpha, bias, True, d_type)
     mism = int((D != ref).sum())
     say("epilogue", family, a_type, d_type, "mismatches", mism)
     assert mism == 0
 
 
 def test_k16_is_the_automatic_choice():
-    """K-contiguous f16 / bf16 / s8 at 256 x 256 scale take the 16x16-form
-    kernel; MN-major, unsigned and fp8 operands keep their kernels."""
+    """K-contiguous f16 / bf16 / s8 / fp8 at 256 x 256 scale take the
+    rolling-fragment kernel; MN-major and unsigned operands keep theirs."""
     def name(t, d, **kw):
         return G.gemm_plan(G.make_desc(8192, 8192, 8192, t, t, d, **kw)).name
     assert name("bf16", "bf16") == "tiled256w8tk16_bf16"
@@ -127,8 +132,10 @@ def test_k16_is_the_automatic_choice():
     assert name("bf16", "bf16", a_layout="col") == "tiled256w8_bf16_acol"
     assert name("s8", "s32", b_layout="row") == "tiled256w8t_s8_brow"
     assert name("u8", "s32").startswith("tiled256w8t")
-    assert G.gemm_plan(G.make_desc(8192, 8192, 8192, "e4m3", "e5m2", "f16")).name.startswith(
-        "tiled256_")
+    fp8 = G.make_desc(8192, 8192, 8192, "e4m3", "e5m2", "f16")
+    assert G.gemm_plan(fp8).name == "tiled256w8k16_e4m3xe5m2"
+    fp8mn = G.make_desc(8192, 8192, 8192, "e4m3", "e5m2", "f16", a_layout="col")
+    assert G.gemm_plan(fp8mn).name.startswith("tiled256_")
 
 
 @pytest.mark.parametrize("a_type,b_type", PAIRS)

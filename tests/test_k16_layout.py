@@ -26,8 +26,22 @@ def slot(r, c):
     return r * BKB + 16 * (c ^ swz16(r))
 
 
-@pytest.mark.parametrize("GM,GN", [(2, 4), (4, 2)], ids=["tiled256w8k16", "tiled256w8tk16"])
-def test_k16_lds_indexing(GM, GN):
+def swz64(r):
+    return (r >> 2) & 3
+
+
+@pytest.mark.parametrize("GM,GN,FB", [(2, 4, 16), (4, 2, 16), (2, 4, 32), (4, 2, 32)],
+                         ids=["tiled256w8k16", "tiled256w8tk16", "fp8_2x4", "fp8_4x2"])
+def test_k16_lds_indexing(GM, GN, FB):
+    """FB = 16: 16x16 fragments, one 16-byte read per lane at chunk l / 16,
+    slot function swz16.  FB = 32 (fp8, 32x32x64): two reads per lane at
+    chunks 2 (l / 32) and 2 (l / 32) + 1, slot function swz64."""
+    sw = swz16 if FB == 16 else swz64
+    NRD = 1 if FB == 16 else 2
+
+    def slot(r, c):
+        return r * BKB + 16 * (c ^ sw(r))
+
     BM = BN = 256
     A_TILE = BM * BKB
     stage = {}
@@ -37,34 +51,40 @@ def test_k16_lds_indexing(GM, GN):
             for i in range(rows // RPP):
                 r = r0 + i * RPP
                 off = base + slot(r0, ch) + i * RPP * BKB  # the kernel's l0 + i RPP BKB
-                assert off == base + slot(r, ch)           # swz16 is RPP-periodic
+                assert off == base + slot(r, ch)           # the slot function is RPP-periodic
                 for b in range(16):
                     assert off + b not in stage
                     stage[off + b] = (op, r, 16 * ch + b)
     assert len(stage) == (BM + BN) * BKB and max(stage) < (BM + BN) * BKB
 
     WM, WN = BM // GM, BN // GN
-    FI, FJ = WM // 16, WN // 16
+    FI, FJ = WM // FB, WN // FB
     for wave in range(GM * GN):
         wm, wn = wave // GN, wave % GN
         covered = set()
         for lane in range(64):
-            arow = wm * WM + (lane & 15)
-            brow = wn * WN + (lane & 15)
-            grp = lane >> 4
-            a_off = arow * BKB + 16 * (grp ^ swz16(arow))
-            b_off = A_TILE + brow * BKB + 16 * (grp ^ swz16(brow))
-            for i in range(FI):
-                got = [stage[a_off + i * 16 * BKB + q] for q in range(16)]
-                assert got == [("A", arow + 16 * i, 16 * grp + q) for q in range(16)]
-            for j in range(FJ):
-                got = [stage[b_off + j * 16 * BKB + q] for q in range(16)]
-                assert got == [("B", brow + 16 * j, 16 * grp + q) for q in range(16)]
-            # accumulator register r of (i, j): row 4 (l / 16) + r, column l % 16
+            arow = wm * WM + (lane & (FB - 1))
+            brow = wn * WN + (lane & (FB - 1))
+            grp = lane >> 4 if FB == 16 else 2 * (lane >> 5)
+            for q in range(NRD):
+                a_off = arow * BKB + 16 * ((grp + q) ^ sw(arow))
+                b_off = A_TILE + brow * BKB + 16 * ((grp + q) ^ sw(brow))
+                for i in range(FI):
+                    got = [stage[a_off + i * FB * BKB + e] for e in range(16)]
+                    assert got == [("A", arow + FB * i, 16 * (grp + q) + e) for e in range(16)]
+                for j in range(FJ):
+                    got = [stage[b_off + j * FB * BKB + e] for e in range(16)]
+                    assert got == [("B", brow + FB * j, 16 * (grp + q) + e) for e in range(16)]
+            # accumulator register r of block (i, j): 16x16: row 4 (l / 16) + r,
+            # column l % 16; 32x32: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
             for i in range(FI):
                 for j in range(FJ):
-                    for r in range(4):
-                        out = (wm * WM + 16 * i + 4 * (lane >> 4) + r, wn * WN + 16 * j + lane % 16)
+                    for r in range(4 if FB == 16 else 16):
+                        if FB == 16:
+                            rr, cc = 4 * (lane >> 4) + r, lane % 16
+                        else:
+                            rr, cc = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), lane % 32
+                        out = (wm * WM + FB * i + rr, wn * WN + FB * j + cc)
                         assert out not in covered
                         covered.add(out)
         assert len(covered) == WM * WN
