@@ -99,7 +99,15 @@ __global__ __launch_bounds__(256) void k_generic(GemmArgs g)
 // bytes of its row at byte 64 g, and MFMA step j uses bytes 16 j.. of every
 // lane's 64 (32 j.. for fp8): A and B use the same lane <-> K assignment, so
 // each product pairs equal K.  Each row's 256 bytes are fetched by 4 lanes as
-// whole cache lines; two chunks are kept in flight per wave.
+// whole cache lines; two chunks are kept in flight per wave.  B (the stream
+// from HBM) is loaded 1 KB per instruction instead -- rows 4k .. 4k+3 of
+// the chunk, 16 lanes per row -- into the wave's own LDS buffer (16-byte
+// chunk q of row r at slot q ^ (r & 15), so the 16 rows a fragment read
+// touches fall on 16 different slots of a 256-byte bank window) and read
+// back in the layout above: a load-only probe of this kernel's B stream
+// moved 4.6 TB/s with such loads against 3.6 TB/s with fragment-shaped
+// ones.  (A, 16 rows read by every workgroup, comes from L2; W4A16 keeps
+// its register path.)
 template <class OP>
 __global__ __launch_bounds__(512, 1) void k_skinny(GemmArgs g)
 {
@@ -110,6 +118,9 @@ __global__ __launch_bounds__(512, 1) void k_skinny(GemmArgs g)
     constexpr int STEPS = LB / OP::LANE_BYTES;   // MFMAs per fragment per chunk
     constexpr int FW = OP::LANE_BYTES / 4;
     __shared__ __attribute__((aligned(16))) uint32_t red[WAVES][2][64][4];
+    // per wave: 32 B rows x 256 bytes (one buffer: a wave's LDS accesses are
+    // ordered, so a chunk's stores cannot overtake the previous chunk's reads)
+    __shared__ __attribute__((aligned(16))) uint8_t bst[OP::W4 ? 16 : WAVES * 32 * 256];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -137,6 +148,12 @@ __global__ __launch_bounds__(512, 1) void k_skinny(GemmArgs g)
     const bool has_wz = g.wz != nullptr;
 
     u4_t pa[2][NLD], pb[2][2][W4 ? 1 : NLD];
+    // B chunk loaded 1 KB per instruction: load k, lane l holds row 4 k + l / 16,
+    // bytes 16 (l % 16) of the chunk
+    u4_t pc[2][W4 ? 1 : 8];
+    const int vc0 = (lane >> 4) * (int)ldb_b + 16 * (lane & 15);
+    uint8_t *bwave = bst + (W4 ? 0 : wave * 32 * 256);
+    auto bslot = [](int r, int q) STG_AI { return r * 256 + ((q ^ (r & 15)) << 4); };
     uint32_t wsb[2][2], wzb[2][2];
     auto load = [&](auto set, int c) STG_AI {
         constexpr int S = decltype(set)::value;
@@ -157,10 +174,8 @@ __global__ __launch_bounds__(512, 1) void k_skinny(GemmArgs g)
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < NLD; ++j) {
-                pb[S][0][j] = buf_load16(rb, vb0 + 16 * j, soff);
-                pb[S][1][j] = buf_load16(rb, vb1 + 16 * j, soff);
-            }
+            for (int k = 0; k < 8; ++k)
+                pc[S][k] = buf_load16(rb, vc0 + 4 * k * (int)ldb_b, soff);
         }
     };
     typename OP::acc_t acc[2] = {typename OP::acc_t{}, typename OP::acc_t{}};
@@ -182,6 +197,17 @@ __global__ __launch_bounds__(512, 1) void k_skinny(GemmArgs g)
                     acc[f] = OP::mma(a + st * FW, (const uint32_t *)bq + st * FW, acc[f]);
             }
         } else {
+            // the chunk through this wave's LDS buffer into the fragment layout
+            uint8_t *buf = bwave;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                *(u4_t *)(buf + bslot(4 * k + (lane >> 4), lane & 15)) = pc[S][k];
+            wave_lds_sync();
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int j = 0; j < NLD; ++j)
+                    pb[S][f][j] = *(const u4_t *)(buf + bslot(16 * f + row, 4 * grp + j));
 #pragma unroll
             for (int st = 0; st < STEPS; ++st)
 #pragma unroll
